@@ -1,0 +1,187 @@
+"""Seeded synthetic workloads and work accounting for the attention forward.
+
+This module draws inputs and counts work; it performs none of the attention
+arithmetic, so both the fp64 oracle tests and the GPU path take their inputs
+from here without sharing any of the method's code.
+
+Workload shapes follow the FlashAttention Cheat Sheet, §1 "The whole
+operation" (Q is [B, Hq, Lq, D], K and V are [B, Hkv, Lk, D]) and the shape
+family of the FlashAttention-4 benchmark summarised in "FlashAttention-4:
+Blackwell Attention Kernel Co-Design", "How we know: Blackwell benchmarks and
+ablations" (bf16, sequence lengths 1K-32K, head dimensions 64 and 128, causal
+and non-causal).  Inputs are iid N(0, 1) drawn in fp32 and rounded to bf16,
+the illustrative assumption of FlashAttention from Scratch, §2 ("Why divide by
+sqrt d?").
+
+Generation recipe (fixed; never changed to make a comparison pass):
+  * a torch CPU generator seeded with ``1000 + config index``;
+  * Q, K, V drawn in that order with ``torch.randn`` in fp32, then cast to
+    bf16 (round to nearest even);
+  * the long-context GQA workload multiplies Q on every head h with
+    h % 8 == 0 by 4 (exact in bf16) so that large row maxima arrive late;
+  * the decode workload then draws ``kv_lens`` uniformly in [512, 8192] with
+    ``torch.randint(512, 8193)``; K and V are allocated at the full capacity
+    of 8192 rows per sequence and only the first ``kv_lens[b]`` are valid.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    D: int
+    causal: bool
+    index: int
+    q_boost_every: int = 0      # multiply Q by q_boost on heads h % q_boost_every == 0
+    q_boost: float = 1.0
+    ragged: Optional[tuple] = None  # (lo, hi) inclusive range of kv_lens, else None
+    description: str = ""
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+WORKLOADS = [
+    Workload("tiny_b1_h2_l256_d64", 1, 2, 2, 256, 256, 64, False, 0,
+             description="tiny exact-attention forward, non-causal"),
+    Workload("prefill_b4_h16_l1024_d64", 4, 16, 16, 1024, 1024, 64, False, 1,
+             description="prefill forward, no mask"),
+    Workload("causal_b2_h16_l4096_d128", 2, 16, 16, 4096, 4096, 128, True, 2,
+             description="causal prefill forward"),
+    Workload("gqa_causal_b1_hq32_hkv8_l16384_d128", 1, 32, 8, 16384, 16384, 128, True, 3,
+             q_boost_every=8, q_boost=4.0,
+             description="long-context causal GQA forward, Q x4 on every 8th head"),
+    Workload("decode_b64_hq32_hkv8_d128_ragged", 64, 32, 8, 1, 8192, 128, False, 4,
+             ragged=(512, 8192),
+             description="split-KV decode, ragged kv_lens in [512, 8192]"),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+@dataclass
+class Inputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    kv_lens: Optional[torch.Tensor]
+    scale: float
+    causal: bool
+    meta: dict = field(default_factory=dict)
+
+
+def make_inputs(w: Workload) -> Inputs:
+    """Draw the workload's inputs on the CPU (bf16 Q, K, V; int32 kv_lens)."""
+    g = torch.Generator().manual_seed(w.seed)
+    q = torch.randn(w.B, w.Hq, w.Lq, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn(w.B, w.Hkv, w.Lk, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(w.B, w.Hkv, w.Lk, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    if w.q_boost_every:
+        q[:, ::w.q_boost_every] *= w.q_boost
+    kv_lens = None
+    if w.ragged is not None:
+        lo, hi = w.ragged
+        kv_lens = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
+    return Inputs(q, k, v, kv_lens, w.scale, w.causal, {"workload": w.name, "seed": w.seed})
+
+
+def random_case(seed: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D: int,
+                causal: bool = False, kv_lens=None, scale: Optional[float] = None,
+                q_mult: float = 1.0, k_mult: float = 1.0) -> Inputs:
+    """A seeded N(0,1) case of arbitrary shape for parity tests.
+
+    ``kv_lens`` may be None, a list of ints, or the string "ragged" (drawn
+    uniformly in [0, Lk] after Q, K, V from the same generator).
+    """
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(B, Hq, Lq, D, generator=g) * q_mult).to(torch.bfloat16)
+    k = (torch.randn(B, Hkv, Lk, D, generator=g) * k_mult).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, Lk, D, generator=g).to(torch.bfloat16)
+    if isinstance(kv_lens, str) and kv_lens == "ragged":
+        kv_lens = torch.randint(0, Lk + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    elif kv_lens is not None:
+        kv_lens = torch.tensor(list(kv_lens), dtype=torch.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return Inputs(q, k, v, kv_lens, scale, causal, {"seed": seed})
+
+
+# ---------------------------------------------------------------------------
+# Work accounting (algorithmic FLOPs and compulsory bytes)
+# ---------------------------------------------------------------------------
+
+def valid_lengths(w_or_shape, kv_lens=None):
+    """Per-sequence valid key counts n_b (kv_lens clamped to [0, Lk], else Lk)."""
+    B, Lk = w_or_shape.B, w_or_shape.Lk
+    if kv_lens is None:
+        return [Lk] * B
+    return [min(max(int(x), 0), Lk) for x in kv_lens]
+
+
+def allowed_pairs(Lq: int, n: int, causal: bool) -> int:
+    """Number of allowed (query, key) pairs in one head.
+
+    Causal masking is bottom-right aligned: query i sits at absolute position
+    n - Lq + i and sees keys j <= that position (FlashAttention from Scratch,
+    §5 "Rectangular causal masking is a correctness issue").
+    """
+    if not causal:
+        return Lq * n
+    tot = 0
+    off = n - Lq
+    # rows with position p = off + i see min(max(p + 1, 0), n) keys
+    for i in range(Lq):
+        tot += min(max(off + i + 1, 0), n)
+    return tot
+
+
+def algorithmic_flops(w, kv_lens=None) -> int:
+    """4 * D FLOPs per allowed pair: two matrix products with multiply and add
+    counted separately (FlashAttention from Scratch, §11.1 counts 4MNd per tile)."""
+    ns = valid_lengths(w, kv_lens)
+    return sum(4 * w.D * allowed_pairs(w.Lq, n, w.causal) * w.Hq for n in ns)
+
+
+def compulsory_bytes(w, kv_lens=None) -> int:
+    """Bytes that must cross HBM once: Q read, valid K and V rows read once per
+    KV head, O written (bf16) and the LSE written (fp32)."""
+    ns = valid_lengths(w, kv_lens)
+    qo = 2 * w.B * w.Hq * w.Lq * w.D * 2
+    lse = w.B * w.Hq * w.Lq * 4
+    kv = sum(2 * w.Hkv * n * w.D * 2 for n in ns)
+    return qo + lse + kv
+
+
+def paper_tiled_traffic_bytes(N: int, d: int, tile: int, elem_bytes: int = 2) -> int:
+    """Forward HBM traffic of the tiled schedule for one head: Q read once, O
+    written once, K and V re-read N / tile times, i.e. 2Nd + 2N^2 d / tile
+    numbers (FlashAttention visualisation, giaicuuthegioi.com, "Tiling: one S
+    tile at a time")."""
+    return (2 * N * d + 2 * N * N * d // tile) * elem_bytes
+
+
+def paper_naive_traffic_bytes(N: int, d: int, elem_bytes: int = 2) -> int:
+    """Three-kernel materialised attention: 4N^2 + 4Nd numbers in total
+    (same page, "Naive attention: three kernels" table)."""
+    return (4 * N * N + 4 * N * d) * elem_bytes
+
+
+def paper_tile_live_numbers(tile: int, d: int) -> int:
+    """On-chip numbers live for one tile: Q, K, V, O tiles (4Bd), the S tile
+    (B^2) and m, l (2B) (same page, "Tile size and SRAM")."""
+    return 4 * tile * d + tile * tile + 2 * tile

@@ -1,0 +1,35 @@
+"""fp64 CPU oracle for the FlashAttention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The GPU library never imports this
+package and this package imports nothing from the library: the two share no
+kernels, headers, helpers, tables or constants.  The only thing both sides
+consume is the seeded input generator (``exact_attention_07_amd.workloads``),
+which draws random numbers and performs none of the attention arithmetic.
+
+Contents
+--------
+attention.dense_head / attention_forward / attention_rows
+    The plain definition, materialising S, P and O in fp64 (the oracle the GPU
+    path is compared against).
+streaming.streaming_head
+    An independent fp64 model of the online-softmax recurrence with free tile
+    sizes, free KV tile order and an optional conditional-rescale threshold;
+    used only to pin the dense definition and vice versa.
+merge
+    The partition-state merge and the log-sum-exp merge of normalised
+    partials, used to pin the split-KV algebra.
+
+Every function cites the passage of the pages it follows.  All of them are
+pinned by ``tests/test_oracle.py`` to values the pages print, closed forms,
+invariances, brute force on tiny inputs and a library routine.
+"""
+from .attention import as_f64, dense_head, attention_forward, attention_rows
+from .streaming import streaming_head
+from .merge import partition_state, merge_states, finish_state, merge_normalized
+
+__all__ = [
+    "as_f64", "dense_head", "attention_forward", "attention_rows",
+    "streaming_head", "partition_state", "merge_states", "finish_state",
+    "merge_normalized",
+]

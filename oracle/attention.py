@@ -1,0 +1,113 @@
+"""The definition of exact attention, written out in fp64 (test infrastructure).
+
+O = softmax(S + M) V with S = scale * Q K^T and M_ij = 0 for an allowed pair,
+-inf otherwise, one softmax per query row.  Sources:
+  * FlashAttention from Scratch (ryhuang.blog), §2 "Begin with one attention
+    row" (the formula, the per-row softmax, the {0, -inf} mask) and
+    "Stabilize softmax before doing anything clever" (subtract the row max);
+  * §3 "Why straightforward attention is expensive": the materialised form
+    (write S, softmax it into P, multiply P by V) is exactly what this module
+    does, in fp64 on the CPU;
+  * §4.4 "Handle the empty state deliberately": a row with no allowed key
+    returns a zero output and log-sum-exp -inf (an API convention);
+  * §5 "Run the math before writing a GPU kernel": causal pairs are allowed
+    when key position <= query position, with absolute positions;
+    "Rectangular causal masking is a correctness issue": with fewer queries
+    than keys the queries are the last positions of the cache
+    (bottom-right alignment);
+  * §7.1 / FlashAttention 1-4 (noviorlu.github.io), FlashAttention-2 change 1:
+    the saved row statistic is the natural-log LSE = m + log(l);
+  * §9.2 "GQA changes the reuse opportunity": query head h reads KV head
+    floor(h / r) with r = Hq / Hkv;
+  * FlashAttention Cheat Sheet (mxino.github.io), §1 "The whole operation":
+    Q [B, Hq, Lq, D], K and V [B, Hkv, Lk, D].
+
+Inputs are taken at their exact values (bf16 tensors are widened to fp64 with
+no rounding), so the oracle answers "what is the exact attention of these
+bf16 numbers", which is what the tolerances of the GPU comparison are about.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def as_f64(x) -> np.ndarray:
+    """Widen a numpy array or a torch tensor (any dtype, any device) to fp64."""
+    if hasattr(x, "detach"):  # torch tensor, converted without importing torch here
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None):
+    """Materialised attention for one (batch, head): returns (O, LSE) in fp64.
+
+    q: [Lq, D]; k: [Lk, D]; v: [Lk, Dv].  q_pos / k_pos are the absolute
+    token positions of the rows (default 0..L-1); with ``causal`` a pair is
+    allowed iff k_pos[j] <= q_pos[i].
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    Lq, Lk, Dv = q.shape[0], k.shape[0], v.shape[1]
+    q_pos = np.arange(Lq) if q_pos is None else np.asarray(q_pos)
+    k_pos = np.arange(Lk) if k_pos is None else np.asarray(k_pos)
+    if Lk == 0:
+        return np.zeros((Lq, Dv)), np.full(Lq, -np.inf)
+
+    # Write the whole score matrix.
+    S = scale * (q @ k.T)
+    if causal:
+        S = np.where(k_pos[None, :] > q_pos[:, None], -np.inf, S)
+
+    # Row softmax with the max shift; masked entries give exp(-inf) = 0.
+    m = S.max(axis=1)
+    has_key = np.isfinite(m)
+    shift = np.where(has_key, m, 0.0)
+    E = np.exp(S - shift[:, None])
+    ell = E.sum(axis=1)
+    safe_ell = np.where(has_key, ell, 1.0)
+    P = E / safe_ell[:, None]
+
+    # Multiply the probability matrix by V.
+    O = P @ v
+    O[~has_key] = 0.0
+    lse = np.where(has_key, shift + np.log(safe_ell), -np.inf)
+    return O, lse
+
+
+def _kv_len(kv_lens, b, Lk):
+    if kv_lens is None:
+        return Lk
+    return int(min(max(int(as_f64(kv_lens)[b]), 0), Lk))
+
+
+def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None):
+    """(O, LSE) of selected query rows of one (b, h) of a batched problem.
+
+    Rows are evaluated by the same definition as ``attention_forward``; this
+    lets full-size problems be checked on sampled rows.
+    """
+    Hq, Lq = q.shape[1], q.shape[2]
+    Hkv, Lk = k.shape[1], k.shape[2]
+    r = Hq // Hkv
+    g = h // r
+    n = _kv_len(kv_lens, b, Lk)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    q_bh = as_f64(q[b, h])[rows]
+    k_bg = as_f64(k[b, g, :n])
+    v_bg = as_f64(v[b, g, :n])
+    q_pos = (n - Lq) + rows          # bottom-right: the queries end the cache
+    return dense_head(q_bh, k_bg, v_bg, scale, causal, q_pos, np.arange(n))
+
+
+def attention_forward(q, k, v, scale, causal=False, kv_lens=None):
+    """Batched attention over [B, H, L, D] inputs: returns O [B, Hq, Lq, Dv]
+    and LSE [B, Hq, Lq], both fp64.  ``kv_lens[b]`` (clamped to [0, Lk]) is the
+    number of valid keys of sequence b; None means all Lk are valid."""
+    B, Hq, Lq = q.shape[0], q.shape[1], q.shape[2]
+    Hkv, Dv = k.shape[1], v.shape[3]
+    assert Hq % Hkv == 0, "query heads must be a multiple of KV heads"
+    O = np.zeros((B, Hq, Lq, Dv))
+    lse = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            O[b, h], lse[b, h] = attention_rows(q, k, v, scale, causal, kv_lens, b, h)
+    return O, lse

@@ -1,0 +1,474 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Every pin is a ``check_*`` function of an oracle namespace, so the same pins
+run against the real oracle (the ordinary tests) and against copies of it
+with a plausible mistake planted on the CPU (``test_pins_catch_mutants``),
+which shows that a dropped term, a wrong sign, index or alignment, or a
+transposed operand anywhere in the oracle fails at least one pin.
+
+Pins used (none of them retypes the oracle's own formula):
+  * values the pages print: the worked row (FlashAttention from Scratch,
+    §2 and §4.2), the two-tile example (FlashAttention Cheat Sheet, §6), the
+    rectangular causal mask table (FlashAttention from Scratch, §5);
+  * the page's own fp64 experiments re-derived with the same seeds and
+    shapes (§5 streaming vs dense, §9.1 split-KV merge);
+  * invariances the pages state (+1000 shift, §2 checkpoint; tile size and
+    tile order, Cheat Sheet §5; merge trees, §4.3);
+  * closed forms (one key, identical keys, zero query, causal row 0);
+  * brute force on tiny inputs: sum of e^s v over sum of e^s with no max
+    shift, evaluated with math.fsum in pure Python;
+  * a library routine: torch's CPU scaled_dot_product_attention in fp64 with
+    an explicit boolean mask, GQA by repeating KV heads.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as real_oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+ORACLE_DIR = os.path.join(os.path.dirname(HERE), "oracle")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def oracle_namespace(mutations=()):
+    """Load fresh copies of the oracle modules, optionally with textual
+    mutations (module, old, new) applied, and expose their functions."""
+    mods = {}
+    for name in ("attention", "streaming", "merge"):
+        path = os.path.join(ORACLE_DIR, name + ".py")
+        with open(path) as f:
+            src = f.read()
+        for mname, old, new in mutations:
+            if mname == name:
+                assert old in src, f"mutation target not found in {name}.py: {old!r}"
+                src = src.replace(old, new, 1)
+        mod = types.ModuleType(f"_oracle_copy_{name}")
+        exec(compile(src, path, "exec"), mod.__dict__)
+        mods[name] = mod
+    a, s, m = mods["attention"], mods["streaming"], mods["merge"]
+    return types.SimpleNamespace(
+        dense_head=a.dense_head, attention_forward=a.attention_forward,
+        attention_rows=a.attention_rows, streaming_head=s.streaming_head,
+        partition_state=m.partition_state, merge_states=m.merge_states,
+        finish_state=m.finish_state, merge_normalized=m.merge_normalized)
+
+
+def row_inputs(scores, values):
+    """One query whose scores against the keys are ``scores`` at scale 1:
+    q = e0, k_j = s_j e0; scalar values v_j (Dv = 1)."""
+    n = len(scores)
+    q = np.zeros((1, 2))
+    q[0, 0] = 1.0
+    k = np.zeros((n, 2))
+    k[:, 0] = scores
+    v = np.asarray(values, dtype=np.float64).reshape(n, 1)
+    return q, k, v
+
+
+def rng_case(seed, Lq, Lk, D, Dv=None, mult=1.0):
+    r = np.random.default_rng(seed)
+    Dv = D if Dv is None else Dv
+    return (r.standard_normal((Lq, D)) * mult, r.standard_normal((Lk, D)) * mult,
+            r.standard_normal((Lk, Dv)))
+
+
+def close(a, b, tol=1e-10):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    fin_a, fin_b = np.isfinite(a), np.isfinite(b)
+    assert np.array_equal(fin_a, fin_b), "finite/non-finite pattern differs"
+    assert np.array_equal(a[~fin_a], b[~fin_b]), "non-finite values differ"
+    if fin_a.any():
+        err = np.abs(a[fin_a] - b[fin_b])
+        lim = tol * (1.0 + np.abs(b[fin_b]))
+        assert np.all(err <= lim), f"max err {err.max():.3e}"
+
+
+# ---------------------------------------------------------------------------
+# The checks
+# ---------------------------------------------------------------------------
+
+def check_worked_row(orc):
+    g = golden("worked_row.json")
+    q, k, v = row_inputs(g["scores"], g["values"])
+    out, lse = orc.dense_head(q, k, v, 1.0)
+    assert abs(out[0, 0] - g["output"]["value"]) <= g["output"]["abs_tol"], out
+    # LSE closed form, evaluated without any shift: log(e^1 + e^2 + e^3).
+    assert abs(lse[0] - math.log(sum(math.exp(s) for s in g["scores"]))) < 1e-12
+    # Streamed as [1, 2] then [3] (§4.2): alpha = e^-1 on the second tile.
+    trace = []
+    o2, l2 = orc.streaming_head(q, k, v, 1.0, block_q=1, block_k=2, trace=trace)
+    assert len(trace) == 2
+    t1, t2 = trace
+    assert t1["m"][0] == 2.0
+    assert abs(t1["ell"][0] - (1.0 + math.exp(-1.0))) < 1e-14          # e^{1-2} + e^{2-2}
+    assert abs(t1["u"][0, 0] - (10.0 * math.exp(-1.0) + 20.0)) < 1e-12
+    assert abs(t2["alpha"][0] - g["alpha_second_tile"]["value"]) < 1e-15
+    assert abs(o2[0, 0] - g["output"]["value"]) <= g["output"]["abs_tol"]
+    assert abs(l2[0] - lse[0]) < 1e-12
+
+
+def check_shift_invariance(orc):
+    g = golden("worked_row.json")
+    c = g["shift_invariance_offset"]
+    q, k, v = row_inputs(g["scores"], g["values"])
+    qs, ks, vs = row_inputs([s + c for s in g["scores"]], g["values"])
+    o, l = orc.dense_head(q, k, v, 1.0)
+    os_, ls = orc.dense_head(qs, ks, vs, 1.0)
+    assert np.all(np.isfinite(os_)), "shifted scores overflowed"
+    assert abs(os_[0, 0] - o[0, 0]) < 1e-12
+    assert abs(ls[0] - (l[0] + c)) < 1e-9
+    ot, lt = orc.streaming_head(qs, ks, vs, 1.0, block_k=1)
+    assert abs(ot[0, 0] - o[0, 0]) < 1e-12
+    assert abs(lt[0] - (l[0] + c)) < 1e-9
+
+
+def check_mask_renormalises(orc):
+    # §2 checkpoint: mask the third key; the remaining two weights renormalise.
+    g = golden("worked_row.json")
+    q, k, v = row_inputs(g["scores"], g["values"])
+    out, lse = orc.dense_head(q, k, v, 1.0, causal=True, q_pos=[1], k_pos=[0, 1, 2])
+    e = math.e
+    expected = 10.0 / (1.0 + e) + 20.0 * e / (1.0 + e)
+    assert abs(out[0, 0] - expected) < 1e-12
+    assert abs(lse[0] - math.log(e + e * e)) < 1e-12
+    zeroed = sum(math.exp(s) * v for s, v in zip(g["scores"][:2], g["values"][:2])) / \
+        sum(math.exp(s) for s in g["scores"])
+    assert abs(out[0, 0] - zeroed) > 1.0
+
+
+def check_two_tile(orc):
+    g = golden("two_tile_example.json")
+    q, k, v = row_inputs(g["scores"], g["values"])
+    trace = []
+    out, lse = orc.streaming_head(q, k, v, 1.0, block_q=1, block_k=g["tile_size"], trace=trace)
+    t1, t2 = trace
+    a1, a2 = g["after_tile_1"], g["after_tile_2"]
+    assert t1["m"][0] == a1["m"] and t2["m"][0] == a2["m"]
+    assert abs(t1["ell"][0] - a1["ell"]) <= 1e-4
+    assert abs(t1["u"][0, 0] - a1["A"]) <= 1e-3
+    assert abs(t2["alpha"][0] - a2["alpha"]) <= 1e-4
+    assert abs(t2["ell"][0] - a2["ell"]) <= 1e-4
+    assert abs(t2["u"][0, 0] - a2["A"]) <= 1e-3
+    assert abs(out[0, 0] - g["output"]) <= 1e-2
+    od, ld = orc.dense_head(q, k, v, 1.0)
+    assert abs(od[0, 0] - g["output"]) <= 1e-2
+    assert abs(od[0, 0] - out[0, 0]) < 1e-12 and abs(ld[0] - lse[0]) < 1e-12
+
+
+def check_mask_table(orc):
+    # All scores 0 and V = identity: a row's output is uniform over its allowed keys.
+    g = golden("rectangular_causal_mask.json")
+    nq, nk = g["n_queries"], g["n_keys"]
+    q = np.zeros((1, 1, nq, 1))
+    k = np.zeros((1, 1, nk, 1))
+    v = np.eye(nk).reshape(1, 1, nk, nk)
+    out, lse = orc.attention_forward(q, k, v, 1.0, causal=True)
+    allowed = (out[0, 0] > 0).astype(int).tolist()
+    assert allowed == g["allowed"], allowed
+    counts = np.asarray(g["allowed"]).sum(axis=1)
+    close(lse[0, 0], np.log(counts), 1e-14)
+
+
+def check_streaming_vs_dense(orc):
+    cases = [(11, 5, 13, 16, 8, 8), (12, 33, 70, 8, 8, 0), (13, 64, 64, 4, 3, -5),
+             (14, 7, 19, 5, 5, 12)]
+    for seed, Lq, Lk, D, Dv, q_start in cases:
+        q, k, v = rng_case(seed, Lq, Lk, D, Dv)
+        scale = 1.0 / math.sqrt(D)
+        for causal in (False, True):
+            qp = q_start + np.arange(Lq)
+            od, ld = orc.dense_head(q, k, v, scale, causal, q_pos=qp)
+            for bq, bk in [(1, 1), (3, 4), (4, 7), (64, 64), (Lq, Lk), (7, 3)]:
+                nt = (Lk + bk - 1) // bk
+                orders = [None, list(range(nt))[::-1],
+                          list(np.random.default_rng(seed + bk).permutation(nt))]
+                for order in orders:
+                    for tau in (None, 0.0, 8 * math.log(2.0), 1e3):
+                        os_, ls = orc.streaming_head(q, k, v, scale, causal, q_pos=qp,
+                                                     block_q=bq, block_k=bk,
+                                                     kv_order=order, tau=tau)
+                        close(os_, od)
+                        close(ls, ld)
+
+
+def check_merge_trees(orc):
+    q, k, v = rng_case(21, 6, 13, 8, 5)
+    scale = 0.3
+    qp = np.array([-1, 2, 5, 7, 11, 12])        # row 0 sees no key at all
+    kp = np.arange(13)
+    od, ld = orc.dense_head(q, k, v, scale, True, q_pos=qp, k_pos=kp)
+    assert np.all(od[0] == 0.0) and ld[0] == -np.inf
+    bounds = [(0, 3), (3, 3), (3, 7), (7, 13)]   # includes an empty partition
+    states = [orc.partition_state(q, k[a:b], v[a:b], scale, True, qp, kp[a:b]) for a, b in bounds]
+    A, B_, C, D_ = states
+    trees = [
+        orc.merge_states(orc.merge_states(orc.merge_states(A, B_), C), D_),
+        orc.merge_states(A, orc.merge_states(B_, orc.merge_states(C, D_))),
+        orc.merge_states(orc.merge_states(D_, B_), orc.merge_states(C, A)),
+    ]
+    for st in trees:
+        o, l = orc.finish_state(st)
+        close(o, od)
+        close(l, ld)
+    parts = [orc.finish_state(s) for s in states]
+    (oa, la), (ob, lb), (oc, lc), (oe, le) = parts
+    o1, l1 = orc.merge_normalized(*orc.merge_normalized(*orc.merge_normalized(oa, la, ob, lb), oc, lc), oe, le)
+    o2, l2 = orc.merge_normalized(oe, le, *orc.merge_normalized(oc, lc, *orc.merge_normalized(ob, lb, oa, la)))
+    for o, l in ((o1, l1), (o2, l2)):
+        close(o, od)
+        close(l, ld)
+
+
+def check_page_streaming_experiment(orc):
+    # FlashAttention from Scratch §5: seed 7, q 5x16, k 13x16, v 13x8, causal,
+    # queries are the last five positions of a 13-token cache, blocks 3 / 4, 1e-10.
+    torch.manual_seed(7)
+    q = torch.randn(5, 16)
+    k = torch.randn(13, 16)
+    v = torch.randn(13, 8)
+    scale = 1.0 / math.sqrt(16)
+    qp = 8 + np.arange(5)
+    ref, ref_lse = orc.dense_head(q, k, v, scale, True, q_pos=qp)
+    out, lse = orc.streaming_head(q, k, v, scale, True, q_pos=qp, block_q=3, block_k=4)
+    close(out, ref)
+    close(lse, ref_lse)
+
+
+def check_page_split_experiment(orc):
+    # FlashAttention from Scratch §9.1: seed 9, q 2x8, k 11x8, v 11x5; partitions
+    # [0, 4) and [4, 11) with absolute key offsets; causal from position 9.
+    torch.manual_seed(9)
+    q = torch.randn(2, 8)
+    k = torch.randn(11, 8)
+    v = torch.randn(11, 5)
+    scale = 1.0 / math.sqrt(8)
+    qp = 9 + np.arange(2)
+    oa, la = orc.streaming_head(q, k[:4], v[:4], scale, True, q_pos=qp, k_pos=np.arange(4))
+    ob, lb = orc.streaming_head(q, k[4:], v[4:], scale, True, q_pos=qp, k_pos=4 + np.arange(7))
+    merged, mlse = orc.merge_normalized(oa, la, ob, lb)
+    ref, ref_lse = orc.dense_head(q, k, v, scale, True, q_pos=qp)
+    close(merged, ref)
+    close(mlse, ref_lse)
+
+
+def _brute_row(qi, K, V, scale, allowed):
+    """sum_j e^{s_j} v_j / sum_j e^{s_j} over allowed j, with no max shift."""
+    idx = [j for j in range(len(K)) if allowed[j]]
+    if not idx:
+        return [0.0] * len(V[0]), -math.inf
+    s = {j: scale * math.fsum(a * b for a, b in zip(qi, K[j])) for j in idx}
+    den = math.fsum(math.exp(s[j]) for j in idx)
+    out = [math.fsum(math.exp(s[j]) * V[j][c] for j in idx) / den for c in range(len(V[0]))]
+    return out, math.log(den)
+
+
+def check_brute_force(orc):
+    r = np.random.default_rng(5)
+    for trial in range(60):
+        Lq, Lk = int(r.integers(1, 7)), int(r.integers(1, 7))
+        D, Dv = int(r.integers(1, 5)), int(r.integers(1, 4))
+        q = r.integers(-3, 4, (Lq, D)).astype(float)
+        k = r.integers(-3, 4, (Lk, D)).astype(float)
+        v = r.integers(-5, 6, (Lk, Dv)).astype(float)
+        scale = 0.5
+        for causal in (False, True):
+            for q_start in range(-Lk, Lk + 1):
+                qp = q_start + np.arange(Lq)
+                out, lse = orc.dense_head(q, k, v, scale, causal, q_pos=qp)
+                for i in range(Lq):
+                    allowed = [(not causal) or j <= qp[i] for j in range(Lk)]
+                    bo, bl = _brute_row(q[i].tolist(), k.tolist(), v.tolist(), scale, allowed)
+                    if bl == -math.inf:
+                        assert lse[i] == -math.inf and np.all(out[i] == 0.0)
+                    else:
+                        assert abs(lse[i] - bl) <= 1e-12 * (1 + abs(bl))
+                        for c in range(Dv):
+                            assert abs(out[i, c] - bo[c]) <= 1e-12 * (1 + abs(bo[c]))
+                if not causal:
+                    break
+
+
+def check_closed_forms(orc):
+    r = np.random.default_rng(3)
+    # One key: the output is that key's value row exactly; LSE is its score.
+    q, k, v = r.standard_normal((4, 8)), r.standard_normal((1, 8)), r.standard_normal((1, 6))
+    out, lse = orc.dense_head(q, k, v, 0.25)
+    assert np.array_equal(out, np.repeat(v, 4, axis=0))
+    close(lse, 0.25 * (q @ k[0]), 1e-14)
+    # Identical keys: the output is mean(V); LSE = s + ln n.
+    n = 9
+    k = np.repeat(r.standard_normal((1, 8)), n, axis=0)
+    v = r.standard_normal((n, 5))
+    out, lse = orc.dense_head(q, k, v, 0.25)
+    close(out, np.repeat(v.mean(axis=0, keepdims=True), 4, axis=0), 1e-13)
+    close(lse, 0.25 * (q @ k[0]) + math.log(n), 1e-13)
+    # Zero query: uniform weights.
+    k = r.standard_normal((n, 8))
+    out, lse = orc.dense_head(np.zeros((2, 8)), k, v, 0.7)
+    close(out, np.repeat(v.mean(axis=0, keepdims=True), 2, axis=0), 1e-13)
+    close(lse, np.full(2, math.log(n)), 1e-14)
+    # Causal row 0 (query at position 0) sees only key 0: output is v_0 exactly.
+    q = r.standard_normal((n, 8))
+    out, lse = orc.dense_head(q, k, v, 0.7, causal=True)
+    assert np.array_equal(out[0], v[0])
+    close(lse[0], 0.7 * (q[0] @ k[0]), 1e-14)
+
+
+def _sdpa_reference(q, k, v, scale, causal, kv_lens):
+    """torch CPU SDPA in fp64 with an explicit boolean mask (True = allowed)."""
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    r = Hq // Hkv
+    qd, kd, vd = q.double(), k.double().repeat_interleave(r, dim=1), v.double().repeat_interleave(r, dim=1)
+    mask = torch.zeros(B, 1, Lq, Lk, dtype=torch.bool)
+    for b in range(B):
+        n = Lk if kv_lens is None else int(kv_lens[b])
+        for i in range(Lq):
+            hi = n if not causal else min(n, n - Lq + i + 1)
+            mask[b, 0, i, :max(hi, 0)] = True
+    out = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask,
+                                                           dropout_p=0.0, scale=scale)
+    return out.numpy(), mask
+
+
+def check_vs_sdpa(orc):
+    g = torch.Generator().manual_seed(17)
+    B, Hq, Hkv, Lq, Lk, D = 2, 6, 2, 5, 9, 8
+    q = torch.randn(B, Hq, Lq, D, generator=g)
+    k = torch.randn(B, Hkv, Lk, D, generator=g)
+    v = torch.randn(B, Hkv, Lk, D, generator=g)
+    scale = 1.0 / math.sqrt(D)
+    for causal, lens in ((False, None), (True, None), (False, [9, 6]), (True, [9, 7])):
+        ref, mask = _sdpa_reference(q, k, v, scale, causal, lens)
+        out, lse = orc.attention_forward(q, k, v, scale, causal, lens)
+        close(out, ref)
+        # LSE against an independent evaluation: torch.logsumexp over masked scores.
+        s = scale * (q.double() @ k.double().repeat_interleave(Hq // Hkv, 1).transpose(-1, -2))
+        s = s.masked_fill(~mask, -math.inf)
+        close(lse, torch.logsumexp(s, dim=-1).numpy())
+
+
+def check_gqa_vs_repeated(orc):
+    r = np.random.default_rng(8)
+    B, Hq, Hkv, L, D = 1, 6, 2, 7, 4
+    q = r.standard_normal((B, Hq, L, D))
+    k = r.standard_normal((B, Hkv, L, D))
+    v = r.standard_normal((B, Hkv, L, D))
+    for causal in (False, True):
+        o1, l1 = orc.attention_forward(q, k, v, 0.5, causal)
+        o2, l2 = orc.attention_forward(q, np.repeat(k, Hq // Hkv, axis=1),
+                                       np.repeat(v, Hq // Hkv, axis=1), 0.5, causal)
+        close(o1, o2, 1e-15)
+        close(l1, l2, 1e-15)
+
+
+def check_kv_lens(orc):
+    r = np.random.default_rng(9)
+    B, H, Lq, Lk, D = 3, 2, 4, 10, 4
+    q = r.standard_normal((B, H, Lq, D))
+    k = r.standard_normal((B, H, Lk, D))
+    v = r.standard_normal((B, H, Lk, D))
+    lens = [10, 6, 0]
+    for causal in (False, True):
+        o, l = orc.attention_forward(q, k, v, 0.5, causal, lens)
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert np.all(o[b] == 0.0) and np.all(l[b] == -np.inf)
+                continue
+            ob, lb = orc.attention_forward(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.5, causal)
+            close(o[b], ob[0], 1e-15)
+            close(l[b], lb[0], 1e-15)
+
+
+def check_fully_masked_rows(orc):
+    # §5 experiment: q_start = -2 masks the first two rows entirely; the rest
+    # must equal the rows computed on their own.  Also Q and K multiplied by 20.
+    q, k, v = rng_case(31, 6, 8, 8, 3, mult=20.0)
+    qp = -2 + np.arange(6)
+    out, lse = orc.dense_head(q, k, v, 0.125, True, q_pos=qp)
+    assert np.all(out[:2] == 0.0) and np.all(lse[:2] == -np.inf)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse[2:]))
+    o2, l2 = orc.dense_head(q[2:], k, v, 0.125, True, q_pos=qp[2:])
+    close(out[2:], o2, 1e-15)
+    close(lse[2:], l2, 1e-15)
+    os_, ls = orc.streaming_head(q, k, v, 0.125, True, q_pos=qp, block_q=4, block_k=3)
+    close(os_, out)
+    close(ls, lse)
+    # Fewer keys than queries under bottom-right causal alignment: leading rows empty.
+    Q = q.reshape(1, 1, 6, 8)
+    K = k[:4].reshape(1, 1, 4, 8)
+    V = v[:4].reshape(1, 1, 4, 3)
+    o, l = orc.attention_forward(Q, K, V, 0.125, True)
+    assert np.all(o[0, 0, :2] == 0.0) and np.all(l[0, 0, :2] == -np.inf)
+    assert np.all(np.isfinite(l[0, 0, 2:]))
+
+
+CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, check_two_tile,
+          check_mask_table, check_streaming_vs_dense, check_merge_trees,
+          check_page_streaming_experiment, check_page_split_experiment, check_brute_force,
+          check_closed_forms, check_vs_sdpa, check_gqa_vs_repeated, check_kv_lens,
+          check_fully_masked_rows]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
+def test_oracle_pin(check):
+    check(oracle_namespace())
+
+
+def test_package_exports_match_copies():
+    # The pins run on fresh copies of the modules; the package must export those same functions.
+    ns = oracle_namespace()
+    for name in ("dense_head", "attention_forward", "streaming_head", "merge_normalized"):
+        assert getattr(real_oracle, name).__code__.co_code == getattr(ns, name).__code__.co_code
+
+
+# Plausible mistakes; each must make at least one pin fail.
+MUTANTS = {
+    "scale_dropped": [("attention", "S = scale * (q @ k.T)", "S = (q @ k.T)")],
+    "causal_off_by_one": [("attention", "k_pos[None, :] > q_pos[:, None]", "k_pos[None, :] >= q_pos[:, None]")],
+    "causal_top_left": [("attention", "q_pos = (n - Lq) + rows", "q_pos = rows")],
+    "gqa_modulo_map": [("attention", "g = h // r", "g = h % Hkv")],
+    "lse_without_max": [("attention", "shift + np.log(safe_ell)", "np.log(safe_ell)")],
+    "no_max_shift": [("attention", "E = np.exp(S - shift[:, None])", "E = np.exp(S)")],
+    "no_normalisation": [("attention", "P = E / safe_ell[:, None]", "P = E")],
+    "scores_transposed": [("attention", "S = scale * (q @ k.T)", "S = scale * (k @ q.T).T[::-1, ::-1]")],
+    "empty_row_lse_zero": [("attention", "shift + np.log(safe_ell), -np.inf)", "shift + np.log(safe_ell), 0.0)")],
+    "kv_len_ignored": [("attention", "n = _kv_len(kv_lens, b, Lk)", "n = Lk")],
+    "alpha_sign": [("streaming", "alpha = np.exp(m - shift)", "alpha = np.exp(shift - m)")],
+    "ell_not_rescaled": [("streaming", "ell = alpha * ell + p.sum(axis=1)", "ell = ell + p.sum(axis=1)")],
+    "acc_not_rescaled": [("streaming", "u = alpha[:, None] * u + p @ vt", "u = u + p @ vt")],
+    "tau_inverted": [("streaming", "move = ~(jump <= tau)", "move = jump <= tau")],
+    "stream_mask_dropped": [("streaming", "s[kp[None, :] > qp[:, None]] = -np.inf", "pass")],
+    "merge_unweighted_ell": [("merge", "wa * la + wb * lb, wa[:, None] * ua", "la + lb, wa[:, None] * ua")],
+    "merge_lse_max": [("merge", "L = np.logaddexp(la, lb)", "L = np.maximum(la, lb)")],
+    "merge_weight_swapped": [("merge", "return wa[:, None] * oa + wb[:, None] * ob, L",
+                              "return wb[:, None] * oa + wa[:, None] * ob, L")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutants(name):
+    orc = oracle_namespace(MUTANTS[name])
+    failed = []
+    for check in CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(orc)
+        except Exception:  # an assertion or a crash both count as caught
+            failed.append(check.__name__)
+    assert failed, f"mutant {name} survived every pin"

@@ -1,0 +1,76 @@
+"""Host-side checks of the seeded workloads and of the work accounting."""
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from exact_attention_07_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_traffic_model_reproduces_page_table():
+    with open(os.path.join(GOLDEN, "traffic_table.json")) as f:
+        g = json.load(f)
+    MiB, GiB = 2.0 ** 20, 2.0 ** 30
+
+    def half_unit(x):
+        """Half a unit of the last digit the page prints."""
+        text = str(x)
+        return 0.5 * 10.0 ** -(len(text.split(".")[1]) if "." in text else 0)
+
+    for row in g["rows"]:
+        N, d, t = row["N"], row["d"], row["tile"]
+        naive = W.paper_naive_traffic_bytes(N, d)
+        flash = W.paper_tiled_traffic_bytes(N, d, t)
+        if "naive_bytes" in row:
+            assert naive == row["naive_bytes"] and flash == row["flash_bytes"]
+            continue
+        if "naive_MiB" in row:
+            assert abs(naive / MiB - row["naive_MiB"]) <= half_unit(row["naive_MiB"]), (N, naive / MiB)
+        else:
+            assert abs(naive / GiB - row["naive_GiB"]) <= 0.05 * row["naive_GiB"], (N, naive / GiB)
+        assert abs(flash / MiB - row["flash_MiB"]) <= half_unit(row["flash_MiB"]), (N, flash / MiB)
+    for row in g["sram_numbers"]:
+        assert W.paper_tile_live_numbers(row["tile"], row["d"]) == row["numbers"]
+
+
+def test_allowed_pairs_closed_forms():
+    # Square causal: L(L+1)/2 pairs; no mask: Lq * n; rectangular bottom-right.
+    for L in (1, 2, 7, 128, 4096):
+        assert W.allowed_pairs(L, L, True) == L * (L + 1) // 2
+        assert W.allowed_pairs(L, L, False) == L * L
+    # Two queries at the end of a five-key cache: 4 + 5 allowed pairs.
+    assert W.allowed_pairs(2, 5, True) == 9
+    # More queries than keys: the first Lq - n rows see nothing.
+    assert W.allowed_pairs(6, 4, True) == 1 + 2 + 3 + 4
+
+
+def test_workload_flops_and_bytes():
+    c2 = W.BY_NAME["prefill_b4_h16_l1024_d64"]
+    assert W.algorithmic_flops(c2) == 4 * 64 * 1024 * 1024 * 64
+    c3 = W.BY_NAME["causal_b2_h16_l4096_d128"]
+    assert W.algorithmic_flops(c3) == 4 * 128 * (4096 * 4097 // 2) * 32
+    c4 = W.BY_NAME["gqa_causal_b1_hq32_hkv8_l16384_d128"]
+    assert abs(W.algorithmic_flops(c4) / 2.1992e12 - 1) < 1e-3
+    assert W.compulsory_bytes(c2) == 4 * 16 * 1024 * 64 * 2 * 4 + 4 * 16 * 1024 * 4
+
+
+def test_generation_recipe_is_deterministic_and_shaped():
+    w = W.WORKLOADS[0]
+    a, b = W.make_inputs(w), W.make_inputs(w)
+    assert torch.equal(a.q, b.q) and torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+    assert a.q.dtype == torch.bfloat16 and tuple(a.q.shape) == (1, 2, 256, 64)
+    assert a.kv_lens is None and math.isclose(a.scale, 0.125)
+    # The recipe: Q, K, V in that order from seed 1000 + index, fp32 then bf16.
+    g = torch.Generator().manual_seed(1000)
+    q = torch.randn(1, 2, 256, 64, generator=g).to(torch.bfloat16)
+    assert torch.equal(q, a.q)
+
+
+def test_random_case_ragged_lengths_in_range():
+    c = W.random_case(3, 5, 4, 2, 3, 40, 64, kv_lens="ragged")
+    assert c.kv_lens.dtype == torch.int32 and c.kv_lens.shape == (5,)
+    assert int(c.kv_lens.min()) >= 0 and int(c.kv_lens.max()) <= 40
