@@ -1,0 +1,214 @@
+"""Benchmark of the attention forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
+                [--cpu-seconds S] [--no-cpu] [--copy-calibration-mib M]
+
+A step is one fa_fwd call over one batch of the workload's seeded synthetic
+input, resident in HBM before timing starts.  The headline workload is the
+non-causal prefill B=4, Hq=Hkv=16, Lq=Lk=1024, D=64; the causal, long-context
+GQA and split-KV decode workloads are timed the same way and reported under
+"workloads".  Time is taken with HIP events on the stream the kernels are
+launched on (torch's current stream), bracketed by device synchronisation.
+
+Printed: one JSON line with the metric, throughput, a roofline object for the
+dominant kernel of the headline workload and a CPU baseline (the fp64 oracle
+timed on this host on a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import glob
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % of MI355X bf16 MFMA peak; decode HBM GB/s & % peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+HEADLINE = "prefill_b4_h16_l1024_d64"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; a stored traffic figure is only reported for
+    the exact sources its counters were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_07_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def time_workload(w, steps, warmup, dev):
+    import torch
+    from exact_attention_07_amd import binding, workloads as W
+
+    inp = W.make_inputs(w)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    kl = None if inp.kv_lens is None else inp.kv_lens.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.Lq, dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        binding.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=kl)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        binding.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=kl)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = W.algorithmic_flops(w, inp.kv_lens)
+    nbytes = W.compulsory_bytes(w, inp.kv_lens)
+    rec = {"ms_per_step": ms, "flops": flops, "bytes": nbytes,
+           "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9}
+    if w.Lq == 1:
+        rec.update(bound="hbm", frac=rec["gbs"] / PEAK_HBM_GBS)
+    else:
+        rec.update(bound="mfma", frac=rec["tflops"] / PEAK_BF16_TFLOPS)
+    del q, k, v, o, lse, kl
+    torch.cuda.empty_cache()
+    return rec, inp
+
+
+def cpu_baseline(w, inp, seconds):
+    """Time the fp64 oracle on (b, h) heads of the workload until about
+    ``seconds`` of CPU work; report the oracle's algorithmic TFLOP/s (or GB/s)."""
+    import numpy as np
+    import oracle
+    from exact_attention_07_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        threads = os.cpu_count() or 1
+    ns = W.valid_lengths(w, inp.kv_lens)
+    done_flops = done_bytes = 0
+    heads = 0
+    t0 = time.perf_counter()
+    total_heads = w.B * w.Hq
+    for idx in range(total_heads):
+        b, h = divmod(idx, w.Hq)
+        oracle.attention_rows(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens, b, h)
+        pairs = W.allowed_pairs(w.Lq, ns[b], w.causal)
+        done_flops += 4 * w.D * pairs
+        done_bytes += (2 * w.Lq * w.D * 2 + w.Lq * 4) + 2 * ns[b] * w.D * 2 // (w.Hq // w.Hkv)
+        heads += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    sample = f"{heads} of {total_heads} (batch, query head) units, all rows, fp64, {dt:.1f} s"
+    if w.Lq == 1:
+        return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": sample}
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample}
+
+
+def copy_calibration(mib, dev):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {n} bytes read, {n} bytes written", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the forward of one GPU's share is the unit measured; "
+              "multi-GPU runs are not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_attention_07_amd import binding, workloads as W
+
+    binding.load_library()   # raises if libfa.so is not built: there is no fallback path
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, dev)
+
+    head = W.BY_NAME[args.workload]
+    print(f"[bench] timing {head.name}: warmup {args.warmup}, steps {args.steps}", flush=True)
+    rec, inp = time_workload(head, args.steps, args.warmup, dev)
+    print(f"[bench] {head.name}: {rec['ms_per_step'] * 1e3:.1f} us/step", flush=True)
+
+    extra = {}
+    if not args.no_extra:
+        for w in W.WORKLOADS[1:]:
+            if w.name == head.name:
+                continue
+            steps = max(3, min(args.steps, 20))
+            r, _ = time_workload(w, steps, max(2, min(args.warmup, 5)), dev)
+            extra[w.name] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+            print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.1f} us/step, "
+                  f"{r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s", flush=True)
+
+    decode = head.Lq == 1
+    value = rec["gbs"] if decode else rec["tflops"]
+    unit = "GB/s" if decode else "TFLOP/s"
+    traffic = stored_traffic(head.name)
+    roof = {"bound": rec["bound"], "achieved": round(value, 3),
+            "peak": PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS,
+            "unit": unit, "frac": round(rec["frac"], 4), "traffic": traffic}
+    cpu = None
+    if not args.no_cpu:
+        print(f"[bench] CPU oracle baseline on {head.name} (~{args.cpu_seconds:.0f} s)", flush=True)
+        cpu = cpu_baseline(head, inp, args.cpu_seconds)
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(rec["ms_per_step"], 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs)",
+        "config": {"workload": head.name, "B": head.B, "Hq": head.Hq, "Hkv": head.Hkv,
+                   "Lq": head.Lq, "Lk": head.Lk, "D": head.D, "causal": head.causal,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "workloads": extra,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

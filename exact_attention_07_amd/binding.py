@@ -1,0 +1,121 @@
+"""ctypes binding of libfa.so: argument marshalling only.
+
+Every step of the attention forward runs in the library's HIP kernels; this
+module checks tensor properties, allocates outputs with torch when the caller
+does not pass them, and forwards raw device pointers and sizes to the C ABI
+declared in include/fa.h.  There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+# Every entry point declared in include/fa.h.
+EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_workspace_bytes", "fa_status_string", "fa_last_error")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FaError(-1, f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fwd_args = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp]
+    lib.fa_fwd.argtypes = fwd_args
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_splits.argtypes = fwd_args + [i32]
+    lib.fa_fwd_splits.restype = i32
+    lib.fa_workspace_bytes.argtypes = [i32] * 6
+    lib.fa_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def fa_workspace_bytes(B, Hq, Hkv, Lq, Lk, D) -> int:
+    return int(load_library().fa_workspace_bytes(B, Hq, Hkv, Lq, Lk, D))
+
+
+def _check(status: int):
+    if status != FA_OK:
+        lib = load_library()
+        raise FaError(status, f"{lib.fa_status_string(status).decode()}: {lib.fa_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _prepare(q, k, v, o, lse, kv_lens, want_lse):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 tensor [B, H, L, D]")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, Lk, D] with the batch and D of q")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device=q.device)
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or kv_lens.device != q.device or kv_lens.numel() != B \
+                or not kv_lens.is_contiguous():
+            raise ValueError("kv_lens must be a contiguous int32 device tensor of B entries")
+    return o, lse, (B, Hq, Hkv, Lq, Lk, D)
+
+
+def fa_fwd(q, k, v, o=None, lse=None, *, causal=False, scale=None, kv_lens=None,
+           stream=None, want_lse=True):
+    """O, LSE = attention(q, k, v) through ``fa_fwd``; returns (o, lse)."""
+    o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    lib = load_library()
+    _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
+                      int(bool(causal)), scale, _ptr(kv_lens), s))
+    return o, lse
+
+
+def fa_fwd_splits(q, k, v, num_splits, o=None, lse=None, *, causal=False, scale=None,
+                  kv_lens=None, stream=None, want_lse=True):
+    """Same as fa_fwd through the split-KV path with at most ``num_splits`` partitions."""
+    o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    lib = load_library()
+    _check(lib.fa_fwd_splits(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk,
+                             D, int(bool(causal)), scale, _ptr(kv_lens), s, int(num_splits)))
+    return o, lse

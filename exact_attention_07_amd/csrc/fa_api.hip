@@ -1,0 +1,250 @@
+// C ABI of libfa: host-side validation, path choice, workspace and launches.
+// The operation and the contract of every entry point are documented in
+// include/fa.h.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+constexpr int kTileKeys = 32;          // split-KV partitions are multiples of one 32-key tile
+constexpr int kMaxDevices = 64;
+
+struct Shape {
+    int B, Hq, Hkv, Lq, Lk, D;
+};
+
+// Host-only argument checks shared by every entry point.
+int validate_shape(const Shape& s) {
+    if (s.B <= 0 || s.Hq <= 0 || s.Hkv <= 0 || s.Lq <= 0 || s.D <= 0 || s.Lk < 0)
+        return fail(FA_ERR_INVALID_ARG, "sizes must be positive (Lk may be 0): B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d",
+                    s.B, s.Hq, s.Hkv, s.Lq, s.Lk, s.D);
+    if (s.Hq % s.Hkv != 0)
+        return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", s.Hq, s.Hkv);
+    if (s.D != 64 && s.D != 128)
+        return fail(FA_ERR_UNSUPPORTED, "head dimension D=%d is not supported (64 or 128)", s.D);
+    const long long qrows = (long long)s.B * s.Hq * s.Lq;
+    const long long kvrows = (long long)s.B * s.Hkv * s.Lk;
+    if ((long long)s.Lq * s.D > INT32_MAX || (long long)s.Lk * s.D > INT32_MAX ||
+        qrows > INT32_MAX || kvrows > INT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for 32-bit row indexing");
+    return FA_OK;
+}
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const Shape& s, int causal, float scale, const int* kv_lens) {
+    int st = validate_shape(s);
+    if (st != FA_OK) return st;
+    if (!q || !o) return fail(FA_ERR_INVALID_ARG, "q and o must not be NULL");
+    if (s.Lk > 0 && (!k || !v)) return fail(FA_ERR_INVALID_ARG, "k and v must not be NULL when Lk > 0");
+    if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
+        return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if ((lse && !aligned(lse, 4)) || (kv_lens && !aligned(kv_lens, 4)))
+        return fail(FA_ERR_INVALID_ARG, "lse and kv_lens must be 4-byte aligned");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(scale) || !(scale > 0.0f))
+        return fail(FA_ERR_INVALID_ARG, "scale must be finite and positive");
+    return FA_OK;
+}
+
+struct SplitPlan {
+    int num_splits;  // partitions per sequence
+    int chunk;       // keys per partition
+    int n_groups;    // 32-row groups per KV head
+};
+
+int cu_count() {
+    static int cached = 0;
+    if (cached > 0) return cached;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        cached = n;
+    return cached > 0 ? cached : 256;
+}
+
+SplitPlan plan_splits(const Shape& s, int requested, int cus) {
+    SplitPlan pl;
+    const int rows = (s.Hq / s.Hkv) * s.Lq;
+    pl.n_groups = (rows + 31) / 32;
+    const int tiles = (s.Lk + kTileKeys - 1) / kTileKeys;
+    int want;
+    if (requested > 0) {
+        want = requested;
+    } else {
+        // Partitions of about 256 keys bound the time of the longest wavefront;
+        // more partitions when the batch alone cannot fill the GPU (8 waves per CU).
+        const long long units = (long long)s.B * s.Hkv * pl.n_groups;
+        const long long by_len = (s.Lk + 255) / 256;
+        const long long by_fill = (8LL * cus + units - 1) / units;
+        want = (int)(by_len > by_fill ? by_len : by_fill);
+    }
+    if (want > tiles) want = tiles;
+    if (want < 1) want = 1;
+    const int tiles_per = tiles > 0 ? (tiles + want - 1) / want : 1;
+    pl.chunk = tiles_per * kTileKeys;
+    pl.num_splits = s.Lk > 0 ? (s.Lk + pl.chunk - 1) / pl.chunk : 1;
+    return pl;
+}
+
+size_t split_workspace_bytes(const Shape& s, const SplitPlan& pl) {
+    const size_t rows = (size_t)s.B * s.Hq * s.Lq;
+    return rows * pl.num_splits * ((size_t)s.D + 1) * sizeof(float);
+}
+
+bool use_split_path(const Shape& s, int requested) {
+    if (requested > 0) return true;
+    return s.Lq == 1;
+}
+
+// Library-held split-KV workspace, one per device, grown on demand.
+std::mutex g_ws_mutex;
+void* g_ws_ptr[kMaxDevices] = {};
+size_t g_ws_size[kMaxDevices] = {};
+
+int get_workspace(size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (g_ws_size[dev] < bytes) {
+        if (g_ws_ptr[dev]) {
+            e = hipDeviceSynchronize();   // earlier launches may still read the old buffer
+            if (e != hipSuccess) return fail(FA_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+            (void)hipFree(g_ws_ptr[dev]);
+            g_ws_ptr[dev] = nullptr;
+            g_ws_size[dev] = 0;
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) return fail(FA_ERR_HIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+        g_ws_ptr[dev] = p;
+        g_ws_size[dev] = bytes;
+    }
+    *out = g_ws_ptr[dev];
+    return FA_OK;
+}
+
+int run(const void* q, const void* k, const void* v, void* o, float* lse, const Shape& s,
+        int causal, float scale, const int* kv_lens, void* stream_ptr, int requested_splits) {
+    int st = validate(q, k, v, o, lse, s, causal, scale, kv_lens);
+    if (st != FA_OK) return st;
+    if (requested_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    const float c = scale * 1.4426950408889634f;  // scale * log2(e)
+    const int r = s.Hq / s.Hkv;
+    const auto* qb = static_cast<const __bf16*>(q);
+    const auto* kb = static_cast<const __bf16*>(k);
+    const auto* vb = static_cast<const __bf16*>(v);
+    auto* ob = static_cast<__bf16*>(o);
+
+    if (!use_split_path(s, requested_splits)) {
+        fa::PrefillParams p;
+        p.q = qb; p.k = kb; p.v = vb; p.o = ob; p.lse = lse; p.kv_lens = kv_lens;
+        p.B = s.B; p.Hq = s.Hq; p.Hkv = s.Hkv; p.Lq = s.Lq; p.Lk = s.Lk;
+        p.r = r;
+        p.n_qblocks = (s.Lq + 127) / 128;
+        const int units = s.B * s.Hkv;
+        p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+        p.scale = scale;
+        p.c = c;
+        const long long total = (long long)s.B * s.Hq * p.n_qblocks;
+        if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+        hipError_t e = fa::launch_prefill(s.D, causal != 0, p, stream);
+        if (e != hipSuccess) return fail(FA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+        return FA_OK;
+    }
+
+    const SplitPlan pl = plan_splits(s, requested_splits, cu_count());
+    void* ws = nullptr;
+    st = get_workspace(split_workspace_bytes(s, pl), &ws);
+    if (st != FA_OK) return st;
+    const size_t rows = (size_t)s.B * s.Hq * s.Lq;
+    float* part_o = static_cast<float*>(ws);
+    float* part_lse = part_o + rows * pl.num_splits * s.D;
+
+    fa::SplitParams sp;
+    sp.q = qb; sp.k = kb; sp.v = vb; sp.part_o = part_o; sp.part_lse = part_lse;
+    sp.kv_lens = kv_lens;
+    sp.B = s.B; sp.Hq = s.Hq; sp.Hkv = s.Hkv; sp.Lq = s.Lq; sp.Lk = s.Lk;
+    sp.r = r; sp.rows = r * s.Lq; sp.n_groups = pl.n_groups;
+    sp.num_splits = pl.num_splits; sp.chunk = pl.chunk; sp.causal = causal; sp.c = c;
+    const long long total = (long long)s.B * s.Hkv * pl.n_groups * pl.num_splits;
+    if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    hipError_t e = fa::launch_splitkv(s.D, sp, stream);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "split-KV launch: %s", hipGetErrorString(e));
+
+    fa::CombineParams cp;
+    cp.part_o = part_o; cp.part_lse = part_lse; cp.o = ob; cp.lse = lse; cp.kv_lens = kv_lens;
+    cp.B = s.B; cp.Hq = s.Hq; cp.Lq = s.Lq; cp.Lk = s.Lk;
+    cp.num_splits = pl.num_splits; cp.chunk = pl.chunk;
+    e = fa::launch_combine(s.D, cp, stream);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Lq, int Lk, int D,
+           int causal, float scale, const int* kv_lens, void* stream) {
+    g_last_error[0] = '\0';
+    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream, 0);
+}
+
+int fa_fwd_splits(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                  int causal, float scale, const int* kv_lens, void* stream,
+                  int num_splits) {
+    g_last_error[0] = '\0';
+    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream,
+               num_splits);
+}
+
+size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
+    const Shape s{B, Hq, Hkv, Lq, Lk, D};
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    const int st = validate_shape(s);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != FA_OK || !use_split_path(s, 0)) return 0;
+    return split_workspace_bytes(s, plan_splits(s, 0, cu_count()));
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid but unsupported configuration";
+        case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime or launch failure";
+        default: return "unknown fa_status";
+    }
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

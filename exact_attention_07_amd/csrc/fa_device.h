@@ -1,0 +1,76 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Register layouts of the bf16 MFMA used here (v_mfma_f32_32x32x16_bf16, one
+// wave64, D[32x32] += A[32x16] * B[16x32]):
+//   A operand : lane l holds row (l % 32), k = 8 * (l / 32) + e, e = 0..7
+//   B operand : lane l holds column (l % 32), k = 8 * (l / 32) + e
+//   C / D     : lane l holds column (l % 32), rows 8 * (v / 4) + 4 * (l / 32) + (v % 4),
+//               v = 0..15
+// Every lane of these layouts is exercised by the parity tests.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309417232121458176568f;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane (l ^ 32): v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second; with both operands x,
+// result[0] is x[l - 32] on the upper lanes and result[1] is x[l + 32] on the
+// lower lanes.
+__device__ __forceinline__ float lane_xor32(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned lane = __lane_id();
+    return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// Key-row permutation that makes the S^T accumulator of one 32-key block line
+// up with the B operand of the PV product: swap bits 2 and 3 of the row.
+// Accumulator entry v of lane l then holds key 16*(v/8) + 8*(l/32) + (v%8).
+__device__ __forceinline__ int swap_bits_2_3(int i) {
+    return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    bf16x8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+    return z;
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+    f32x16 z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+    return z;
+}
+
+// Eight fp32 values to bf16, round to nearest even.
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
+                                            float a4, float a5, float a6, float a7) {
+    bf16x8 r;
+    r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+    r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+    return r;
+}
+
+}  // namespace fa

@@ -1,0 +1,57 @@
+// Host-side launch parameters shared by the API layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct PrefillParams {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    __bf16* o;
+    float* lse;            // may be null
+    const int* kv_lens;    // may be null
+    int B, Hq, Hkv, Lq, Lk;
+    int r;                 // query heads per KV head
+    int n_qblocks;         // ceil(Lq / 128)
+    int xcd_units;         // (B * Hkv) / 8 when divisible by 8, else 0
+    float scale;           // softmax scale
+    float c;               // scale * log2(e): scores enter exp2 as s * c
+};
+
+struct SplitParams {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    float* part_o;         // [B * Hq * Lq, num_splits, D] fp32, normalised partial outputs
+    float* part_lse;       // [B * Hq * Lq, num_splits] fp32, base-2 log-sum-exp of each partial
+    const int* kv_lens;
+    int B, Hq, Hkv, Lq, Lk;
+    int r;
+    int rows;              // r * Lq packed rows per KV head
+    int n_groups;          // ceil(rows / 32)
+    int num_splits;        // partitions per sequence
+    int chunk;             // keys per partition (multiple of 32)
+    int causal;
+    float c;
+};
+
+struct CombineParams {
+    const float* part_o;
+    const float* part_lse;
+    __bf16* o;
+    float* lse;            // may be null
+    const int* kv_lens;
+    int B, Hq, Lq, Lk;
+    int num_splits;
+    int chunk;
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
+hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream);
+hipError_t launch_splitkv(int D, const SplitParams& p, hipStream_t stream);
+hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,110 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) FlashAttention forward library (libfa.so).
+ *
+ * The operation (FlashAttention from Scratch, ryhuang.blog, section 2 "Begin
+ * with one attention row"; FlashAttention Cheat Sheet, mxino.github.io,
+ * section 1 "The whole operation"): for every batch b, query head h and query
+ * row i,
+ *
+ *     O[b,h,i,:] = sum_j P_ij V[b,g,j,:],  P_ij = softmax_j(scale * Q[b,h,i,:] . K[b,g,j,:] + M_ij)
+ *     LSE[b,h,i] = log sum_j exp(scale * Q[b,h,i,:] . K[b,g,j,:] + M_ij)   (natural log)
+ *
+ * with g = floor(h / (Hq / Hkv)) (grouped-query attention: FlashAttention
+ * from Scratch, section 9.2) and M_ij in {0, -inf}.  The only masks are:
+ *   - length: key j is valid iff j < n_b, where n_b = kv_lens[b] clamped to
+ *     [0, Lk] (or Lk when kv_lens is NULL);
+ *   - causal (optional): bottom-right alignment, query i sits at absolute
+ *     position n_b - Lq + i and sees keys j <= that position (FlashAttention
+ *     from Scratch, section 5, "Rectangular causal masking is a correctness
+ *     issue").
+ * A row with no allowed key returns O = 0 and LSE = -inf (same page, section
+ * 4.4 "Handle the empty state deliberately").
+ *
+ * The result is computed tile by tile with the online-softmax recurrence
+ * (running max, running sum, rescaled accumulator; same page, section 4.1;
+ * Cheat Sheet, section 5) so the Lq x Lk score matrix never reaches HBM.
+ * Both matrix products run on bf16 MFMA with fp32 accumulation.
+ *
+ * Memory layout and ownership (all entry points):
+ *   q   : bf16, device, contiguous [B, Hq,  Lq, D]
+ *   k, v: bf16, device, contiguous [B, Hkv, Lk, D]; Lk is the per-sequence
+ *         row capacity (stride); only the first n_b rows of each sequence are
+ *         read, rows >= n_b may hold anything (even NaN)
+ *   o   : bf16, device, contiguous [B, Hq, Lq, D], written
+ *   lse : fp32, device, contiguous [B, Hq, Lq], written; may be NULL
+ *   kv_lens : int32, device, [B], or NULL
+ *   stream  : a hipStream_t (NULL = the null stream)
+ * q, k, v and o must be 16-byte aligned; lse and kv_lens 4-byte aligned.
+ * The caller owns every buffer; the library keeps no pointer after return.
+ * All work is enqueued on `stream`; the call returns without synchronising and
+ * the outputs are valid once the stream has reached that point.
+ *
+ * Errors: arguments are validated on the host before any HIP call.  A failed
+ * validation returns FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED and enqueues
+ * nothing.  A HIP failure (launch, allocation) returns FA_ERR_HIP.
+ * fa_last_error() describes the most recent failure on the calling thread.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad alignment, bad scale, Hq % Hkv != 0 */
+    FA_ERR_UNSUPPORTED = 2,  /* valid but not implemented: D not in {64, 128} */
+    FA_ERR_HIP = 3           /* a HIP runtime call or a kernel launch failed */
+} fa_status;
+
+/*
+ * Attention forward.  Returns an fa_status.
+ *   B, Hq, Hkv, Lq, D > 0; Lk >= 0; Hq % Hkv == 0; D in {64, 128};
+ *   causal: 0 or 1; scale: finite and > 0 (the usual choice is 1/sqrt(D)).
+ * Path choice: when Lq == 1 (single-token decode) the split-KV path runs
+ * (Flash-Decoding, FlashAttention from Scratch section 9.1): the valid keys
+ * of each sequence are cut into partitions, each partition's normalised
+ * output and LSE go to a library-held workspace, and a second kernel merges
+ * them by their LSEs (section 4.3).  Otherwise one workgroup per (batch,
+ * query head, 128-row query block) runs the whole KV loop on chip.
+ * The split-KV workspace is allocated by the library on first need per
+ * device and grown (synchronously, with a device synchronisation) when a
+ * larger one is needed; concurrent split-KV calls on different streams of
+ * one device share it and must not overlap.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Lq, int Lk, int D,
+           int causal, float scale, const int* kv_lens, void* stream);
+
+/*
+ * Same operation, forcing the split-KV path for any Lq with at most
+ * num_splits partitions per sequence (num_splits >= 1).  Partition s covers
+ * keys [s*C, (s+1)*C) of each sequence, C = 32 * ceil(ceil(Lk/32) / num_splits);
+ * partitions past n_b are empty.  Any partition count gives the same exact
+ * result (section 4.3); num_splits == 0 behaves exactly like fa_fwd.
+ * Query heads that share a KV head are packed, with their query rows, into
+ * the 32 columns of one matrix-core tile (section 9.2).
+ */
+int fa_fwd_splits(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                  int causal, float scale, const int* kv_lens, void* stream,
+                  int num_splits);
+
+/* Bytes of split-KV workspace fa_fwd would use for this shape (0 when it
+ * takes the prefill path, or for invalid sizes). */
+size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);
+
+/* Static text for a status code. */
+const char* fa_status_string(int status);
+
+/* Text describing the most recent failed call on this thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

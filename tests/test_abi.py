@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: every declared symbol is exported, and host
+validation rejects bad arguments with the documented status before any HIP
+call (the pointers passed here are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_07_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from exact_attention_07_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_entry_points():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libfa.so"
+
+
+P = ctypes.c_void_p(1 << 20)   # 16-byte aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p((1 << 20) + 2)
+
+
+def call(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Lq=4, Lk=8, D=64, causal=0,
+         scale=0.125, kv_lens=None, splits=None):
+    args = [q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, causal, ctypes.c_float(scale), kv_lens, None]
+    if splits is None:
+        return lib.fa_fwd(*args)
+    return lib.fa_fwd_splits(*args, splits)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(k=None), binding.FA_ERR_INVALID_ARG),
+    (dict(B=0), binding.FA_ERR_INVALID_ARG),
+    (dict(Lq=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(Lk=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), binding.FA_ERR_INVALID_ARG),
+    (dict(D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(D=256), binding.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), binding.FA_ERR_INVALID_ARG),
+    (dict(q=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(v=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=ctypes.c_void_p((1 << 20) + 1)), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+    (dict(splits=-1, D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(Lq=1 << 20, D=128, Lk=1 << 15, B=1 << 12), binding.FA_ERR_INVALID_ARG),
+])
+def test_validation_rejects_before_any_launch(lib, kw, status):
+    got = call(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_negative_split_count_is_rejected(lib):
+    # Sizes are valid, so validation reaches the split-count check; it fails before launching.
+    assert call(lib, splits=-3) == binding.FA_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    assert lib.fa_status_string(0).decode() == "FA_OK"
+    for s in (1, 2, 3):
+        assert lib.fa_status_string(s).decode().startswith("FA_ERR_")
+    assert lib.fa_status_string(99).decode() == "unknown fa_status"
+
+
+def test_workspace_bytes(lib):
+    # Prefill shapes use no workspace; invalid shapes report 0.
+    assert lib.fa_workspace_bytes(4, 16, 16, 1024, 1024, 64) == 0
+    assert lib.fa_workspace_bytes(1, 3, 2, 1, 8, 64) == 0
+    # Decode: rows * splits * (D + 1) * 4 bytes, splits >= 1.
+    ws = lib.fa_workspace_bytes(64, 32, 8, 1, 8192, 128)
+    rows = 64 * 32
+    assert ws > 0 and ws % (rows * 129 * 4) == 0
+    assert ws // (rows * 129 * 4) <= 8192 // 32
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding._prepare(q, q, q, None, None, None, True)

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Inputs are the seeded workloads (every config at its full size, compared on
+all outputs or on sampled rows the oracle computes one by one) and seeded
+small cases that span several tiles with ragged tails, plus the edge cases of
+the method: empty and fully masked rows, more queries than keys, zero-length
+sequences, NaN in the padding past a sequence's length, large scores, the
+pages' hand examples, and split-count invariance of the split-KV path.
+Tolerances and the bf16 representability floor are defined in parity.py.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_07_amd import binding, workloads as W
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity import compare, sample_rows  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    if not os.path.exists(binding.LIB_PATH):
+        from exact_attention_07_amd import build
+        build.build()
+    binding.load_library()
+    return torch.device("cuda:0")
+
+
+def to_dev(case, dev):
+    kl = None if case.kv_lens is None else case.kv_lens.to(dev)
+    return case.q.to(dev), case.k.to(dev), case.v.to(dev), kl
+
+
+def run(case, dev, splits=None, k=None, v=None):
+    q, kd, vd, kl = to_dev(case, dev)
+    if k is not None:
+        kd, vd = k.to(dev), v.to(dev)
+    if splits is None:
+        o, lse = binding.fa_fwd(q, kd, vd, causal=case.causal, scale=case.scale, kv_lens=kl)
+    else:
+        o, lse = binding.fa_fwd_splits(q, kd, vd, splits, causal=case.causal, scale=case.scale,
+                                       kv_lens=kl)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def full_reference(case):
+    return oracle.attention_forward(case.q, case.k, case.v, case.scale, case.causal, case.kv_lens)
+
+
+def report(name, metrics):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}"
+                                          for k, v in metrics.items()), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_workload_tiny(dev):
+    case = W.make_inputs(W.WORKLOADS[0])
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report("tiny", compare(o, lse, ref_o, ref_lse))
+
+
+def test_workload_prefill_1k(dev):
+    case = W.make_inputs(W.WORKLOADS[1])
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report("prefill_1k", compare(o, lse, ref_o, ref_lse))
+
+
+@pytest.mark.parametrize("index", [2, 3])
+def test_workload_causal_sampled(dev, index):
+    w = W.WORKLOADS[index]
+    case = W.make_inputs(w)
+    o, lse = run(case, dev)
+    rows = sample_rows(w.Lq, seed=index)
+    go, gl, ro, rl = [], [], [], []
+    for b in range(w.B):
+        for h in range(w.Hq):
+            ref_o, ref_lse = oracle.attention_rows(case.q, case.k, case.v, case.scale, True,
+                                                   case.kv_lens, b, h, rows)
+            go.append(o[b, h, rows]); gl.append(lse[b, h, rows]); ro.append(ref_o); rl.append(ref_lse)
+    metrics = compare(torch.stack(go), torch.stack(gl), np.stack(ro), np.stack(rl))
+    report(w.name, metrics)
+
+
+def test_workload_decode(dev):
+    w = W.WORKLOADS[4]
+    case = W.make_inputs(w)
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report(w.name, compare(o, lse, ref_o, ref_lse))
+
+
+# ---------------------------------------------------------------------------
+# Small seeded cases: several tiles, ragged tails, GQA, lengths
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # B, Hq, Hkv, Lq, Lk, D, causal, kv_lens
+    (2, 4, 2, 300, 333, 64, False, None),
+    (2, 4, 2, 300, 333, 64, True, None),
+    (2, 4, 2, 300, 333, 128, False, None),
+    (2, 4, 2, 300, 333, 128, True, None),
+    (3, 6, 3, 129, 257, 128, True, "ragged"),
+    (3, 8, 1, 65, 190, 64, False, "ragged"),
+    (1, 2, 2, 257, 64, 128, True, None),          # more queries than keys: leading rows empty
+    (2, 2, 1, 1, 1000, 128, False, [1000, 37]),   # decode through the split path
+    (4, 8, 2, 1, 515, 64, True, "ragged"),        # decode, causal (same as non-causal at Lq = 1)
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:6])) + f"_c{int(s[6])}_{s[7] is not None}")
+def test_small_cases(dev, shape):
+    B, Hq, Hkv, Lq, Lk, D, causal, lens = shape
+    case = W.random_case(100 + Lq + Lk + D, B, Hq, Hkv, Lq, Lk, D, causal, lens)
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report(str(shape), compare(o, lse, ref_o, ref_lse))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 1, 777, 128, False, "ragged"),
+                                   (1, 4, 4, 45, 300, 64, True, None),
+                                   (2, 4, 1, 9, 200, 128, True, [200, 150])])
+def test_split_path_any_partition_count(dev, shape, splits):
+    B, Hq, Hkv, Lq, Lk, D, causal, lens = shape
+    case = W.random_case(7 + splits, B, Hq, Hkv, Lq, Lk, D, causal, lens)
+    o, lse = run(case, dev, splits=splits)
+    ref_o, ref_lse = full_reference(case)
+    report(f"splits={splits} {shape}", compare(o, lse, ref_o, ref_lse))
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+def test_zero_length_sequences_give_zero_and_minus_inf(dev):
+    for Lq in (1, 70):
+        case = W.random_case(5, 3, 4, 2, Lq, 96, 64, False, [0, 96, 0])
+        o, lse = run(case, dev)
+        assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
+        assert torch.all(lse[0] == -math.inf) and torch.all(lse[2] == -math.inf)
+        ref_o, ref_lse = full_reference(case)
+        compare(o, lse, ref_o, ref_lse)
+
+
+def test_nan_padding_past_length_is_never_read(dev):
+    case = W.random_case(9, 2, 4, 2, 1, 512, 128, False, [300, 77])
+    k, v = case.k.clone(), case.v.clone()
+    k[0, :, 300:] = float("nan"); v[0, :, 300:] = float("nan")
+    k[1, :, 77:] = float("nan"); v[1, :, 77:] = float("nan")
+    o_clean, l_clean = run(case, dev)
+    o_nan, l_nan = run(case, dev, k=k, v=v)
+    assert torch.equal(o_clean, o_nan) and torch.equal(l_clean, l_nan)
+    prefill = W.random_case(9, 2, 4, 2, 150, 512, 64, True, [300, 200])
+    k, v = prefill.k.clone(), prefill.v.clone()
+    k[0, :, 300:] = float("nan"); v[0, :, 300:] = float("nan")
+    k[1, :, 200:] = float("nan"); v[1, :, 200:] = float("nan")
+    o_nan, l_nan = run(prefill, dev, k=k, v=v)
+    ref_o, ref_lse = full_reference(prefill)
+    compare(o_nan, l_nan, ref_o, ref_lse)
+
+
+def test_large_scores(dev):
+    # Q and K multiplied by 20 (FlashAttention from Scratch, section 5 experiment).
+    case = W.random_case(21, 1, 2, 2, 200, 300, 64, True, None, q_mult=20.0, k_mult=20.0)
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report("x20", compare(o, lse, ref_o, ref_lse))
+
+
+def test_causal_row_zero_is_value_row_zero_exactly(dev):
+    case = W.random_case(4, 2, 4, 2, 256, 256, 128, True, None)
+    o, _ = run(case, dev)
+    for h in range(4):
+        assert torch.equal(o[:, h, 0], case.v[:, h // 2, 0])
+
+
+def _hand_case(scores, values, D=64, offset=0.0):
+    """One query whose scores at scale 1 are ``offset + scores``: q = e0 + e1,
+    k_j = offset e0 + s_j e1 (1000 and small integers are exact in bf16 and
+    the products are exact in fp32).  Values are put on every column and
+    divided by 64 so they are exact in bf16 and the bf16 output floor stays
+    well below the tolerance."""
+    n = len(scores)
+    q = torch.zeros(1, 1, 1, D)
+    q[..., 0] = 1.0
+    q[..., 1] = 1.0
+    k = torch.zeros(1, 1, n, D)
+    k[0, 0, :, 0] = offset
+    k[0, 0, :, 1] = torch.tensor(scores)
+    v = (torch.tensor(values, dtype=torch.float32) / 64.0)[:, None].expand(n, D).reshape(1, 1, n, D)
+    return W.Inputs(q.to(torch.bfloat16), k.to(torch.bfloat16), v.contiguous().to(torch.bfloat16),
+                    None, 1.0, False)
+
+
+@pytest.mark.parametrize("splits", [None, 1, 2])
+def test_pages_hand_examples_through_the_api(dev, splits):
+    # Worked row (FlashAttention from Scratch, sections 2 and 4.2): 25.7521.
+    worked = _hand_case([1.0, 2.0, 3.0], [10.0, 20.0, 30.0])
+    o, lse = run(worked, dev, splits=splits)
+    assert abs(float(o[0, 0, 0, 0]) * 64 - 25.7521) < 64 * 4e-3
+    assert abs(float(lse[0, 0, 0]) - math.log(math.e + math.e ** 2 + math.e ** 3)) < 1e-3
+    # +1000 on every score (section 2 checkpoint): same output, LSE + 1000.
+    shifted = _hand_case([1.0, 2.0, 3.0], [10.0, 20.0, 30.0], offset=1000.0)
+    o2, lse2 = run(shifted, dev, splits=splits)
+    assert float((o2.float() - o.float()).abs().max()) <= 1e-3
+    assert abs(float(lse2[0, 0, 0]) - (1000.0 + math.log(math.e + math.e ** 2 + math.e ** 3))) < 1e-3
+    # Two-tile example (FlashAttention Cheat Sheet, section 6): 24.71.
+    two = _hand_case([2.0, 1.0, 3.0, 0.0], [10.0, 20.0, 30.0, 40.0])
+    o3, _ = run(two, dev, splits=splits)
+    assert abs(float(o3[0, 0, 0, 0]) * 64 - 24.71) < 0.02 + 64 * 4e-3
+
+
+def test_bitwise_deterministic(dev):
+    case = W.random_case(2, 2, 8, 2, 333, 500, 128, True, "ragged")
+    a = run(case, dev)
+    b = run(case, dev)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    dec = W.random_case(3, 8, 8, 2, 1, 3000, 128, False, "ragged")
+    a = run(dec, dev)
+    b = run(dec, dev)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_lse_is_optional(dev):
+    case = W.random_case(6, 1, 4, 4, 64, 64, 64, False, None)
+    q, k, v, _ = to_dev(case, dev)
+    o, lse = binding.fa_fwd(q, k, v, scale=case.scale, want_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    o_ref, _ = run(case, dev)
+    assert torch.equal(o.cpu(), o_ref)
