@@ -46,9 +46,12 @@ int validate_shape(const Shape& s) {
         return fail(FA_ERR_UNSUPPORTED, "head dimension D=%d is not supported (64 or 128)", s.D);
     const long long qrows = (long long)s.B * s.Hq * s.Lq;
     const long long kvrows = (long long)s.B * s.Hkv * s.Lk;
-    if ((long long)s.Lq * s.D > INT32_MAX || (long long)s.Lk * s.D > INT32_MAX ||
-        qrows > INT32_MAX || kvrows > INT32_MAX)
-        return fail(FA_ERR_INVALID_ARG, "problem too large for 32-bit row indexing");
+    // Per-head byte offsets (plus one tile of overshoot) must fit the 32-bit
+    // offsets of the buffer loads; row counts must fit 32-bit indices.
+    const long long head_bytes_q = ((long long)s.Lq + 256) * s.D * 2;
+    const long long head_bytes_k = ((long long)s.Lk + 256) * s.D * 2;
+    if (head_bytes_q > UINT32_MAX || head_bytes_k > UINT32_MAX || qrows > INT32_MAX || kvrows > INT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for 32-bit per-head offsets");
     return FA_OK;
 }
 

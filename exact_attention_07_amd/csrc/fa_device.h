@@ -50,6 +50,22 @@ __device__ __forceinline__ int swap_bits_2_3(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
+// Buffer resource over [base, base + bytes): a raw buffer load whose 16 bytes
+// lie past `bytes` returns zeros (hardware range check), so rows beyond a
+// sequence's valid length read as zero without a branch and are never fetched.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 load16(rsrc_t r, uint32_t byte_offset) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
+}
+
+// s_waitcnt vmcnt(0): wait for every outstanding vector-memory load of this
+// wave (expcnt and lgkmcnt left at their maxima).  Issued through the builtin
+// so the compiler's own wait-count tracking knows the loads have completed.
+__device__ __forceinline__ void wait_all_vector_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
 #pragma unroll

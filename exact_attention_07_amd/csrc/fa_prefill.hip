@@ -104,17 +104,17 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
 
     const size_t qoff = (size_t)(b * p.Hq + h) * p.Lq * D;
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
-    const bf16* __restrict__ Qp = p.q + qoff;
-    const bf16* __restrict__ Kp = p.k + kvoff;
-    const bf16* __restrict__ Vp = p.v + kvoff;
+
+    // Range-checked buffers: Q rows >= Lq and K/V rows >= n read as zero.
+    const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)p.Lq * D * 2);
+    const rsrc_t kbuf = make_rsrc(p.k + kvoff, (uint32_t)n * D * 2);
+    const rsrc_t vbuf = make_rsrc(p.v + kvoff, (uint32_t)n * D * 2);
 
     // ---- Q tile: B operand of S^T, resident in registers -------------------
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = (qrow < p.Lq)
-                     ? *reinterpret_cast<const bf16x8*>(Qp + (size_t)qrow * D + ks * 16 + hi * 8)
-                     : zero_bf16x8();
+        qf[ks] = load16(qbuf, (uint32_t)(qrow * D + ks * 16 + hi * 8) * 2);
 
     // ---- K/V tile staging: global -> registers -> LDS -----------------------
     bf16x8 kreg[KCH];
@@ -128,16 +128,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
         for (int i = 0; i < KCH; ++i) {
             const int c = tid + 256 * i;
             const int row = c / DG, col = c % DG;
-            const int key = k0 + row;
-            kreg[i] = key < n ? *reinterpret_cast<const bf16x8*>(Kp + (size_t)key * D + col * 8)
-                              : zero_bf16x8();
+            kreg[i] = load16(kbuf, (uint32_t)((k0 + row) * D + col * 8) * 2);
         }
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int key = k0 + vkg * KPT + i;   // rows past n are zero: 0 * garbage would be NaN
-            vreg[i] = key < n ? *reinterpret_cast<const bf16x8*>(Vp + (size_t)key * D + vdg * 8)
-                              : zero_bf16x8();
-        }
+        for (int i = 0; i < KPT; ++i)   // rows past n read as zero: 0 * garbage would be NaN
+            vreg[i] = load16(vbuf, (uint32_t)((k0 + vkg * KPT + i) * D + vdg * 8) * 2);
     };
     auto store_tile = [&](int buf) {
         bf16* Ks = smem + buf * BUF;
@@ -167,10 +162,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
 
     const int krow = swap_bits_2_3(l & 31);
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
+    // Prologue, unconditional: with range-checked loads an empty tile reads as
+    // zeros, and every Q load is then complete before the loop starts.
+    load_tile(0);
+    store_tile(0);
+    wait_all_vector_loads();   // Q is resident: no wait on it inside the loop
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {

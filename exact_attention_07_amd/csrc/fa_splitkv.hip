@@ -63,38 +63,33 @@ __global__ void __launch_bounds__(64) splitkv_kernel(SplitParams p) {
     const int qi = row_ok ? rho % p.Lq : 0;
     const size_t grow = (size_t)(b * p.Hq + g * p.r) * p.Lq + rho;  // row in [B*Hq*Lq]
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
-    const bf16* __restrict__ Kp = p.k + kvoff;
-    const bf16* __restrict__ Vp = p.v + kvoff;
     const int qpos = n - p.Lq + qi;         // bottom-right causal position
+    // Range-checked buffers: keys >= kend (past this partition) read as zero.
+    const rsrc_t kbuf = make_rsrc(p.k + kvoff, (uint32_t)kend * D * 2);
+    const rsrc_t vbuf = make_rsrc(p.v + kvoff, (uint32_t)kend * D * 2);
+    const size_t qbase = (size_t)(b * p.Hq + g * p.r) * p.Lq;      // first packed row of this KV head
+    const rsrc_t qbuf = make_rsrc(p.q + qbase * D, (uint32_t)p.rows * D * 2);
 
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(p.q + grow * D + ks * 16 + hi * 8)
-                        : zero_bf16x8();
+        qf[ks] = load16(qbuf, (uint32_t)(rho * D + ks * 16 + hi * 8) * 2);
 
     const int krow = swap_bits_2_3(l & 31);
     bf16x8 kreg[KS];
     bf16x8 vreg[VBLK][4];
     auto load_tile = [&](int t) {
         const int k0 = kbeg + t * 32;
-        const int key = k0 + krow;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            kreg[ks] = key < kend
-                           ? *reinterpret_cast<const bf16x8*>(Kp + (size_t)key * D + ks * 16 + hi * 8)
-                           : zero_bf16x8();
+            kreg[ks] = load16(kbuf, (uint32_t)((k0 + krow) * D + ks * 16 + hi * 8) * 2);
 #pragma unroll
         for (int i = 0; i < VBLK; ++i) {
             const int blk = l + 64 * i;
             const int dg = blk % DG, kg = blk / DG;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int vkey = k0 + kg * 4 + j;   // rows past the partition are zero
-                vreg[i][j] = vkey < kend
-                                 ? *reinterpret_cast<const bf16x8*>(Vp + (size_t)vkey * D + dg * 8)
-                                 : zero_bf16x8();
-            }
+            for (int j = 0; j < 4; ++j)   // rows past the partition read as zero
+                vreg[i][j] = load16(vbuf, (uint32_t)((k0 + kg * 4 + j) * D + dg * 8) * 2);
         }
     };
 
