@@ -25,7 +25,12 @@
 // exponentials); the LSE is converted back to natural log once
 // (LSE = (m*c + log2 l) * ln 2).  alpha = 2^((m_old - m_new) * c) rescales the
 // running sum and the accumulator; the accumulator multiply is skipped when no
-// row of the wavefront changed its max.
+// row of the wavefront changed its max.  The running max is always the true
+// max, so the largest probability of every tile is exactly 1.0 and passes
+// through the bf16 P operand unrounded.  (FA4's conditional rescaling keeps a
+// stale reference, which puts the dominant probability in (1, 256] where bf16
+// rounds it; measured on peaky rows it doubles the worst output error, so it
+// is not used.)
 //
 // Causal work (section 7.3; FlashAttention-4 summary, "LPT scheduling for
 // imbalanced grids"): KV tiles past the block's last visible key are never
@@ -119,8 +124,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
     // ---- K/V tile staging: global -> registers -> LDS -----------------------
     bf16x8 kreg[KCH];
     bf16x8 vreg[KPT];
-    const int vdg = tid % DG;               // V: this thread's 8-column group
-    const int vkg = tid / DG;               // V: this thread's KPT-key group
+    // V: this thread's KPT-key group and 8-column group.  Consecutive lanes take
+    // consecutive key groups, so one transposed LDS store of a wavefront covers
+    // contiguous bytes of V^T rows (all 64 banks, no conflicts).
+    constexpr int KG = BN / KPT;
+    const int vkg = tid % KG;
+    const int vdg = tid / KG;
 
     auto load_tile = [&](int t) {
         const int k0 = t * BN;
