@@ -46,6 +46,19 @@ __device__ __forceinline__ float lane_xor32(float x) {
 // Key-row permutation that makes the S^T accumulator of one 32-key block line
 // up with the B operand of the PV product: swap bits 2 and 3 of the row.
 // Accumulator entry v of lane l then holds key 16*(v/8) + 8*(l/32) + (v%8).
+// max(x, x of lane l ^ 32) and x + (x of lane l ^ 32): the two results of the
+// swap hold x and its partner, in an order that depends on the half.
+__device__ __forceinline__ float max_with_partner(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int swap_bits_2_3(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
@@ -65,6 +78,25 @@ __device__ __forceinline__ bf16x8 load16(rsrc_t r, uint32_t byte_offset) {
 // wave (expcnt and lgkmcnt left at their maxima).  Issued through the builtin
 // so the compiler's own wait-count tracking knows the loads have completed.
 __device__ __forceinline__ void wait_all_vector_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Direct HBM -> LDS copy of 16 bytes per lane through a range-checked buffer:
+// lane l's bytes land at lds_base + 16 * l (lane-linear), out-of-range bytes
+// arrive as zeros.  lds_base must be the same for the whole wavefront.
+__device__ __forceinline__ void load16_to_lds(rsrc_t r, uint32_t byte_offset, bf16* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_base, 16, byte_offset, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives element
+// (j % 4) of the 8-byte rows read by lanes 4k + j / 4 of its group, k = 0..3.
+// When four consecutive lanes point at four consecutive columns of one row of
+// a row-major tile, each lane gets one column of four consecutive rows.
+__device__ __forceinline__ bf16x4 lds_read_transposed(const bf16* addr) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(addr)));
+    return __builtin_bit_cast(bf16x4, v);
+}
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;

@@ -9,6 +9,15 @@
 // complete query rows (FA2's split-Q ownership, section 7.3), so no partial
 // outputs are exchanged between wavefronts.
 //
+// Pipelining (section 10.2's dependency sketch, applied on one wavefront):
+// the score product of tile t+1 is issued in the same basic block as the
+// softmax of tile t, so the matrix cores work while the vector ALUs compute
+// exponentials; K therefore runs one tile ahead of V.  K and V each have two
+// LDS buffers and are copied HBM -> LDS directly (buffer loads with the LDS
+// destination, range-checked so rows past the valid length arrive as zeros);
+// the copies for tiles t+2 (K) and t+1 (V) are issued at the top of step t
+// and waited for at its end.
+//
 // gfx950 mapping.  The score tile is computed transposed, S^T = K Q^T, on
 // v_mfma_f32_32x32x16_bf16: the accumulator puts one query per lane (column
 // l % 32) with 16 keys per 32-key block, so a row's max and sum are in-lane
@@ -16,9 +25,10 @@
 // state (m, l) is one scalar per lane.  K rows are fed to the MFMA through the
 // bit-2/3 swap of fa_device.h, which makes the S^T accumulator, converted to
 // bf16, exactly the B operand (P^T, keys as the reduction index) of the second
-// product O^T += V^T P^T: the probabilities never leave registers.  V is
-// transposed once per tile while it is written to LDS so that each lane's
-// A-operand read of V^T is one 16-byte LDS load.
+// product O^T += V^T P^T: the probabilities never leave registers.  V stays
+// row-major in LDS; its A-operand fragments (four keys of one column per read)
+// come from ds_read_b64_tr_b16, the gfx950 transposing LDS read.  Both tiles
+// are XOR-swizzled in 16-byte units so every LDS read is bank-conflict-free.
 //
 // Softmax in base 2 with the scale folded into the exponent: p = 2^(s*c - m*c),
 // c = scale * log2(e) (FlashAttention from Scratch, section 6.3, base-2
@@ -46,26 +56,36 @@
 
 namespace fa {
 
-template <int D, int BN, bool CAUSAL>
+// 16-byte-chunk XOR swizzles of the K and V tiles in LDS (row-major, D
+// columns).  K is read one row per lane (16 consecutive lanes: 16 distinct
+// rows, one chunk column); V is read by ds_read_b64_tr_b16 (32 lanes: 4 rows x
+// 4 chunks).  Either way the chosen XOR spreads each batch of lanes over all
+// 64 banks.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swizzle(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+template <int N>
+struct Const { static constexpr int value = N; };
+
+template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
     constexpr int BM = 128;                 // query rows per workgroup
+    constexpr int BN = 64;                  // keys per KV tile
     constexpr int KS = D / 16;              // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;              // 32-row blocks of O^T
     constexpr int KB = BN / 32;             // 32-key blocks per KV tile
-    constexpr int KST = D + 8;              // LDS row stride of K in bf16 (16-byte pad)
-    constexpr int VST = BN + 8;             // LDS row stride of V^T in bf16
-    constexpr int BUF = BN * KST + D * VST; // one K + V^T buffer, bf16 elements
-    constexpr int DG = D / 8;               // 16-byte groups per row
-    constexpr int KCH = BN * DG / 256;      // 16-byte K chunks per thread
-    constexpr int KPT = BN * DG / 256;      // keys per thread in the V transpose
-    static_assert(KCH >= 1 && (BN * DG) % 256 == 0, "tile must split evenly over 256 threads");
-    static_assert((BN / KPT) * DG == 256, "V transpose blocks must cover the tile");
-    typedef __bf16 bf16xk __attribute__((ext_vector_type(KPT)));
+    constexpr int CH = D / 8;               // 16-byte chunks per K/V row
+    constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
+    constexpr int NI = BN * CH / 256;       // 16-byte direct copies per thread per tile
+    static_assert(NI >= 1 && (BN * CH) % 256 == 0, "a tile must split evenly over 256 threads");
 
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+    // K buffers at [0, 2 TILE), V buffers at [2 TILE, 4 TILE).
+    __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int l = tid & 63;
     const int hi = l >> 5;                  // which half of the wave (0 or 1)
 
@@ -110,165 +130,200 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
     const size_t qoff = (size_t)(b * p.Hq + h) * p.Lq * D;
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
 
-    // Range-checked buffers: Q rows >= Lq and K/V rows >= n read as zero.
-    const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)p.Lq * D * 2);
-    const rsrc_t kbuf = make_rsrc(p.k + kvoff, (uint32_t)n * D * 2);
-    const rsrc_t vbuf = make_rsrc(p.v + kvoff, (uint32_t)n * D * 2);
-
     // ---- Q tile: B operand of S^T, resident in registers -------------------
+    const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)p.Lq * D * 2);   // rows >= Lq read as zero
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         qf[ks] = load16(qbuf, (uint32_t)(qrow * D + ks * 16 + hi * 8) * 2);
 
-    // ---- K/V tile staging: global -> registers -> LDS -----------------------
-    bf16x8 kreg[KCH];
-    bf16x8 vreg[KPT];
-    // V: this thread's KPT-key group and 8-column group.  Consecutive lanes take
-    // consecutive key groups, so one transposed LDS store of a wavefront covers
-    // contiguous bytes of V^T rows (all 64 banks, no conflicts).
-    constexpr int KG = BN / KPT;
-    const int vkg = tid % KG;
-    const int vdg = tid / KG;
-
-    auto load_tile = [&](int t) {
-        const int k0 = t * BN;
+    // ---- direct HBM -> LDS copies -----------------------------------------
+    // Copy i of wavefront w fills LDS chunk positions P = (w*NI + i)*64 + lane of
+    // a tile buffer; position P holds chunk (P % CH) ^ swizzle(row) of row P / CH.
+    // The per-lane source offsets are fixed; each tile gets its own buffer
+    // descriptor (base advanced by the tile, range = the valid rows left), so
+    // rows past n arrive as zeros and the per-tile work is scalar.
+    uint32_t koff[NI], voff[NI];
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c / DG, col = c % DG;
-            kreg[i] = load16(kbuf, (uint32_t)((k0 + row) * D + col * 8) * 2);
-        }
-#pragma unroll
-        for (int i = 0; i < KPT; ++i)   // rows past n read as zero: 0 * garbage would be NaN
-            vreg[i] = load16(vbuf, (uint32_t)((k0 + vkg * KPT + i) * D + vdg * 8) * 2);
+    for (int i = 0; i < NI; ++i) {
+        const int P = (w * NI + i) * 64 + l;
+        const int row = P / CH;
+        koff[i] = (uint32_t)(row * D + (((P % CH) ^ k_swizzle<D>(row)) * 8)) * 2;
+        voff[i] = (uint32_t)(row * D + (((P % CH) ^ v_swizzle<D>(row)) * 8)) * 2;
+    }
+    auto tile_rsrc = [&](const bf16* base, int t) {
+        const int rows = n - t * BN;        // valid rows from the tile start (> 0 for t < ntiles)
+        return make_rsrc(base + kvoff + (size_t)t * BN * D, (uint32_t)(rows > 0 ? rows : 0) * D * 2);
     };
-    auto store_tile = [&](int buf) {
-        bf16* Ks = smem + buf * BUF;
-        bf16* Vs = Ks + BN * KST;
+    auto copy_k = [&](int t, int buf) {
+        const rsrc_t r = tile_rsrc(p.k, t);
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c / DG, col = c % DG;
-            *reinterpret_cast<bf16x8*>(Ks + row * KST + col * 8) = kreg[i];
+        for (int i = 0; i < NI; ++i) load16_to_lds(r, koff[i], smem + buf * TILE + (w * NI + i) * 512);
+    };
+    auto copy_v = [&](int t, int buf) {
+        const rsrc_t r = tile_rsrc(p.v, t);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) load16_to_lds(r, voff[i], smem + (2 + buf) * TILE + (w * NI + i) * 512);
+    };
+
+    // ---- per-lane LDS read offsets (constant over the loop) -----------------
+    // K (A operand of S^T): row kb*32 + krow, chunk 2*ks + hi.
+    const int krow = swap_bits_2_3(l & 31);
+    const int kxor = k_swizzle<D>(krow);    // swizzle of rows kb*32 + krow does not depend on kb
+    // V (A operand of O^T via the transposing read): row
+    // kbase + 8*hi + 4*hh + (l & 15) / 4, column db*32 + 16*((l >> 4) & 1) + 4*(l & 3).
+    const int vrow = 8 * hi + ((l & 15) >> 2);
+    const int vxor = v_swizzle<D>(vrow);    // rows differ from vrow by multiples of 4
+    const int vcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+
+    auto score_tile = [&](int buf, f32x16 (&s)[KB]) {
+        const bf16* Ks = smem + buf * TILE;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s[kb] = zero_f32x16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    Ks + (kb * 32 + krow) * D + (((2 * ks + hi) ^ kxor) * 8));
+                s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+            }
         }
+    };
+    // Masks of tile t: valid length, and causal on tiles crossing the diagonal.
+    // Tiles past the last one are masked entirely by the same rule.
+    auto mask_tile = [&](int t, f32x16 (&s)[KB]) {
+        const int k0 = t * BN;
+        const bool need = (k0 + BN > n) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
+        if (need) {
+            const int qpos = qrow + off;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16xk col;
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < KPT; ++i) col[i] = vreg[i][e];
-            *reinterpret_cast<bf16xk*>(Vs + (vdg * 8 + e) * VST + vkg * KPT) = col;
+                for (int v = 0; v < 16; ++v) {
+                    const int key = k0 + kb * 32 + 16 * (v >> 3) + 8 * hi + (v & 7);
+                    const bool ok = key < n && (!CAUSAL || key <= qpos);
+                    if (!ok) s[kb][v] = kNegInf;
+                }
         }
+    };
+    auto row_max = [&](const f32x16 (&s)[KB]) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        return max_with_partner(mx);
     };
 
     // ---- online-softmax state ----------------------------------------------
     const float c = p.c;
     float m = kNegInf;                      // running max of raw scores q.k (this lane's row)
+    float mc = 0.0f;                        // m * c, or 0 while the row has no valid key
     float ell = 0.0f;                       // this lane's half of the running sum
     f32x16 acc[DB];                         // O^T accumulator: rows d, column = this lane's query
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
 
-    const int krow = swap_bits_2_3(l & 31);
+    // One step for tile t, entered with sc = masked S(t) and (m, mc, ell, acc)
+    // referenced to the max m(t) over tiles 0..t:
+    //   block 1: score product of tile t + 1 || p = 2^(s c - m c), row sum, P -> bf16;
+    //   block 2: O^T += V^T P^T of tile t     || max of tile t + 1 and alpha;
+    //   then A and l are rescaled to m(t + 1).
+    // PAR = t % 2 selects the LDS buffers at compile time.
+    auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto par) {
+        constexpr int PAR = decltype(par)::value;
+        if (t + 2 < ntiles) copy_k(t + 2, PAR);         // into the buffer K(t) used
+        if (t + 1 < ntiles) copy_v(t + 1, PAR ^ 1);     // into the buffer V(t - 1) used
 
-    // Prologue, unconditional: with range-checked loads an empty tile reads as
-    // zeros, and every Q load is then complete before the loop starts.
-    load_tile(0);
-    store_tile(0);
-    wait_all_vector_loads();   // Q is resident: no wait on it inside the loop
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
-        const int k0 = t * BN;
-        const bool wave_active = !CAUSAL || (k0 <= qw0 + 31 + off);
-        if (wave_active) {
-            const bf16* Ks = smem + buf * BUF;
-            const bf16* Vs = Ks + BN * KST;
-
-            // S^T = K Q^T
-            f32x16 s[KB];
+        // ---- block 1 ----
+        score_tile(PAR ^ 1, sn);                         // K(t+1) is resident
+        float psum = 0.0f;
+        bf16x8 pb[KB][2];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                s[kb] = zero_f32x16();
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        Ks + (kb * 32 + krow) * KST + ks * 16 + hi * 8);
-                    s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
+            for (int half = 0; half < 2; ++half) {
+                float e[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    e[j] = exp2_fast(__builtin_fmaf(sc[kb][8 * half + j], c, -mc));
+                    psum += e[j];
                 }
+                pb[kb][half] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
             }
-
-            // Masks: valid length, and causal on tiles crossing the diagonal.
-            const bool need_mask = (k0 + BN > n) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
-            if (need_mask) {
-                const int qpos = qrow + off;
+        ell += psum;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = k0 + kb * 32 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                        const bool ok = key < n && (!CAUSAL || key <= qpos);
-                        if (!ok) s[kb][v] = kNegInf;
-                    }
-            }
+        for (int i = 0; i < KB * KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // K read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // score MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, (7 * KB * 8 + KB * KS - 1) / (KB * KS), 0);
+        }
 
-            // Row max: in-lane, then across the two lanes holding this row.
-            float mx = kNegInf;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-            mx = fmaxf(mx, lane_xor32(mx));
+        mask_tile(t + 1, sn);
 
-            const float m_new = fmaxf(m, mx);
-            const float mc = (m_new == kNegInf) ? 0.0f : m_new * c;  // never form -inf - (-inf)
-            const float alpha = exp2_fast(m * c - mc);               // 0 while the row was empty
-
-            // p = 2^(s c - m c), row sum, and P^T as the B operand of the PV product.
-            float psum = 0.0f;
-            bf16x8 pb[KB][2];
+        // ---- block 2 ----
+        const bf16* Vs = smem + (2 + PAR) * TILE;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    float e[8];
+                    const int row0 = kb * 32 + half * 16 + vrow;
+                    const int col = db * 32 + vcol;
+                    const bf16* base = Vs + row0 * D + (((col >> 3) ^ vxor) * 8) + (col & 7);
+                    const bf16x4 lo = lds_read_transposed(base);
+                    const bf16x4 up = lds_read_transposed(base + 4 * D);
+                    bf16x8 a;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        e[j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], c, -mc));
-                        psum += e[j];
-                    }
-                    pb[kb][half] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+                    for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = up[e]; }
+                    acc[db] = mfma_32x32x16(a, pb[kb][half], acc[db]);
                 }
-            ell = alpha * ell + psum;
-            m = m_new;
-
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        const float mx = row_max(sn);
+        const float m_new = fmaxf(m, mx);
+        const float mc_new = (m_new == kNegInf) ? 0.0f : m_new * c;  // never form -inf - (-inf)
+        const float alpha = exp2_fast(m * c - mc_new);              // 0 while the row was empty
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
-            }
+        for (int i = 0; i < DB * KB * 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // transposing V reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // PV MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
 
-            // O^T += V^T P^T
+        // ---- rescale to m(t + 1) ----
+        ell *= alpha;
+        m = m_new;
+        mc = mc_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            Vs + (db * 32 + (l & 31)) * VST + kb * 32 + half * 16 + hi * 8);
-                        acc[db] = mfma_32x32x16(a, pb[kb][half], acc[db]);
-                    }
+                for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
         }
-        if (t + 1 < ntiles) store_tile(buf ^ 1);
+        wait_all_vector_loads();
         __syncthreads();
+    };
+
+    // ---- prologue: K(0), K(1), V(0) resident; S(0) masked; m = max of tile 0 ---
+    copy_k(0, 0);
+    if (ntiles > 1) copy_k(1, 1);
+    copy_v(0, 0);
+    wait_all_vector_loads();                // Q and the first tiles have landed
+    __syncthreads();
+    f32x16 s0[KB], s1[KB];
+    score_tile(0, s0);
+    mask_tile(0, s0);
+    m = row_max(s0);
+    mc = (m == kNegInf) ? 0.0f : m * c;
+    __syncthreads();                        // step 0 refills K buffer 0 with K(2)
+
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, s0, s1, Const<0>{});
+        if (t + 1 < ntiles) step(t + 1, s1, s0, Const<1>{});
     }
 
     // ---- epilogue: O = A / l, LSE = ln 2 * (m c + log2 l) -------------------
-    const float ell_t = ell + lane_xor32(ell);
+    const float ell_t = sum_with_partner(ell);
     const float inv = ell_t > 0.0f ? 1.0f / ell_t : 0.0f;
     if (qrow < p.Lq) {
         bf16* Op = p.o + qoff + (size_t)qrow * D;
@@ -291,11 +346,11 @@ hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_
     const long long total = (long long)p.B * p.Hq * p.n_qblocks;
     const dim3 grid((unsigned)total), block(256);
     if (D == 64) {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<64, 128, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<64, 128, false>), grid, block, 0, stream, p);
+        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p);
     } else {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<128, 64, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<128, 64, false>), grid, block, 0, stream, p);
+        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
