@@ -5,7 +5,7 @@
 the first call into the library loads it and raises if it has not been built.
 """
 _EXPORTS = ("fa_fwd", "fa_fwd_splits", "fa_workspace_bytes", "fa_status_string",
-            "load_library", "FaError")
+            "load_library", "FaError", "PreparedCall")
 
 
 def __getattr__(name):

@@ -109,6 +109,37 @@ def fa_fwd(q, k, v, o=None, lse=None, *, causal=False, scale=None, kv_lens=None,
     return o, lse
 
 
+class PreparedCall:
+    """fa_fwd with its arguments checked and marshalled once.
+
+    Calling the object enqueues the same forward again with no per-call
+    Python checks (one ctypes call), for timing loops and serving loops where
+    host overhead would otherwise exceed the kernel time.  The caller keeps
+    the tensors alive and unchanged in shape."""
+
+    def __init__(self, q, k, v, o=None, lse=None, *, causal=False, scale=None, kv_lens=None,
+                 stream=None, want_lse=True, num_splits=None):
+        o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, want_lse)
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        self.o, self.lse = o, lse
+        self._keep = (q, k, v, o, lse, kv_lens)
+        lib = load_library()
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
+                int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), s)
+        if num_splits is None:
+            self._fn, self._args = lib.fa_fwd, args
+        else:
+            self._fn, self._args = lib.fa_fwd_splits, args + (int(num_splits),)
+        self()                                   # validate now: raises on a bad argument
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+        return self.o, self.lse
+
+
 def fa_fwd_splits(q, k, v, num_splits, o=None, lse=None, *, causal=False, scale=None,
                   kv_lens=None, stream=None, want_lse=True):
     """Same as fa_fwd through the split-KV path with at most ``num_splits`` partitions."""

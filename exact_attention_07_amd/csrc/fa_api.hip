@@ -168,7 +168,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
         p.q = qb; p.k = kb; p.v = vb; p.o = ob; p.lse = lse; p.kv_lens = kv_lens;
         p.B = s.B; p.Hq = s.Hq; p.Hkv = s.Hkv; p.Lq = s.Lq; p.Lk = s.Lk;
         p.r = r;
-        p.n_qblocks = (s.Lq + 127) / 128;
+        p.n_qblocks = (s.Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
         const int units = s.B * s.Hkv;
         p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
         p.scale = scale;

@@ -87,6 +87,46 @@ __device__ __forceinline__ void load16_to_lds(rsrc_t r, uint32_t byte_offset, bf
         r, (__attribute__((address_space(3))) void*)lds_base, 16, byte_offset, 0, 0, 0);
 }
 
+// Buffer descriptor as four scalar dwords, for the inline-assembly copy below:
+// base address (wave-uniform), stride 0, range in bytes, raw-buffer format.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 d;
+    d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFF));
+    d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    d[3] = 0x00020000;
+    return d;
+}
+
+// The same direct HBM -> LDS copy as load16_to_lds, issued from inline assembly
+// so the compiler's wait-count tracking does not see it: the caller waits for
+// it explicitly (vmcnt) before any wavefront reads the destination.  Without
+// this the compiler waits for every outstanding copy before the first LDS read
+// that it cannot prove disjoint, which defeats copying tiles several steps ahead.
+// M0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void copy16_to_lds_async(i32x4 desc, uint32_t byte_offset,
+                                                    uint32_t lds_addr) {
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(byte_offset), "s"(desc), "s"(lds_addr)
+        : "memory");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left at their maxima (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vector_loads_until() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives element
 // (j % 4) of the 8-byte rows read by lanes 4k + j / 4 of its group, k = 0..3.
 // When four consecutive lanes point at four consecutive columns of one row of

@@ -6,6 +6,14 @@
 
 namespace fa {
 
+// Wavefronts per prefill workgroup; each owns 32 query rows, so a workgroup
+// covers 32 * kPrefillWaves rows and shares every K/V tile among them.
+#ifndef FA_PREFILL_WAVES
+#define FA_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaves = FA_PREFILL_WAVES;
+constexpr int kPrefillRows = 32 * kPrefillWaves;
+
 struct PrefillParams {
     const __bf16* q;
     const __bf16* k;
@@ -15,7 +23,7 @@ struct PrefillParams {
     const int* kv_lens;    // may be null
     int B, Hq, Hkv, Lq, Lk;
     int r;                 // query heads per KV head
-    int n_qblocks;         // ceil(Lq / 128)
+    int n_qblocks;         // ceil(Lq / kPrefillRows)
     int xcd_units;         // (B * Hkv) / 8 when divisible by 8, else 0
     float scale;           // softmax scale
     float c;               // scale * log2(e): scores enter exp2 as s * c

@@ -69,20 +69,31 @@ __device__ __forceinline__ int v_swizzle(int row) { return D == 128 ? 4 * (row &
 template <int N>
 struct Const { static constexpr int value = N; };
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
-    constexpr int BM = 128;                 // query rows per workgroup
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(PrefillParams p) {
+    constexpr int NT = 64 * NW;             // threads per workgroup
+    constexpr int BM = 32 * NW;             // query rows per workgroup
     constexpr int BN = 64;                  // keys per KV tile
     constexpr int KS = D / 16;              // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;              // 32-row blocks of O^T
     constexpr int KB = BN / 32;             // 32-key blocks per KV tile
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
     constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
-    constexpr int NI = BN * CH / 256;       // 16-byte direct copies per thread per tile
-    static_assert(NI >= 1 && (BN * CH) % 256 == 0, "a tile must split evenly over 256 threads");
+    constexpr int NI = BN * CH / NT;        // 16-byte direct copies per thread per tile
+    static_assert(NI >= 1 && (BN * CH) % NT == 0, "a tile must split evenly over the workgroup");
+    // LDS stages per operand: K(t) lives in K buffer t % NB, V(t) in V buffer t % NB.
+    // Step t copies K(t + NB) and V(t + NB - 1), so copies run NB - 2 steps
+    // ahead of the step that first needs them.
+#ifdef FA_PREFILL_STAGES
+    constexpr int NB = FA_PREFILL_STAGES;
+#else
+    constexpr int NB = D == 64 ? 4 : 3;
+#endif
+    // Copies issued after the pair a step waits for: NB - 2 steps of 2 * NI.
+    constexpr int kPendingAfter = (NB - 2) * 2 * NI;
 
-    // K buffers at [0, 2 TILE), V buffers at [2 TILE, 4 TILE).
-    __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];
+    // K buffers at [0, NB TILE), V buffers at [NB TILE, 2 NB TILE).
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * NB * TILE];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
@@ -151,20 +162,17 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
         koff[i] = (uint32_t)(row * D + (((P % CH) ^ k_swizzle<D>(row)) * 8)) * 2;
         voff[i] = (uint32_t)(row * D + (((P % CH) ^ v_swizzle<D>(row)) * 8)) * 2;
     }
-    auto tile_rsrc = [&](const bf16* base, int t) {
-        const int rows = n - t * BN;        // valid rows from the tile start (> 0 for t < ntiles)
-        return make_rsrc(base + kvoff + (size_t)t * BN * D, (uint32_t)(rows > 0 ? rows : 0) * D * 2);
-    };
-    auto copy_k = [&](int t, int buf) {
-        const rsrc_t r = tile_rsrc(p.k, t);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)smem);
+    auto copy_tile = [&](const bf16* base, int t, int buf, const uint32_t (&offs)[NI]) {
+        const int rows = n - t * BN;        // valid rows from the tile start; <= 0 past the end
+        const i32x4 d = make_desc(base + kvoff + (size_t)t * BN * D,
+                                  (uint32_t)(rows > 0 ? rows : 0) * D * 2);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) load16_to_lds(r, koff[i], smem + buf * TILE + (w * NI + i) * 512);
+        for (int i = 0; i < NI; ++i)
+            copy16_to_lds_async(d, offs[i], lds0 + (uint32_t)(buf * TILE + (w * NI + i) * 512) * 2);
     };
-    auto copy_v = [&](int t, int buf) {
-        const rsrc_t r = tile_rsrc(p.v, t);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) load16_to_lds(r, voff[i], smem + (2 + buf) * TILE + (w * NI + i) * 512);
-    };
+    auto copy_k = [&](int t, int buf) { copy_tile(p.k, t, buf, koff); };
+    auto copy_v = [&](int t, int buf) { copy_tile(p.v, t, NB + buf, voff); };
 
     // ---- per-lane LDS read offsets (constant over the loop) -----------------
     // K (A operand of S^T): row kb*32 + krow, chunk 2*ks + hi.
@@ -177,7 +185,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
     const int vcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
     auto score_tile = [&](int buf, f32x16 (&s)[KB]) {
-        const bf16* Ks = smem + buf * TILE;
+        const bf16* Ks = smem + buf * TILE;     // buf: K buffer index
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             s[kb] = zero_f32x16();
@@ -218,25 +226,37 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
     // ---- online-softmax state ----------------------------------------------
     const float c = p.c;
     float m = kNegInf;                      // running max of raw scores q.k (this lane's row)
-    float mc = 0.0f;                        // m * c, or 0 while the row has no valid key
     float ell = 0.0f;                       // this lane's half of the running sum
     f32x16 acc[DB];                         // O^T accumulator: rows d, column = this lane's query
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
 
-    // One step for tile t, entered with sc = masked S(t) and (m, mc, ell, acc)
-    // referenced to the max m(t) over tiles 0..t:
-    //   block 1: score product of tile t + 1 || p = 2^(s c - m c), row sum, P -> bf16;
-    //   block 2: O^T += V^T P^T of tile t     || max of tile t + 1 and alpha;
-    //   then A and l are rescaled to m(t + 1).
-    // PAR = t % 2 selects the LDS buffers at compile time.
-    auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto par) {
-        constexpr int PAR = decltype(par)::value;
-        if (t + 2 < ntiles) copy_k(t + 2, PAR);         // into the buffer K(t) used
-        if (t + 1 < ntiles) copy_v(t + 1, PAR ^ 1);     // into the buffer V(t - 1) used
+    // One step for tile t, entered with sc = masked S(t) and (m, ell, acc)
+    // referenced to the max over tiles 0..t-1.  One basic block holds:
+    //   the score product of tile t + 1 (matrix cores), and on the vector ALUs
+    //   the row max of tile t, alpha, p = 2^(s c - m c) with the row sum and
+    //   P -> bf16, and the rescale of A by alpha;
+    //   then O^T += V^T P^T of tile t, each accumulator block rescaled just
+    //   before its first product.
+    // The rescale is unconditional (no branch), so nothing splits the block and
+    // the vector work of tile t overlaps the matrix work.  Tile t + 1 is masked
+    // at the end of the step (a branch taken only on diagonal and tail tiles).
+    // PH = t % lcm(2, NB) makes every buffer index a compile-time constant.
+    // Copies are issued for every step, also past the last tile (they then
+    // read zeros), so the number of copies in flight, and with it the wait
+    // count at the end of a step, is a constant.
+    auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto phase) {
+        constexpr int PH = decltype(phase)::value;
+        copy_k(t + NB, PH % NB);                         // into the buffer of K(t), last read in step t - 1
+        copy_v(t + NB - 1, (PH + NB - 1) % NB);          // into the buffer of V(t - 1)
 
-        // ---- block 1 ----
-        score_tile(PAR ^ 1, sn);                         // K(t+1) is resident
+        score_tile((PH + 1) % NB, sn);                   // K(t+1) is resident
+
+        const float mx = row_max(sc);
+        const float m_new = fmaxf(m, mx);
+        const float mc = (m_new == kNegInf) ? 0.0f : m_new * c;    // never form -inf - (-inf)
+        const float alpha = exp2_fast(m * c - mc);                 // 0 while the row was empty
+        m = m_new;
         float psum = 0.0f;
         bf16x8 pb[KB][2];
 #pragma unroll
@@ -251,20 +271,13 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
                 }
                 pb[kb][half] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
             }
-        ell += psum;
-#pragma unroll
-        for (int i = 0; i < KB * KS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // K read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // score MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, (7 * KB * 8 + KB * KS - 1) / (KB * KS), 0);
-        }
+        ell = alpha * ell + psum;
 
-        mask_tile(t + 1, sn);
-
-        // ---- block 2 ----
-        const bf16* Vs = smem + (2 + PAR) * TILE;
+        const bf16* Vs = smem + (NB + PH % NB) * TILE;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -279,47 +292,61 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
                     for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = up[e]; }
                     acc[db] = mfma_32x32x16(a, pb[kb][half], acc[db]);
                 }
-        const float mx = row_max(sn);
-        const float m_new = fmaxf(m, mx);
-        const float mc_new = (m_new == kNegInf) ? 0.0f : m_new * c;  // never form -inf - (-inf)
-        const float alpha = exp2_fast(m * c - mc_new);              // 0 while the row was empty
+        }
+        // Interleave: LDS reads run three MFMAs ahead; every MFMA is followed by
+        // an even share of the vector work.
+        constexpr int kQk = KB * KS, kPv = DB * KB * 2;
+        constexpr int kValu = 7 * KB * 8 + 16 * DB + 2 * KB * 8 + 12;
+        constexpr int kPer = (kValu + kQk + kPv - 1) / (kQk + kPv);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-        for (int i = 0; i < DB * KB * 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // transposing V reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // PV MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        for (int i = 0; i < kQk; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // score MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next LDS read
+        }
+#pragma unroll
+        for (int i = 0; i < kPv; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // PV MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // next transposing V reads
         }
 
-        // ---- rescale to m(t + 1) ----
-        ell *= alpha;
-        m = m_new;
-        mc = mc_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
-        }
-        wait_all_vector_loads();
+        mask_tile(t + 1, sn);
+        wait_vector_loads_until<kPendingAfter>();        // K(t+2) and V(t+1) have landed
         __syncthreads();
     };
 
-    // ---- prologue: K(0), K(1), V(0) resident; S(0) masked; m = max of tile 0 ---
+    // ---- prologue: copies K(0..NB-1), V(0..NB-2); S(0) masked ------------------
     copy_k(0, 0);
-    if (ntiles > 1) copy_k(1, 1);
+    copy_k(1, 1);
     copy_v(0, 0);
-    wait_all_vector_loads();                // Q and the first tiles have landed
+#pragma unroll
+    for (int j = 2; j < NB; ++j) {
+        copy_k(j, j);
+        copy_v(j - 1, j - 1);
+    }
+    wait_vector_loads_until<kPendingAfter>();            // Q, K(0), K(1), V(0) have landed
     __syncthreads();
     f32x16 s0[KB], s1[KB];
     score_tile(0, s0);
     mask_tile(0, s0);
-    m = row_max(s0);
-    mc = (m == kNegInf) ? 0.0f : m * c;
-    __syncthreads();                        // step 0 refills K buffer 0 with K(2)
+    __syncthreads();                        // step 0 refills K buffer 0
 
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, s0, s1, Const<0>{});
-        if (t + 1 < ntiles) step(t + 1, s1, s0, Const<1>{});
+    constexpr int NU = NB % 2 == 0 ? NB : 2 * NB;       // lcm(2, NB)
+    auto run = [&](int t, auto phase) {
+        if constexpr (decltype(phase)::value % 2 == 0) step(t, s0, s1, phase);
+        else step(t, s1, s0, phase);
+    };
+    for (int t = 0; t < ntiles; t += NU) {
+        run(t, Const<0>{});
+        if (t + 1 < ntiles) run(t + 1, Const<1>{});
+        if (t + 2 < ntiles) run(t + 2, Const<2 % NU>{});
+        if (t + 3 < ntiles) run(t + 3, Const<3 % NU>{});
+        if constexpr (NU > 4) {
+            if (t + 4 < ntiles) run(t + 4, Const<4 % NU>{});
+            if (t + 5 < ntiles) run(t + 5, Const<5 % NU>{});
+        }
     }
 
     // ---- epilogue: O = A / l, LSE = ln 2 * (m c + log2 l) -------------------
@@ -344,13 +371,14 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillParams p) {
 
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream) {
     const long long total = (long long)p.B * p.Hq * p.n_qblocks;
-    const dim3 grid((unsigned)total), block(256);
+    constexpr int NW = kPrefillWaves;
+    const dim3 grid((unsigned)total), block(64 * NW);
     if (D == 64) {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p);
+        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true, NW>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<64, false, NW>), grid, block, 0, stream, p);
     } else {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p);
+        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, NW>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<128, false, NW>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
