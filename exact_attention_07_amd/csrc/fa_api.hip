@@ -96,12 +96,16 @@ SplitPlan plan_splits(const Shape& s, int requested, int cus) {
     if (requested > 0) {
         want = requested;
     } else {
-        // Partitions of about 256 keys bound the time of the longest wavefront;
-        // more partitions when the batch alone cannot fill the GPU (8 waves per CU).
+        // The split kernel runs two wavefronts per SIMD, 8 per CU.  About 1.5
+        // wavefronts per slot fills the GPU even when part of the partitions
+        // of ragged sequences are empty, while keeping each wavefront's stream
+        // long (its start-up latency is paid once) and the partials few.
+        // Partitions stay at least 256 keys long.
         const long long units = (long long)s.B * s.Hkv * pl.n_groups;
+        const long long slots = 8LL * cus;
+        const long long by_fill = (3 * slots + 2 * units - 1) / (2 * units);
         const long long by_len = (s.Lk + 255) / 256;
-        const long long by_fill = (8LL * cus + units - 1) / units;
-        want = (int)(by_len > by_fill ? by_len : by_fill);
+        want = (int)(by_fill < by_len ? by_fill : by_len);
     }
     if (want > tiles) want = tiles;
     if (want < 1) want = 1;

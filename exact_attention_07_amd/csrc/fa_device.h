@@ -74,6 +74,14 @@ __device__ __forceinline__ bf16x8 load16(rsrc_t r, uint32_t byte_offset) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
+// The same load marked non-temporal (the nt cache policy): for data read once
+// in full lines, so streamed bytes do not displace cached ones.  Only for
+// loads whose lines are consumed whole by the instruction itself: a partial
+// line is not kept for the next instruction and would be fetched again.
+__device__ __forceinline__ bf16x8 load16_stream(rsrc_t r, uint32_t byte_offset) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 2));
+}
+
 // s_waitcnt vmcnt(0): wait for every outstanding vector-memory load of this
 // wave (expcnt and lgkmcnt left at their maxima).  Issued through the builtin
 // so the compiler's own wait-count tracking knows the loads have completed.
@@ -137,6 +145,17 @@ __device__ __forceinline__ bf16x4 lds_read_transposed(const bf16* addr) {
         (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(addr)));
     return __builtin_bit_cast(bf16x4, v);
 }
+
+// 16-byte-chunk XOR swizzles of K and V tiles in LDS (row-major, D columns).
+// K is read one row per lane (16 consecutive lanes: 16 distinct rows, one
+// chunk column); V is read by ds_read_b64_tr_b16 (32 lanes: 4 rows x 4
+// chunks).  Either way the XOR spreads each batch of lanes over all 64 banks.
+// Both depend only on the low bits of the row, so any tile height that is a
+// multiple of 16 rows can use them.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swizzle(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;

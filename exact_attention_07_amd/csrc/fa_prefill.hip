@@ -56,16 +56,6 @@
 
 namespace fa {
 
-// 16-byte-chunk XOR swizzles of the K and V tiles in LDS (row-major, D
-// columns).  K is read one row per lane (16 consecutive lanes: 16 distinct
-// rows, one chunk column); V is read by ds_read_b64_tr_b16 (32 lanes: 4 rows x
-// 4 chunks).  Either way the chosen XOR spreads each batch of lanes over all
-// 64 banks.
-template <int D>
-__device__ __forceinline__ int k_swizzle(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int v_swizzle(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
-
 template <int N>
 struct Const { static constexpr int value = N; };
 

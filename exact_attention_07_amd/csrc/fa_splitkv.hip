@@ -11,62 +11,77 @@
 //
 // split kernel: one wavefront per (batch, KV head, 32-row group, partition).
 // Packed row rho = head_in_group * Lq + query enumerates the rows that read
-// this KV head; they are contiguous in Q, O and LSE memory.  Per 32-key tile:
-//   K rows go straight from global memory into MFMA A-operand registers (one
-//   16-byte load per lane per k-step, rows in the bit-2/3 swapped order);
-//   V rows are loaded with coalesced 16-byte loads and written transposed into
-//   a wave-private LDS tile, then read back as the A operand of O^T += V^T P^T;
-//   the next tile's loads are issued before the current tile's arithmetic.
-// The online-softmax update is the same as the prefill kernel's.
-// Partials are kept in base-2 units: part_lse = m*c + log2 l.
+// this KV head; they are contiguous in Q, O and LSE memory.  The kernel is
+// bound by HBM bandwidth, so it keeps many bytes in flight with few
+// instructions: per 32-key tile each lane issues 16-byte range-checked,
+// non-temporal loads of K and V straight into registers (fully coalesced: one
+// instruction reads 1 KB of consecutive rows; keys past the partition read as
+// zero), and the loads of tile t + 1 are issued as soon as the registers of
+// tile t are consumed, so they are in flight during all of tile t's work.
+// Both tiles then go to wavefront-private LDS tiles (16-byte writes,
+// XOR-swizzled) from which K is read in the MFMA A-operand layout (rows
+// through the bit-2/3 swap) and V through the transposing read.  Register use
+// is capped at 256 so that two wavefronts share each SIMD.  Per tile,
+// S^T = K Q^T and O^T += V^T P^T run on the matrix cores as in the prefill
+// kernel, with the same online-softmax update.
+// Partials are kept in base-2 units: part_lse = m*c + log2 l; a partition that
+// starts past the sequence's valid length writes part_lse = -inf and nothing
+// else, so the combine needs no lengths.
 //
-// combine kernel: one wavefront per output row merges the active partitions
-// (partitions that start before the sequence's valid length) and writes bf16 O
-// and the natural-log LSE; a row with no valid key gets O = 0, LSE = -inf.
+// combine kernel: one wavefront per output row.  Lanes load the partition
+// log-sum-exps together, reduce their max and the weight sum across the
+// wavefront, then every lane accumulates its columns over all partitions with
+// independent loads (a partition of weight 0 is selected away, so the stale
+// data of an empty partition is never used).  A row with no valid key gets
+// O = 0, LSE = -inf.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
 template <int D>
-__global__ void __launch_bounds__(64) splitkv_kernel(SplitParams p) {
+__global__ void __launch_bounds__(64, 2) splitkv_kernel(SplitParams p) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    constexpr int DG = D / 8;               // 16-byte groups per row
-    constexpr int VBLK = D / 64;            // (4 keys x 8 columns) blocks per lane
-    constexpr int VST = 32 + 8;             // LDS row stride of V^T in bf16
+    constexpr int CH = D / 8;               // 16-byte chunks per row
+    constexpr int BN = 32;                  // keys per tile
+    constexpr int NV = BN * CH / 64;        // 16-byte V loads per lane and tile
 
-    __shared__ __attribute__((aligned(16))) bf16 vt[D * VST];
+    __shared__ __attribute__((aligned(16))) bf16 kt[BN * D];   // K tile, row-major, swizzled
+    __shared__ __attribute__((aligned(16))) bf16 vt[BN * D];   // V tile, row-major, swizzled
 
     const int l = threadIdx.x;
     const int hi = l >> 5;
-    int L = blockIdx.x;
-    const int s = L % p.num_splits;
-    L /= p.num_splits;
-    const int rg = L % p.n_groups;
-    L /= p.n_groups;
+    // Partition-major order: consecutive workgroups (dealt round-robin to the
+    // eight XCDs) take the same partition of different (batch, KV head, row
+    // group) units, so every XCD gets a like mix of long and short sequences.
+    const int units = p.B * p.Hkv * p.n_groups;
+    const int s = blockIdx.x / units;
+    int L = blockIdx.x - s * units;
     const int g = L % p.Hkv;
-    const int b = L / p.Hkv;
+    L /= p.Hkv;
+    const int rg = L % p.n_groups;
+    const int b = L / p.n_groups;
 
     int n = p.Lk;
     if (p.kv_lens) {
         n = p.kv_lens[b];
         n = n < 0 ? 0 : (n > p.Lk ? p.Lk : n);
     }
-    const int kbeg = s * p.chunk;
-    if (kbeg >= n) return;                  // an empty partition: the combine skips it
-    const int kend = min(n, kbeg + p.chunk);
-    const int ntiles = (kend - kbeg + 31) / 32;
-
     const int rho = rg * 32 + (l & 31);     // packed row of this lane's column
     const bool row_ok = rho < p.rows;
-    const int qi = row_ok ? rho % p.Lq : 0;
     const size_t grow = (size_t)(b * p.Hq + g * p.r) * p.Lq + rho;  // row in [B*Hq*Lq]
+    const int kbeg = s * p.chunk;
+    if (kbeg >= n) {                        // an empty partition: weight 0 in the combine
+        if (row_ok && hi == 0) p.part_lse[grow * p.num_splits + s] = kNegInf;
+        return;
+    }
+    const int kend = min(n, kbeg + p.chunk);
+    const int ntiles = (kend - kbeg + BN - 1) / BN;
+
+    const int qi = row_ok ? rho % p.Lq : 0;
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
     const int qpos = n - p.Lq + qi;         // bottom-right causal position
-    // Range-checked buffers: keys >= kend (past this partition) read as zero.
-    const rsrc_t kbuf = make_rsrc(p.k + kvoff, (uint32_t)kend * D * 2);
-    const rsrc_t vbuf = make_rsrc(p.v + kvoff, (uint32_t)kend * D * 2);
     const size_t qbase = (size_t)(b * p.Hq + g * p.r) * p.Lq;      // first packed row of this KV head
     const rsrc_t qbuf = make_rsrc(p.q + qbase * D, (uint32_t)p.rows * D * 2);
 
@@ -75,23 +90,36 @@ __global__ void __launch_bounds__(64) splitkv_kernel(SplitParams p) {
     for (int ks = 0; ks < KS; ++ks)
         qf[ks] = load16(qbuf, (uint32_t)(rho * D + ks * 16 + hi * 8) * 2);
 
-    const int krow = swap_bits_2_3(l & 31);
-    bf16x8 kreg[KS];
-    bf16x8 vreg[VBLK][4];
+    // Tile t as 16-byte chunks: chunk i * 64 + lane of the row-major K and V
+    // tiles; past kend the range is 0.
+    bf16x8 kr[NV], vr[NV];
     auto load_tile = [&](int t) {
-        const int k0 = kbeg + t * 32;
+        const int k0 = kbeg + t * BN;
+        const int rows = kend - k0;
+        const uint32_t bytes = (uint32_t)(rows > 0 ? rows : 0) * D * 2;
+        const size_t src = kvoff + (size_t)(rows > 0 ? k0 : 0) * D;
+        const rsrc_t kb = make_rsrc(p.k + src, bytes);
+        const rsrc_t vb = make_rsrc(p.v + src, bytes);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kreg[ks] = load16(kbuf, (uint32_t)((k0 + krow) * D + ks * 16 + hi * 8) * 2);
+        for (int i = 0; i < NV; ++i) kr[i] = load16_stream(kb, (uint32_t)(i * 64 + l) * 16);
 #pragma unroll
-        for (int i = 0; i < VBLK; ++i) {
-            const int blk = l + 64 * i;
-            const int dg = blk % DG, kg = blk / DG;
+        for (int i = 0; i < NV; ++i) vr[i] = load16_stream(vb, (uint32_t)(i * 64 + l) * 16);
+    };
+    // Chunk i * 64 + lane of either tile goes to row P / CH, chunk P % CH xor the swizzle.
+    auto store_tile = [&](bf16* tile, const bf16x8 (&r)[NV], auto swz) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)   // rows past the partition read as zero
-                vreg[i][j] = load16(vbuf, (uint32_t)((k0 + kg * 4 + j) * D + dg * 8) * 2);
+        for (int i = 0; i < NV; ++i) {
+            const int P = i * 64 + l;
+            const int row = P / CH;
+            *reinterpret_cast<bf16x8*>(tile + row * D + (((P % CH) ^ swz(row)) * 8)) = r[i];
         }
     };
+
+    const int krow = swap_bits_2_3(l & 31);
+    const int kxor = k_swizzle<D>(krow);
+    const int vrow = 8 * hi + ((l & 15) >> 2);
+    const int vxor = v_swizzle<D>(vrow);
+    const int vcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
     const float c = p.c;
     float m = kNegInf, ell = 0.0f;
@@ -101,32 +129,22 @@ __global__ void __launch_bounds__(64) splitkv_kernel(SplitParams p) {
 
     load_tile(0);
     for (int t = 0; t < ntiles; ++t) {
-        const int k0 = kbeg + t * 32;
-        // Stage V^T of this tile in LDS (after every lane finished reading the previous one).
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < VBLK; ++i) {
-            const int blk = l + 64 * i;
-            const int dg = blk % DG, kg = blk / DG;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 col;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) col[j] = vreg[i][j][e];
-                *reinterpret_cast<bf16x4*>(vt + (dg * 8 + e) * VST + kg * 4) = col;
-            }
-        }
-        __syncthreads();
-        bf16x8 kcur[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kcur[ks] = kreg[ks];
-        if (t + 1 < ntiles) load_tile(t + 1);
+        const int k0 = kbeg + t * BN;
+        // K(t) and V(t) into the LDS tiles (the previous tile's reads are
+        // ordered before these writes: one wavefront's LDS operations execute
+        // in order), then the registers take tile t + 1.
+        store_tile(kt, kr, [](int row) { return k_swizzle<D>(row); });
+        store_tile(vt, vr, [](int row) { return v_swizzle<D>(row); });
+        load_tile(t + 1);                   // zeros and no traffic past the last tile
 
         f32x16 sacc = zero_f32x16();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc = mfma_32x32x16(kcur[ks], qf[ks], sacc);
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + krow * D + (((2 * ks + hi) ^ kxor) * 8));
+            sacc = mfma_32x32x16(a, qf[ks], sacc);
+        }
 
-        const bool need_mask = (k0 + 32 > kend) || p.causal;
+        const bool need_mask = (k0 + BN > kend) || (p.causal && k0 + BN - 1 > n - p.Lq);
         if (need_mask) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -138,7 +156,7 @@ __global__ void __launch_bounds__(64) splitkv_kernel(SplitParams p) {
         float mx = kNegInf;
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-        mx = fmaxf(mx, lane_xor32(mx));
+        mx = max_with_partner(mx);
         const float m_new = fmaxf(m, mx);
         const float mc = (m_new == kNegInf) ? 0.0f : m_new * c;
         const float alpha = exp2_fast(m * c - mc);
@@ -166,13 +184,18 @@ __global__ void __launch_bounds__(64) splitkv_kernel(SplitParams p) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    vt + (db * 32 + (l & 31)) * VST + half * 16 + hi * 8);
+                const int col = db * 32 + vcol;
+                const bf16* base = vt + (half * 16 + vrow) * D + (((col >> 3) ^ vxor) * 8) + (col & 7);
+                const bf16x4 lo = lds_read_transposed(base);
+                const bf16x4 up = lds_read_transposed(base + 4 * D);
+                bf16x8 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = up[e]; }
                 acc[db] = mfma_32x32x16(a, pb[half], acc[db]);
             }
     }
 
-    const float ell_t = ell + lane_xor32(ell);
+    const float ell_t = sum_with_partner(ell);
     const float inv = ell_t > 0.0f ? 1.0f / ell_t : 0.0f;
     if (row_ok) {
         float* Op = p.part_o + (grow * p.num_splits + s) * D;
@@ -190,6 +213,17 @@ __global__ void __launch_bounds__(64) splitkv_kernel(SplitParams p) {
     }
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(CombineParams p) {
     constexpr int PER_LANE = D / 64;
@@ -198,30 +232,43 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p) {
     const long long rows = (long long)p.B * p.Hq * p.Lq;
     const long long row = (long long)blockIdx.x * 4 + w;
     if (row >= rows) return;
-    const int b = (int)(row / ((long long)p.Hq * p.Lq));
-    int n = p.Lk;
-    if (p.kv_lens) {
-        n = p.kv_lens[b];
-        n = n < 0 ? 0 : (n > p.Lk ? p.Lk : n);
-    }
-    int active = (n + p.chunk - 1) / p.chunk;
-    active = active < p.num_splits ? active : p.num_splits;
-    const float* ls = p.part_lse + row * p.num_splits;
+    const int S = p.num_splits;
+    const float* ls = p.part_lse + row * S;
+    const float* po = p.part_o + row * S * D + l * PER_LANE;
+
     float M = kNegInf;
-    for (int s = 0; s < active; ++s) M = fmaxf(M, ls[s]);
+    for (int s0 = 0; s0 < S; s0 += 64)
+        if (s0 + l < S) M = fmaxf(M, ls[s0 + l]);
+    M = wave_max(M);
+
     float out[PER_LANE];
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) out[j] = 0.0f;
     float lse = kNegInf;
     if (M != kNegInf) {
         float W = 0.0f;
-        const float* po = p.part_o + row * p.num_splits * D;
-        for (int s = 0; s < active; ++s) {
-            const float wgt = exp2_fast(ls[s] - M);  // an empty partition (-inf) weighs 0
-            W += wgt;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            // Lane i holds the weight of partition s0 + i (0 for an empty one).
+            const float wl = (s0 + l < S) ? exp2_fast(ls[s0 + l] - M) : 0.0f;
+            W += wl;
+            const int cnt = S - s0 < 64 ? S - s0 : 64;
+            for (int i0 = 0; i0 < cnt; i0 += 4) {
+                // Four partitions per pass with independent loads; indices past
+                // cnt are clamped to a valid partition and weighted 0.
 #pragma unroll
-            for (int j = 0; j < PER_LANE; ++j) out[j] += wgt * po[(size_t)s * D + l * PER_LANE + j];
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + u < cnt ? i0 + u : cnt - 1;
+                    const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i));
+                    const float wgt = i0 + u < cnt ? wi : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < PER_LANE; ++j) {
+                        const float x = po[(size_t)(s0 + i) * D + j];
+                        out[j] += wgt != 0.0f ? wgt * x : 0.0f;
+                    }
+                }
+            }
         }
+        W = wave_sum(W);
         const float inv = 1.0f / W;
 #pragma unroll
         for (int j = 0; j < PER_LANE; ++j) out[j] *= inv;
