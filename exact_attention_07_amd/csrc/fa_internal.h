@@ -6,13 +6,9 @@
 
 namespace fa {
 
-// Wavefronts per prefill workgroup; each owns 32 query rows, so a workgroup
-// covers 32 * kPrefillWaves rows and shares every K/V tile among them.
-#ifndef FA_PREFILL_WAVES
-#define FA_PREFILL_WAVES 8
-#endif
-constexpr int kPrefillWaves = FA_PREFILL_WAVES;
-constexpr int kPrefillRows = 32 * kPrefillWaves;
+// Query rows per prefill workgroup: four wavefronts of 64 rows, each
+// workgroup sharing every K/V tile among them.
+constexpr int kPrefillRows = 256;
 
 struct PrefillParams {
     const __bf16* q;

@@ -1,52 +1,60 @@
-// Prefill forward: one workgroup per (batch, query head, 128-row query block).
+// Prefill forward: one workgroup per (batch, query head, 256-row query block).
 //
 // Schedule (FlashAttention Cheat Sheet, section 4 "The complete FlashAttention
 // flow"; FlashAttention from Scratch, section 6.3): the Q tile is loaded once
-// and stays in registers; K and V tiles stream through LDS, double-buffered
-// (section 10, "fill one buffer while consuming another"); each KV tile goes
-// through S = Q K^T, masking, the online-softmax update and A += P V; O = A / l
-// and the LSE are written once at the end.  Each of the four wavefronts owns 32
-// complete query rows (FA2's split-Q ownership, section 7.3), so no partial
-// outputs are exchanged between wavefronts.
+// and stays in registers; K and V tiles stream through LDS in three stages
+// (section 10, "fill one buffer while consuming another"), copied HBM -> LDS
+// directly (buffer loads with the LDS destination, range-checked so rows past
+// the valid length arrive as zeros); each KV tile goes through S = Q K^T,
+// masking, the online-softmax update and A += P V; O = A / l and the LSE are
+// written once at the end.  Each of the eight wavefronts owns 32 complete
+// query rows (FA2's split-Q ownership, section 7.3), so no partial outputs are
+// exchanged between wavefronts.
 //
-// Pipelining (section 10.2's dependency sketch, applied on one wavefront):
-// the score product of tile t+1 is issued in the same basic block as the
-// softmax of tile t, so the matrix cores work while the vector ALUs compute
-// exponentials; K therefore runs one tile ahead of V.  K and V each have two
-// LDS buffers and are copied HBM -> LDS directly (buffer loads with the LDS
-// destination, range-checked so rows past the valid length arrive as zeros);
-// the copies for tiles t+2 (K) and t+1 (V) are issued at the top of step t
-// and waited for at its end.
+// Ping-pong (FlashAttention-3 summary, "ping-pong scheduling" of two warp
+// groups): the wavefronts form two groups of four, one wavefront of each group
+// per SIMD, and every wavefront alternates a matrix phase M(t) -- the score
+// product of tile t+1 and O^T += V^T P^T of tile t -- with a vector phase
+// V(t) -- mask, row max and p = 2^(s c - r) for tile t+1.  The second group
+// runs one phase behind the first, and a workgroup barrier ends every phase,
+// so while one wavefront of a SIMD keeps the matrix cores busy the other one
+// computes exponentials on the vector ALUs.  The matrix phase runs at raised
+// wave priority so its products issue first.
 //
-// gfx950 mapping.  The score tile is computed transposed, S^T = K Q^T, on
+// LDS stages.  K(j) lives in K buffer j % 3, V(j) in V buffer j % 3.  With the
+// first group's M(t) in phase 2t and the second's in 2t+1, K(j) is read in
+// phases 2j-2, 2j-1 and V(j) in 2j, 2j+1.  M(t) copies K(t+3) (into the
+// buffer of K(t), free since phase 2t) and V(t+2) (into that of V(t-1), free
+// since phase 2t); every wavefront waits for the copies of M(t-1) at the end
+// of M(t), so all of K(t+2) and V(t+1) are resident after phase 2t+1, before
+// their first reader in phase 2t+2.
+//
+// gfx950 mapping.  Scores are computed transposed, S^T = K Q^T, on
 // v_mfma_f32_32x32x16_bf16: the accumulator puts one query per lane (column
 // l % 32) with 16 keys per 32-key block, so a row's max and sum are in-lane
-// reductions plus one exchange between lanes l and l ^ 32, and the softmax
-// state (m, l) is one scalar per lane.  K rows are fed to the MFMA through the
-// bit-2/3 swap of fa_device.h, which makes the S^T accumulator, converted to
-// bf16, exactly the B operand (P^T, keys as the reduction index) of the second
-// product O^T += V^T P^T: the probabilities never leave registers.  V stays
-// row-major in LDS; its A-operand fragments (four keys of one column per read)
-// come from ds_read_b64_tr_b16, the gfx950 transposing LDS read.  Both tiles
-// are XOR-swizzled in 16-byte units so every LDS read is bank-conflict-free.
+// reductions plus one exchange between lanes l and l ^ 32.  K rows are fed
+// through the bit-2/3 swap of fa_device.h, which makes the S^T accumulator,
+// converted to bf16, exactly the B operand (P^T) of the second product
+// O^T += V^T P^T: the probabilities never leave registers.  V stays row-major
+// in LDS; its A-operand fragments come from ds_read_b64_tr_b16, the gfx950
+// transposing LDS read.  Both tiles are XOR-swizzled in 16-byte units so every
+// LDS read is bank-conflict-free.
 //
-// Softmax in base 2 with the scale folded into the exponent: p = 2^(s*c - m*c),
-// c = scale * log2(e) (FlashAttention from Scratch, section 6.3, base-2
-// exponentials); the LSE is converted back to natural log once
-// (LSE = (m*c + log2 l) * ln 2).  alpha = 2^((m_old - m_new) * c) rescales the
-// running sum and the accumulator; the accumulator multiply is skipped when no
-// row of the wavefront changed its max.  The running max is always the true
-// max, so the largest probability of every tile is exactly 1.0 and passes
-// through the bf16 P operand unrounded.  (FA4's conditional rescaling keeps a
-// stale reference, which puts the dominant probability in (1, 256] where bf16
-// rounds it; measured on peaky rows it doubles the worst output error, so it
-// is not used.)
+// Softmax in base 2 with the scale folded into the exponent: p = 2^(s c - r),
+// c = scale * log2(e), r = the row's reference (FlashAttention from Scratch,
+// section 6.3, base-2 exponentials).  The reference is the running max, but
+// it is only moved, and A and l rescaled by alpha = 2^(r_old - r_new), when a
+// tile raises the row max by more than kTau in base-2 units (the conditional
+// rescaling of the FlashAttention-4 summary); between moves p <= 2^kTau, far
+// from fp32 overflow.  Because p is rounded to bf16 for the PV product, O is
+// normalised by the sum of the rounded probabilities (one v_dot2 per pair),
+// so numerator and denominator carry the same weights and a dominant key
+// passes through exactly; the LSE uses the fp32 sum of the unrounded ones.
 //
 // Causal work (section 7.3; FlashAttention-4 summary, "LPT scheduling for
 // imbalanced grids"): KV tiles past the block's last visible key are never
 // visited, elementwise masks are applied only on tiles that cross the
-// diagonal or the valid length, a wavefront whose rows all precede a tile
-// skips that tile's arithmetic, and query blocks are launched last-first so
+// diagonal or the valid length, and query blocks are launched last-first so
 // the longest workgroups start earliest.  Workgroups of the query heads that
 // share a KV head are adjacent, and when B * Hkv is a multiple of 8 each of
 // the eight XCDs (round-robin workgroup dispatch) receives whole KV heads, so
@@ -59,8 +67,13 @@ namespace fa {
 template <int N>
 struct Const { static constexpr int value = N; };
 
-template <int D, bool CAUSAL, int NW>
-__global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(PrefillParams p) {
+// Rows of the reference may lag the true max by up to kTau (base 2).
+constexpr float kTau = 8.0f;
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_kernel(PrefillParams p) {
+    constexpr int NW = 8;                   // wavefronts: two groups of four
     constexpr int NT = 64 * NW;             // threads per workgroup
     constexpr int BM = 32 * NW;             // query rows per workgroup
     constexpr int BN = 64;                  // keys per KV tile
@@ -70,23 +83,16 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
     constexpr int CH = D / 8;               // 16-byte chunks per K/V row
     constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
     constexpr int NI = BN * CH / NT;        // 16-byte direct copies per thread per tile
+    constexpr int NB = 3;                   // LDS stages per operand (the tile loop is unrolled by NB)
+    static_assert(BM == kPrefillRows, "host and kernel disagree on the query block");
     static_assert(NI >= 1 && (BN * CH) % NT == 0, "a tile must split evenly over the workgroup");
-    // LDS stages per operand: K(t) lives in K buffer t % NB, V(t) in V buffer t % NB.
-    // Step t copies K(t + NB) and V(t + NB - 1), so copies run NB - 2 steps
-    // ahead of the step that first needs them.
-#ifdef FA_PREFILL_STAGES
-    constexpr int NB = FA_PREFILL_STAGES;
-#else
-    constexpr int NB = D == 64 ? 4 : 3;
-#endif
-    // Copies issued after the pair a step waits for: NB - 2 steps of 2 * NI.
-    constexpr int kPendingAfter = (NB - 2) * 2 * NI;
 
     // K buffers at [0, NB TILE), V buffers at [NB TILE, 2 NB TILE).
     __shared__ __attribute__((aligned(16))) bf16 smem[2 * NB * TILE];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
+    const int grp = w >> 2;                 // ping-pong group; waves w and w + 4 share a SIMD
     const int l = tid & 63;
     const int hi = l >> 5;                  // which half of the wave (0 or 1)
 
@@ -107,7 +113,7 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
         unit = rem / p.r;
         hg = rem % p.r;
     }
-    const int qb = p.n_qblocks - 1 - qb_rev;
+    const int qblk = p.n_qblocks - 1 - qb_rev;
     const int b = unit / p.Hkv;
     const int g = unit - b * p.Hkv;
     const int h = g * p.r + hg;
@@ -118,7 +124,7 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
         n = n < 0 ? 0 : (n > p.Lk ? p.Lk : n);
     }
     const int off = n - p.Lq;               // query i sits at key position i + off
-    const int q0 = qb * BM;
+    const int q0 = qblk * BM;
     const int qw0 = q0 + w * 32;            // first row of this wavefront
     const int qrow = qw0 + (l & 31);        // the row this lane's column holds
     int kv_end = n;
@@ -153,16 +159,16 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
         voff[i] = (uint32_t)(row * D + (((P % CH) ^ v_swizzle<D>(row)) * 8)) * 2;
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)smem);
-    auto copy_tile = [&](const bf16* base, int t, int buf, const uint32_t (&offs)[NI]) {
+    auto copy_tile = [&](const bf16* base, int t, int buf, const uint32_t (&offs)[NI]) __attribute__((always_inline)) {
         const int rows = n - t * BN;        // valid rows from the tile start; <= 0 past the end
-        const i32x4 d = make_desc(base + kvoff + (size_t)t * BN * D,
+        const i32x4 d = make_desc(base + kvoff + (size_t)(rows > 0 ? t : 0) * BN * D,
                                   (uint32_t)(rows > 0 ? rows : 0) * D * 2);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
             copy16_to_lds_async(d, offs[i], lds0 + (uint32_t)(buf * TILE + (w * NI + i) * 512) * 2);
     };
-    auto copy_k = [&](int t, int buf) { copy_tile(p.k, t, buf, koff); };
-    auto copy_v = [&](int t, int buf) { copy_tile(p.v, t, NB + buf, voff); };
+    auto copy_k = [&](int t) { copy_tile(p.k, t, t % NB, koff); };
+    auto copy_v = [&](int t) { copy_tile(p.v, t, NB + t % NB, voff); };
 
     // ---- per-lane LDS read offsets (constant over the loop) -----------------
     // K (A operand of S^T): row kb*32 + krow, chunk 2*ks + hi.
@@ -174,8 +180,9 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
     const int vxor = v_swizzle<D>(vrow);    // rows differ from vrow by multiples of 4
     const int vcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-    auto score_tile = [&](int buf, f32x16 (&s)[KB]) {
-        const bf16* Ks = smem + buf * TILE;     // buf: K buffer index
+    f32x16 s[KB];                           // S^T of the tile being prepared
+    auto score_tile = [&](int t) __attribute__((always_inline)) {
+        const bf16* Ks = smem + (t % NB) * TILE;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             s[kb] = zero_f32x16();
@@ -187,9 +194,20 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
             }
         }
     };
-    // Masks of tile t: valid length, and causal on tiles crossing the diagonal.
-    // Tiles past the last one are masked entirely by the same rule.
-    auto mask_tile = [&](int t, f32x16 (&s)[KB]) {
+
+    // ---- online-softmax state ----------------------------------------------
+    const float c = p.c;
+    float ref = kNegInf;                    // reference r = (running max) * c; -inf while the row is empty
+    float ell_e = 0.0f, ell_r = 0.0f;       // this lane's halves of sum p and of sum bf16(p)
+    f32x16 acc[DB];                         // O^T accumulator: rows d, column = this lane's query
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
+    bf16x8 pb[KB][2];                       // P^T of the tile whose PV product is next
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+    // Vector phase for tile t (scores in s): mask where needed, move the
+    // reference if the row max rose by more than kTau, then P -> pb and sums.
+    auto softmax_tile = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BN;
         const bool need = (k0 + BN > n) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
         if (need) {
@@ -203,52 +221,29 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
                     if (!ok) s[kb][v] = kNegInf;
                 }
         }
-    };
-    auto row_max = [&](const f32x16 (&s)[KB]) {
-        float mx = kNegInf;
+        // Row max as a tree (short dependency chains).
+        float m8[8];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(s[0][j], s[0][j + 8]), fmaxf(s[1][j], s[1][j + 8]));
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-        return max_with_partner(mx);
-    };
-
-    // ---- online-softmax state ----------------------------------------------
-    const float c = p.c;
-    float m = kNegInf;                      // running max of raw scores q.k (this lane's row)
-    float ell = 0.0f;                       // this lane's half of the running sum
-    f32x16 acc[DB];                         // O^T accumulator: rows d, column = this lane's query
+        for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
+        float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+        mx = max_with_partner(mx);
+        const bool move = mx * c > ref + kTau;      // mx finite when true
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {  // rare after the first tile
+            const float r_new = move ? mx * c : ref;
+            const float alpha = move ? exp2_fast(ref - r_new) : 1.0f;   // 0 from an empty row
+            ref = r_new;
+            ell_e *= alpha;
+            ell_r *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
-
-    // One step for tile t, entered with sc = masked S(t) and (m, ell, acc)
-    // referenced to the max over tiles 0..t-1.  One basic block holds:
-    //   the score product of tile t + 1 (matrix cores), and on the vector ALUs
-    //   the row max of tile t, alpha, p = 2^(s c - m c) with the row sum and
-    //   P -> bf16, and the rescale of A by alpha;
-    //   then O^T += V^T P^T of tile t, each accumulator block rescaled just
-    //   before its first product.
-    // The rescale is unconditional (no branch), so nothing splits the block and
-    // the vector work of tile t overlaps the matrix work.  Tile t + 1 is masked
-    // at the end of the step (a branch taken only on diagonal and tail tiles).
-    // PH = t % lcm(2, NB) makes every buffer index a compile-time constant.
-    // Copies are issued for every step, also past the last tile (they then
-    // read zeros), so the number of copies in flight, and with it the wait
-    // count at the end of a step, is a constant.
-    auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto phase) {
-        constexpr int PH = decltype(phase)::value;
-        copy_k(t + NB, PH % NB);                         // into the buffer of K(t), last read in step t - 1
-        copy_v(t + NB - 1, (PH + NB - 1) % NB);          // into the buffer of V(t - 1)
-
-        score_tile((PH + 1) % NB, sn);                   // K(t+1) is resident
-
-        const float mx = row_max(sc);
-        const float m_new = fmaxf(m, mx);
-        const float mc = (m_new == kNegInf) ? 0.0f : m_new * c;    // never form -inf - (-inf)
-        const float alpha = exp2_fast(m * c - mc);                 // 0 while the row was empty
-        m = m_new;
-        float psum = 0.0f;
-        bf16x8 pb[KB][2];
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+        }
+        const float r = ref == kNegInf ? 0.0f : ref;   // never form -inf - (-inf)
+        // Four partial sums of p and two of bf16(p) keep the chains short.
+        float se[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sr[2] = {ell_r, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -256,119 +251,141 @@ __global__ void __launch_bounds__(64 * NW, 512 / (64 * NW)) prefill_kernel(Prefi
                 float e[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    e[j] = exp2_fast(__builtin_fmaf(sc[kb][8 * half + j], c, -mc));
-                    psum += e[j];
+                    e[j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], c, -r));
+                    se[j & 3] += e[j];
                 }
-                pb[kb][half] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+                const bf16x8 pv = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+                pb[kb][half] = pv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sr[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[2 * j], pv[2 * j + 1]}, ones, sr[j & 1], false);
             }
-        ell = alpha * ell + psum;
+        ell_e += (se[0] + se[1]) + (se[2] + se[3]);
+        ell_r = sr[0] + sr[1];
+    };
 
-        const bf16* Vs = smem + (NB + PH % NB) * TILE;
+    // Matrix phase M(t) as one software pipeline over its products: the KB*KS
+    // score products of tile t+1, then the DB*KB*2 PV products of tile t.
+    // Product i is issued right after the LDS read(s) of product i + AHEAD, so
+    // every operand is read AHEAD products (~32 cycles each) before its use
+    // and only ~AHEAD fragments are live.  A scheduling fence after each step
+    // keeps this order.
+    auto matrix_phase = [&](auto phase) __attribute__((always_inline)) {
+        constexpr int PH = decltype(phase)::value;      // t % NB
+        const bf16* Ks = smem + ((PH + 1) % NB) * TILE;
+        const bf16* Vs = smem + (NB + PH) * TILE;
+        constexpr int NQ = KB * KS;         // score products
+        constexpr int NF = DB * KB * 2;     // PV products (one V fragment each)
+        constexpr int NOPS = NQ + NF;
+        constexpr int AHEAD = 6;
+        bf16x8 frag[NOPS];
+        auto read_op = [&](int i) __attribute__((always_inline)) {
+            if (i < NQ) {
+                const int kb = i / KS, ks = i % KS;
+                frag[i] = *reinterpret_cast<const bf16x8*>(
+                    Ks + (kb * 32 + krow) * D + (((2 * ks + hi) ^ kxor) * 8));
+            } else {
+                const int f = i - NQ;
+                const int db = f / (KB * 2), kb = (f / 2) % KB, half = f % 2;
+                const int row0 = kb * 32 + half * 16 + vrow;
+                const int col = db * 32 + vcol;
+                const bf16* base = Vs + row0 * D + (((col >> 3) ^ vxor) * 8) + (col & 7);
+                const bf16x4 lo = lds_read_transposed(base);
+                const bf16x4 up = lds_read_transposed(base + 4 * D);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+                for (int e = 0; e < 4; ++e) { frag[i][e] = lo[e]; frag[i][4 + e] = up[e]; }
+            }
+        };
+        auto mfma_op = [&](int i) __attribute__((always_inline)) {
+            if (i < NQ) {
+                const int kb = i / KS, ks = i % KS;
+                s[kb] = mfma_32x32x16(frag[i], qf[ks], ks == 0 ? zero_f32x16() : s[kb]);
+            } else {
+                const int f = i - NQ;
+                const int db = f / (KB * 2), kb = (f / 2) % KB, half = f % 2;
+                acc[db] = mfma_32x32x16(frag[i], pb[kb][half], acc[db]);
+            }
+        };
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+        for (int i = 0; i < AHEAD; ++i) read_op(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int row0 = kb * 32 + half * 16 + vrow;
-                    const int col = db * 32 + vcol;
-                    const bf16* base = Vs + row0 * D + (((col >> 3) ^ vxor) * 8) + (col & 7);
-                    const bf16x4 lo = lds_read_transposed(base);
-                    const bf16x4 up = lds_read_transposed(base + 4 * D);
-                    bf16x8 a;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = up[e]; }
-                    acc[db] = mfma_32x32x16(a, pb[kb][half], acc[db]);
-                }
+        for (int i = 0; i < NOPS; ++i) {
+            mfma_op(i);
+            if (i + AHEAD < NOPS) read_op(i + AHEAD);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // Interleave: LDS reads run three MFMAs ahead; every MFMA is followed by
-        // an even share of the vector work.
-        constexpr int kQk = KB * KS, kPv = DB * KB * 2;
-        constexpr int kValu = 7 * KB * 8 + 16 * DB + 2 * KB * 8 + 12;
-        constexpr int kPer = (kValu + kQk + kPv - 1) / (kQk + kPv);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-        for (int i = 0; i < kQk; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // score MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);   // VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next LDS read
-        }
-#pragma unroll
-        for (int i = 0; i < kPv; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // PV MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // next transposing V reads
-        }
+    };
 
-        mask_tile(t + 1, sn);
-        wait_vector_loads_until<kPendingAfter>();        // K(t+2) and V(t+1) have landed
+    // ---- prologue: K(0..2), V(0..1) resident; S(0) -> P(0) -------------------
+    copy_k(0);
+    copy_k(1);
+    copy_v(0);
+    copy_k(2);
+    copy_v(1);
+    wait_all_vector_loads();                // Q and every prologue copy
+    __syncthreads();
+    score_tile(0);
+    softmax_tile(0);
+    __syncthreads();                        // K(0) read by every wavefront before M(0) refills its buffer
+    if (grp == 1) __syncthreads();          // the second group runs one phase behind
+
+    // One tile: matrix phase M(t), barrier, vector phase V(t), barrier.
+    // PH = t % NB is a compile-time constant, so every LDS offset is one.
+    auto tile_step = [&](int t, auto phase) __attribute__((always_inline)) {
+        // ---- matrix phase M(t) ----
+        __builtin_amdgcn_s_setprio(1);
+        copy_k(t + NB);                     // into the buffer of K(t)
+        copy_v(t + NB - 1);                 // into the buffer of V(t - 1)
+        // The score product runs for the last tile too (on the zero-filled
+        // buffer past the end; the result is not used), which keeps the
+        // phase one basic block.
+        matrix_phase(phase);
+        __builtin_amdgcn_s_setprio(0);
+        wait_vector_loads_until<2 * NI>();  // the copies of M(t-1) have landed
+        __syncthreads();
+        // ---- vector phase V(t) ----
+        if (t + 1 < ntiles) softmax_tile(t + 1);
         __syncthreads();
     };
-
-    // ---- prologue: copies K(0..NB-1), V(0..NB-2); S(0) masked ------------------
-    copy_k(0, 0);
-    copy_k(1, 1);
-    copy_v(0, 0);
-#pragma unroll
-    for (int j = 2; j < NB; ++j) {
-        copy_k(j, j);
-        copy_v(j - 1, j - 1);
+    for (int t = 0; t < ntiles; t += NB) {
+        tile_step(t, Const<0>{});
+        if (t + 1 < ntiles) tile_step(t + 1, Const<1>{});
+        if (t + 2 < ntiles) tile_step(t + 2, Const<2>{});
     }
-    wait_vector_loads_until<kPendingAfter>();            // Q, K(0), K(1), V(0) have landed
-    __syncthreads();
-    f32x16 s0[KB], s1[KB];
-    score_tile(0, s0);
-    mask_tile(0, s0);
-    __syncthreads();                        // step 0 refills K buffer 0
+    if (grp == 0) __syncthreads();          // match the second group's extra barrier
+    wait_all_vector_loads();                // copies past the last tile (zero-range) drained
 
-    constexpr int NU = NB % 2 == 0 ? NB : 2 * NB;       // lcm(2, NB)
-    auto run = [&](int t, auto phase) {
-        if constexpr (decltype(phase)::value % 2 == 0) step(t, s0, s1, phase);
-        else step(t, s1, s0, phase);
-    };
-    for (int t = 0; t < ntiles; t += NU) {
-        run(t, Const<0>{});
-        if (t + 1 < ntiles) run(t + 1, Const<1>{});
-        if (t + 2 < ntiles) run(t + 2, Const<2 % NU>{});
-        if (t + 3 < ntiles) run(t + 3, Const<3 % NU>{});
-        if constexpr (NU > 4) {
-            if (t + 4 < ntiles) run(t + 4, Const<4 % NU>{});
-            if (t + 5 < ntiles) run(t + 5, Const<5 % NU>{});
-        }
-    }
-
-    // ---- epilogue: O = A / l, LSE = ln 2 * (m c + log2 l) -------------------
-    const float ell_t = sum_with_partner(ell);
-    const float inv = ell_t > 0.0f ? 1.0f / ell_t : 0.0f;
+    // ---- epilogue: O = A / l_r, LSE = ln 2 * (r + log2 l_e) ------------------
+    const float le = sum_with_partner(ell_e);
+    const float lr = sum_with_partner(ell_r);
+    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
     if (qrow < p.Lq) {
         bf16* Op = p.o + qoff + (size_t)qrow * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
+            for (int gq = 0; gq < 4; ++gq) {
                 bf16x4 ov;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ov[j] = (bf16)(acc[db][4 * grp + j] * inv);
-                *reinterpret_cast<bf16x4*>(Op + db * 32 + 8 * grp + 4 * hi) = ov;
+                for (int j = 0; j < 4; ++j) ov[j] = (bf16)(acc[db][4 * gq + j] * inv);
+                *reinterpret_cast<bf16x4*>(Op + db * 32 + 8 * gq + 4 * hi) = ov;
             }
         if (p.lse && hi == 0)
             p.lse[(size_t)(b * p.Hq + h) * p.Lq + qrow] =
-                ell_t > 0.0f ? (m * c + log2_fast(ell_t)) * kLn2 : kNegInf;
+                le > 0.0f ? (ref + log2_fast(le)) * kLn2 : kNegInf;
     }
 }
 
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream) {
     const long long total = (long long)p.B * p.Hq * p.n_qblocks;
-    constexpr int NW = kPrefillWaves;
-    const dim3 grid((unsigned)total), block(64 * NW);
+    const dim3 grid((unsigned)total), block(512);
     if (D == 64) {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true, NW>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<64, false, NW>), grid, block, 0, stream, p);
+        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p);
     } else {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, NW>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<128, false, NW>), grid, block, 0, stream, p);
+        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
