@@ -42,11 +42,12 @@
 //
 // Softmax in base 2 with the scale folded into the exponent: p = 2^(s c - r),
 // c = scale * log2(e), r = the row's reference (FlashAttention from Scratch,
-// section 6.3, base-2 exponentials).  The reference is the running max, but
-// it is only moved, and A and l rescaled by alpha = 2^(r_old - r_new), when a
-// tile raises the row max by more than kTau in base-2 units (the conditional
-// rescaling of the FlashAttention-4 summary); between moves p <= 2^kTau, far
-// from fp32 overflow.  Because p is rounded to bf16 for the PV product, O is
+// section 6.3, base-2 exponentials).  The reference is a past row max; it is
+// only moved (to the current max), and A and l rescaled by
+// alpha = 2^(r_old - r_new), when a tile's probabilities for the row sum to
+// more than 2^kTau (the conditional rescaling of the FlashAttention-4 summary,
+// with the sum as the test so that the common path needs no row max); between
+// moves every p <= 2^kTau, far from fp32 overflow.  Because p is rounded to bf16 for the PV product, O is
 // normalised by the sum of the rounded probabilities (one v_dot2 per pair),
 // so numerator and denominator carry the same weights and a dominant key
 // passes through exactly; the LSE uses the fp32 sum of the unrounded ones.
@@ -67,8 +68,10 @@ namespace fa {
 template <int N>
 struct Const { static constexpr int value = N; };
 
-// Rows of the reference may lag the true max by up to kTau (base 2).
+// Rows of the reference may lag the true max by up to kTau (base 2): a
+// tile's probabilities sum to at most kTauSum = 2^kTau per row.
 constexpr float kTau = 8.0f;
+constexpr float kTauSum = 256.0f;
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -202,11 +205,14 @@ prefill_kernel(PrefillParams p) {
     f32x16 acc[DB];                         // O^T accumulator: rows d, column = this lane's query
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
-    bf16x8 pb[KB][2];                       // P^T of the tile whose PV product is next
+    // p of the tile whose PV product is next, as fp32 from the vector phase;
+    // the matrix phase converts it to the bf16 P^T operand (and sums the
+    // rounded values) while its score products run.
+    float pe[KB][2][8];
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    // Vector phase for tile t (scores in s): mask where needed, move the
-    // reference if the row max rose by more than kTau, then P -> pb and sums.
+    // Vector phase for tile t (scores in s): mask where needed, p -> pe and the
+    // fp32 row sum, and the rare reference move.
     auto softmax_tile = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BN;
         const bool need = (k0 + BN > n) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
@@ -221,18 +227,42 @@ prefill_kernel(PrefillParams p) {
                     if (!ok) s[kb][v] = kNegInf;
                 }
         }
-        // Row max as a tree (short dependency chains).
-        float m8[8];
+        // p = 2^(s c - r), the tile's sums and P -> bf16, against the current
+        // reference.  Four partial sums of p and two of bf16(p) keep the
+        // dependency chains short.
+        float se[4];
+        auto exponentials = [&]() __attribute__((always_inline)) {
+            const float r = ref == kNegInf ? 0.0f : ref;   // never form -inf - (-inf)
+            se[0] = se[1] = se[2] = se[3] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(s[0][j], s[0][j + 8]), fmaxf(s[1][j], s[1][j + 8]));
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
-        float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
-        mx = max_with_partner(mx);
-        const bool move = mx * c > ref + kTau;      // mx finite when true
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {  // rare after the first tile
-            const float r_new = move ? mx * c : ref;
-            const float alpha = move ? exp2_fast(ref - r_new) : 1.0f;   // 0 from an empty row
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], c, -r));
+                        se[j & 3] += pe[kb][half][j];
+                    }
+        };
+        exponentials();
+        // The reference holds while the row's tile sum of p is at most
+        // 2^kTau, which bounds every single p by 2^kTau; no row max is needed
+        // on this path.  An empty-so-far row, a larger sum, or a sum that is
+        // not finite moves it (rare after the first tile): to the true row
+        // max, with A and l rescaled, and the tile is recomputed.
+        const float row_sum = sum_with_partner((se[0] + se[1]) + (se[2] + se[3]));
+        const bool move = ref == kNegInf || !(row_sum <= kTauSum);
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            float m8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(s[0][j], s[0][j + 8]), fmaxf(s[1][j], s[1][j + 8]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
+            float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+            mx = max_with_partner(mx);
+            const bool shift = move && mx != kNegInf;   // a row with no valid key so far keeps -inf
+            const float r_new = shift ? mx * c : ref;
+            const float alpha = shift ? exp2_fast(ref - r_new) : 1.0f;   // 0 from an empty row
             ref = r_new;
             ell_e *= alpha;
             ell_r *= alpha;
@@ -240,28 +270,9 @@ prefill_kernel(PrefillParams p) {
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+            exponentials();
         }
-        const float r = ref == kNegInf ? 0.0f : ref;   // never form -inf - (-inf)
-        // Four partial sums of p and two of bf16(p) keep the chains short.
-        float se[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sr[2] = {ell_r, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                float e[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    e[j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], c, -r));
-                    se[j & 3] += e[j];
-                }
-                const bf16x8 pv = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-                pb[kb][half] = pv;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sr[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[2 * j], pv[2 * j + 1]}, ones, sr[j & 1], false);
-            }
         ell_e += (se[0] + se[1]) + (se[2] + se[3]);
-        ell_r = sr[0] + sr[1];
     };
 
     // Matrix phase M(t) as one software pipeline over its products: the KB*KS
@@ -296,10 +307,27 @@ prefill_kernel(PrefillParams p) {
                 for (int e = 0; e < 4; ++e) { frag[i][e] = lo[e]; frag[i][4 + e] = up[e]; }
             }
         };
+        // P -> bf16 operand and the rounded row sum, spread over the score
+        // products (which do not need them); the PV products come after.
+        constexpr int NP = KB * 2;           // bf16x8 operands of P^T
+        static_assert(NQ % NP == 0, "conversions per score product");
+        bf16x8 pb[KB][2];
+        float sr[2] = {0.0f, 0.0f};
+        auto convert_p = [&](int q) __attribute__((always_inline)) {
+            const int kb = q / 2, half = q % 2;
+            const float* e = pe[kb][half];
+            const bf16x8 pv = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+            pb[kb][half] = pv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sr[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[2 * j], pv[2 * j + 1]}, ones, sr[j & 1], false);
+        };
         auto mfma_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
                 const int kb = i / KS, ks = i % KS;
                 s[kb] = mfma_32x32x16(frag[i], qf[ks], ks == 0 ? zero_f32x16() : s[kb]);
+                if (i % (NQ / NP) == 0) convert_p(i / (NQ / NP));
+                if (i == NQ - 1) ell_r += sr[0] + sr[1];
             } else {
                 const int f = i - NQ;
                 const int db = f / (KB * 2), kb = (f / 2) % KB, half = f % 2;
