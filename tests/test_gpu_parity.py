@@ -184,6 +184,46 @@ def test_large_scores(dev):
     report("x20", compare(o, lse, ref_o, ref_lse))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_rising_row_max_moves_reference_mid_sequence(dev, D):
+    # Scores that climb along the keys (a ramp on K's first column, read by
+    # Q's first column with a different slope per row), so a row's max keeps
+    # rising by a few base-2 units per 64-key tile: the kernel's reference
+    # moves many times mid-sequence with probabilities between 1 and 2^8.
+    g = torch.Generator().manual_seed(31)
+    B, H, Lq, Lk = 1, 2, 40, 1100
+    q = torch.randn(B, H, Lq, D, generator=g) * 0.1
+    k = torch.randn(B, H, Lk, D, generator=g) * 0.1
+    v = torch.randn(B, H, Lk, D, generator=g)
+    q[..., 0] = torch.linspace(0.25, 2.0, Lq)
+    k[..., 0] = torch.linspace(0.0, 40.0, Lk)
+    case = W.Inputs(q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), None, 1.0, False)
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report(f"rising max D{D}", compare(o, lse, ref_o, ref_lse))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_tile_sum_alone_moves_reference(dev, D):
+    # First tile: scores 0.  Second tile: every score 3.5 / log2(e), so each
+    # p = 2^3.5 ~ 11 against the first tile's reference (far below 2^8) while
+    # a row's tile sum (~724) exceeds 2^8: only the sum test moves the
+    # reference.  The rest of the keys are random.
+    g = torch.Generator().manual_seed(32)
+    B, H, Lq, Lk = 1, 1, 64, 300
+    q = torch.zeros(B, H, Lq, D)
+    q[..., 0] = 1.0
+    k = torch.randn(B, H, Lk, D, generator=g) * 0.01
+    k[..., 0] = 0.0
+    k[0, 0, 64:128, 0] = 3.5 / math.log2(math.e)
+    k[0, 0, 128:, 0] = torch.randn(Lk - 128, generator=g)
+    v = torch.randn(B, H, Lk, D, generator=g)
+    case = W.Inputs(q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), None, 1.0, False)
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report(f"tile-sum move D{D}", compare(o, lse, ref_o, ref_lse))
+
+
 def test_causal_row_zero_is_value_row_zero_exactly(dev):
     case = W.random_case(4, 2, 4, 2, 256, 256, 128, True, None)
     o, _ = run(case, dev)
