@@ -42,8 +42,9 @@
 //
 // Softmax in base 2 with the scale folded into the exponent: p = 2^(s c - r),
 // c = scale * log2(e), r = the row's reference (FlashAttention from Scratch,
-// section 6.3, base-2 exponentials).  The reference is a past row max; it is
-// only moved (to the current max), and A and l rescaled by
+// section 6.3, base-2 exponentials).  The reference is a past row max plus
+// kTau of headroom; it is only moved (to kTau above the current max), and A
+// and l rescaled by
 // alpha = 2^(r_old - r_new), when a tile's probabilities for the row sum to
 // more than 2^kTau (the conditional rescaling of the FlashAttention-4 summary,
 // with the sum as the test so that the common path needs no row max); between
@@ -68,8 +69,9 @@ namespace fa {
 template <int N>
 struct Const { static constexpr int value = N; };
 
-// Rows of the reference may lag the true max by up to kTau (base 2): a
-// tile's probabilities sum to at most kTauSum = 2^kTau per row.
+// The reference sits kTau (base 2) above the row max when it is set, and a
+// tile's probabilities may sum to at most kTauSum = 2^kTau per row before it
+// moves again.
 constexpr float kTau = 8.0f;
 constexpr float kTauSum = 256.0f;
 
@@ -248,8 +250,10 @@ prefill_kernel(PrefillParams p) {
         // The reference holds while the row's tile sum of p is at most
         // 2^kTau, which bounds every single p by 2^kTau; no row max is needed
         // on this path.  An empty-so-far row, a larger sum, or a sum that is
-        // not finite moves it (rare after the first tile): to the true row
-        // max, with A and l rescaled, and the tile is recomputed.
+        // not finite moves it: to kTau above the true row max (so the max must
+        // rise by about 2 kTau before the next move), with A and l rescaled,
+        // and the tile is recomputed.  The move is decided per wavefront, so
+        // the headroom keeps it rare even on rows whose max keeps climbing.
         const float row_sum = sum_with_partner((se[0] + se[1]) + (se[2] + se[3]));
         const bool move = ref == kNegInf || !(row_sum <= kTauSum);
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
@@ -261,7 +265,7 @@ prefill_kernel(PrefillParams p) {
             float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
             mx = max_with_partner(mx);
             const bool shift = move && mx != kNegInf;   // a row with no valid key so far keeps -inf
-            const float r_new = shift ? mx * c : ref;
+            const float r_new = shift ? mx * c + kTau : ref;   // kTau of headroom above the max
             const float alpha = shift ? exp2_fast(ref - r_new) : 1.0f;   // 0 from an empty row
             ref = r_new;
             ell_e *= alpha;
