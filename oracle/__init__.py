@@ -19,6 +19,9 @@ streaming.streaming_head
 merge
     The partition-state merge and the log-sum-exp merge of normalised
     partials, used to pin the split-KV algebra.
+paged.paged_attention_forward / gather_sequence
+    Attention against a paged KV cache: the logical rows are gathered through
+    the page table, then evaluated by the dense definition.
 
 Every function cites the passage of the pages it follows.  All of them are
 pinned by ``tests/test_oracle.py`` to values the pages print, closed forms,
@@ -27,9 +30,10 @@ invariances, brute force on tiny inputs and a library routine.
 from .attention import as_f64, dense_head, attention_forward, attention_rows
 from .streaming import streaming_head
 from .merge import partition_state, merge_states, finish_state, merge_normalized
+from .paged import gather_sequence, paged_attention_forward
 
 __all__ = [
     "as_f64", "dense_head", "attention_forward", "attention_rows",
     "streaming_head", "partition_state", "merge_states", "finish_state",
-    "merge_normalized",
+    "merge_normalized", "gather_sequence", "paged_attention_forward",
 ]

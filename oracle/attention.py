@@ -19,6 +19,10 @@ O = softmax(S + M) V with S = scale * Q K^T and M_ij = 0 for an allowed pair,
     the saved row statistic is the natural-log LSE = m + log(l);
   * §9.2 "GQA changes the reuse opportunity": query head h reads KV head
     floor(h / r) with r = Hq / Hkv;
+  * §12 "Programmable attention": a causal window of width w allows a key
+    only at the query's position or at most w - 1 positions before it (the
+    page's formula is lost in extraction; this reading makes w the number of
+    keys a row sees once it is w or more positions into the sequence);
   * FlashAttention Cheat Sheet (mxino.github.io), §1 "The whole operation":
     Q [B, Hq, Lq, D], K and V [B, Hkv, Lk, D].
 
@@ -38,12 +42,14 @@ def as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None):
+def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None, window=0):
     """Materialised attention for one (batch, head): returns (O, LSE) in fp64.
 
     q: [Lq, D]; k: [Lk, D]; v: [Lk, Dv].  q_pos / k_pos are the absolute
     token positions of the rows (default 0..L-1); with ``causal`` a pair is
-    allowed iff k_pos[j] <= q_pos[i].
+    allowed iff k_pos[j] <= q_pos[i]; with ``window`` = w > 0 a pair is
+    allowed iff 0 <= q_pos[i] - k_pos[j] < w (the causal window, which is
+    causal by itself).
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     Lq, Lk, Dv = q.shape[0], k.shape[0], v.shape[1]
@@ -56,6 +62,9 @@ def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None):
     S = scale * (q @ k.T)
     if causal:
         S = np.where(k_pos[None, :] > q_pos[:, None], -np.inf, S)
+    if window > 0:
+        dist = q_pos[:, None] - k_pos[None, :]
+        S = np.where((dist < 0) | (dist >= window), -np.inf, S)
 
     # Row softmax with the max shift; masked entries give exp(-inf) = 0.
     m = S.max(axis=1)
@@ -79,7 +88,7 @@ def _kv_len(kv_lens, b, Lk):
     return int(min(max(int(as_f64(kv_lens)[b]), 0), Lk))
 
 
-def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None):
+def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None, window=0):
     """(O, LSE) of selected query rows of one (b, h) of a batched problem.
 
     Rows are evaluated by the same definition as ``attention_forward``; this
@@ -95,13 +104,14 @@ def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None):
     k_bg = as_f64(k[b, g, :n])
     v_bg = as_f64(v[b, g, :n])
     q_pos = (n - Lq) + rows          # bottom-right: the queries end the cache
-    return dense_head(q_bh, k_bg, v_bg, scale, causal, q_pos, np.arange(n))
+    return dense_head(q_bh, k_bg, v_bg, scale, causal, q_pos, np.arange(n), window)
 
 
-def attention_forward(q, k, v, scale, causal=False, kv_lens=None):
+def attention_forward(q, k, v, scale, causal=False, kv_lens=None, window=0):
     """Batched attention over [B, H, L, D] inputs: returns O [B, Hq, Lq, Dv]
     and LSE [B, Hq, Lq], both fp64.  ``kv_lens[b]`` (clamped to [0, Lk]) is the
-    number of valid keys of sequence b; None means all Lk are valid."""
+    number of valid keys of sequence b; None means all Lk are valid.
+    ``window`` > 0 applies the causal window of that width."""
     B, Hq, Lq = q.shape[0], q.shape[1], q.shape[2]
     Hkv, Dv = k.shape[1], v.shape[3]
     assert Hq % Hkv == 0, "query heads must be a multiple of KV heads"
@@ -109,5 +119,6 @@ def attention_forward(q, k, v, scale, causal=False, kv_lens=None):
     lse = np.zeros((B, Hq, Lq))
     for b in range(B):
         for h in range(Hq):
-            O[b, h], lse[b, h] = attention_rows(q, k, v, scale, causal, kv_lens, b, h)
+            O[b, h], lse[b, h] = attention_rows(q, k, v, scale, causal, kv_lens, b, h,
+                                                window=window)
     return O, lse

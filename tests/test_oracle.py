@@ -18,7 +18,14 @@ Pins used (none of them retypes the oracle's own formula):
   * brute force on tiny inputs: sum of e^s v over sum of e^s with no max
     shift, evaluated with math.fsum in pure Python;
   * a library routine: torch's CPU scaled_dot_product_attention in fp64 with
-    an explicit boolean mask, GQA by repeating KV heads.
+    an explicit boolean mask, GQA by repeating KV heads;
+  * causal window (FlashAttention from Scratch, §12): width 1 returns each
+    row's own value row, a window as long as the sequence is plain causal
+    attention, and brute force over the allowed pairs;
+  * paged KV (§9.3): through random page tables over NaN-filled pools the
+    result equals the contiguous cache's; the section's own experiment
+    (permute the physical pages, the table follows, the output stays
+    identical); out-of-range entries against brute force.
 """
 from __future__ import annotations
 
@@ -48,7 +55,7 @@ def oracle_namespace(mutations=()):
     """Load fresh copies of the oracle modules, optionally with textual
     mutations (module, old, new) applied, and expose their functions."""
     mods = {}
-    for name in ("attention", "streaming", "merge"):
+    for name in ("attention", "streaming", "merge", "paged"):
         path = os.path.join(ORACLE_DIR, name + ".py")
         with open(path) as f:
             src = f.read()
@@ -57,14 +64,23 @@ def oracle_namespace(mutations=()):
                 assert old in src, f"mutation target not found in {name}.py: {old!r}"
                 src = src.replace(old, new, 1)
         mod = types.ModuleType(f"_oracle_copy_{name}")
+        if name == "paged":
+            # The paged module evaluates through the (possibly mutated) copy
+            # of the dense definition instead of the package's.
+            imp = "from .attention import as_f64, dense_head\n"
+            assert imp in src
+            src = src.replace(imp, "")
+            mod.as_f64, mod.dense_head = mods["attention"].as_f64, mods["attention"].dense_head
         exec(compile(src, path, "exec"), mod.__dict__)
         mods[name] = mod
-    a, s, m = mods["attention"], mods["streaming"], mods["merge"]
+    a, s, m, pg = mods["attention"], mods["streaming"], mods["merge"], mods["paged"]
     return types.SimpleNamespace(
         dense_head=a.dense_head, attention_forward=a.attention_forward,
         attention_rows=a.attention_rows, streaming_head=s.streaming_head,
         partition_state=m.partition_state, merge_states=m.merge_states,
-        finish_state=m.finish_state, merge_normalized=m.merge_normalized)
+        finish_state=m.finish_state, merge_normalized=m.merge_normalized,
+        gather_sequence=pg.gather_sequence,
+        paged_attention_forward=pg.paged_attention_forward)
 
 
 def row_inputs(scores, values):
@@ -418,11 +434,152 @@ def check_fully_masked_rows(orc):
     assert np.all(np.isfinite(l[0, 0, 2:]))
 
 
+# ---------------------------------------------------------------------------
+# Causal window (FlashAttention from Scratch, §12) and paged KV (§9.3)
+# ---------------------------------------------------------------------------
+
+def check_window_closed_forms(orc):
+    q, k, v = rng_case(41, 9, 9, 8, 5)
+    # Width 1: every row sees only the key at its own position, so O is that
+    # value row exactly and the LSE is that one score -- with or without the
+    # causal flag, since the window is causal by itself.
+    for causal in (True, False):
+        out, lse = orc.dense_head(q, k, v, 0.3, causal, window=1)
+        assert np.array_equal(out, v)
+        close(lse, 0.3 * np.einsum("id,id->i", q, k), 1e-14)
+    # Width 3: row i is plain (unmasked) attention over keys max(0, i-2)..i.
+    out, lse = orc.dense_head(q, k, v, 0.3, True, window=3)
+    for i in range(9):
+        lo = max(0, i - 2)
+        o1, l1 = orc.dense_head(q[i:i + 1], k[lo:i + 1], v[lo:i + 1], 0.3)
+        close(out[i:i + 1], o1, 1e-15)
+        close(lse[i:i + 1], l1, 1e-15)
+    # A window at least as long as the sequence is plain causal attention.
+    oc, lc = orc.dense_head(q, k, v, 0.3, True)
+    for w in (9, 10, 100):
+        ow, lw = orc.dense_head(q, k, v, 0.3, True, window=w)
+        assert np.array_equal(ow, oc) and np.array_equal(lw, lc)
+
+
+def check_window_brute_force(orc):
+    r = np.random.default_rng(43)
+    for trial in range(25):
+        Lq, Lk = int(r.integers(1, 6)), int(r.integers(1, 7))
+        D, Dv = int(r.integers(1, 4)), int(r.integers(1, 3))
+        q = r.integers(-3, 4, (1, 1, Lq, D)).astype(float)
+        k = r.integers(-3, 4, (1, 1, Lk, D)).astype(float)
+        v = r.integers(-5, 6, (1, 1, Lk, Dv)).astype(float)
+        n = int(r.integers(0, Lk + 1))
+        for w in range(1, Lk + 2):
+            out, lse = orc.attention_forward(q, k, v, 0.5, True, [n], window=w)
+            for i in range(Lq):
+                qp = n - Lq + i
+                allowed = [j < n and 0 <= qp - j < w for j in range(Lk)]
+                bo, bl = _brute_row(q[0, 0, i].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.5, allowed)
+                if bl == -math.inf:
+                    assert lse[0, 0, i] == -math.inf and np.all(out[0, 0, i] == 0.0)
+                else:
+                    assert abs(lse[0, 0, i] - bl) <= 1e-12 * (1 + abs(bl))
+                    for c in range(Dv):
+                        assert abs(out[0, 0, i, c] - bo[c]) <= 1e-12 * (1 + abs(bo[c]))
+
+
+def _page_out(k, v, lens, page_size, num_pages, seed):
+    """Scatter contiguous [B, Hkv, Lk, D] K and V into a NaN-filled page pool
+    with a random page table; returns (k_cache, v_cache, table)."""
+    r = np.random.default_rng(seed)
+    B, Hkv, Lk, D = k.shape
+    max_pages = -(-Lk // page_size)
+    table = np.full((B, max_pages), -7, dtype=np.int64)   # unused entries hold garbage
+    order = r.permutation(num_pages)
+    kc = np.full((num_pages, Hkv, page_size, D), np.nan)
+    vc = np.full((num_pages, Hkv, page_size, v.shape[3]), np.nan)
+    nxt = 0
+    for b in range(B):
+        for slot in range(-(-lens[b] // page_size)):
+            page = order[nxt]
+            nxt += 1
+            table[b, slot] = page
+            t0, t1 = slot * page_size, min(lens[b], (slot + 1) * page_size)
+            kc[page, :, :t1 - t0] = k[b, :, t0:t1]
+            vc[page, :, :t1 - t0] = v[b, :, t0:t1]
+    return kc, vc, table
+
+
+def check_paged_matches_contiguous(orc):
+    # Paging changes only where keys live: through any page table, the
+    # result equals the contiguous cache's.  Unused pages, unused table
+    # entries and the tail of the last page hold NaN or garbage.
+    r = np.random.default_rng(47)
+    B, Hq, Hkv, Lq, Lk, D = 3, 4, 2, 3, 20, 4
+    q = r.standard_normal((B, Hq, Lq, D))
+    k = r.standard_normal((B, Hkv, Lk, D))
+    v = r.standard_normal((B, Hkv, Lk, D))
+    lens = [20, 13, 0]
+    for P in (4, 3, 20):
+        kc, vc, table = _page_out(k, v, lens, P, 12, seed=P)
+        for causal, w in ((False, 0), (True, 0), (True, 5)):
+            o1, l1 = orc.paged_attention_forward(q, kc, vc, table, lens, P, 0.5, causal, w)
+            o2, l2 = orc.attention_forward(q, k, v, 0.5, causal, lens, window=w)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def check_paged_permutation(orc):
+    # §9.3's experiment: permute the physical pages and let the table follow;
+    # every output must stay exactly the same.
+    r = np.random.default_rng(53)
+    B, Hq, Hkv, Lq, D, P, NP = 2, 2, 1, 1, 8, 4, 9
+    q = r.standard_normal((B, Hq, Lq, D))
+    kc = r.standard_normal((NP, Hkv, P, D))
+    vc = r.standard_normal((NP, Hkv, P, D))
+    table = np.array([[3, 0, 7, 5], [8, 1, 2, 6]])
+    lens = [15, 11]
+    o1, l1 = orc.paged_attention_forward(q, kc, vc, table, lens, P, 0.4)
+    perm = r.permutation(NP)              # physical page p moves to perm[p]
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[perm], vp[perm] = kc, vc
+    o2, l2 = orc.paged_attention_forward(q, kp, vp, perm[table], lens, P, 0.4)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # Without the table following, the result changes.
+    o3, _ = orc.paged_attention_forward(q, kp, vp, table, lens, P, 0.4)
+    assert not np.allclose(o1, o3)
+
+
+def check_paged_invalid_entries(orc):
+    # Tokens whose table entry is out of range are masked but keep their
+    # logical positions: brute force over the remaining allowed keys.
+    r = np.random.default_rng(59)
+    B, Hq, Hkv, Lq, D, P, NP = 1, 1, 1, 3, 2, 2, 5
+    q = r.integers(-3, 4, (B, Hq, Lq, D)).astype(float)
+    kc = r.integers(-3, 4, (NP, Hkv, P, D)).astype(float)
+    vc = r.integers(-5, 6, (NP, Hkv, P, 2)).astype(float)
+    table = np.array([[4, -1, 0, NP, 2]])
+    n = 9
+    logical_k, logical_v, valid = [], [], []
+    for t in range(n):
+        page = table[0, t // P]
+        ok = 0 <= page < NP
+        logical_k.append(kc[page, 0, t % P].tolist() if ok else [0.0] * D)
+        logical_v.append(vc[page, 0, t % P].tolist() if ok else [0.0, 0.0])
+        valid.append(ok)
+    for causal, w in ((False, 0), (True, 0), (True, 4)):
+        out, lse = orc.paged_attention_forward(q, kc, vc, table, [n], P, 0.5, causal, w)
+        for i in range(Lq):
+            qp = n - Lq + i
+            allowed = [valid[j] and (not causal or j <= qp) and (w == 0 or qp - j < w)
+                       for j in range(n)]
+            bo, bl = _brute_row(q[0, 0, i].tolist(), logical_k, logical_v, 0.5, allowed)
+            assert abs(lse[0, 0, i] - bl) <= 1e-12 * (1 + abs(bl))
+            for c in range(2):
+                assert abs(out[0, 0, i, c] - bo[c]) <= 1e-12 * (1 + abs(bo[c]))
+
+
 CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, check_two_tile,
           check_mask_table, check_streaming_vs_dense, check_merge_trees,
           check_page_streaming_experiment, check_page_split_experiment, check_brute_force,
           check_closed_forms, check_vs_sdpa, check_gqa_vs_repeated, check_kv_lens,
-          check_fully_masked_rows]
+          check_fully_masked_rows, check_window_closed_forms, check_window_brute_force,
+          check_paged_matches_contiguous, check_paged_permutation, check_paged_invalid_entries]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -458,6 +615,16 @@ MUTANTS = {
     "merge_lse_max": [("merge", "L = np.logaddexp(la, lb)", "L = np.maximum(la, lb)")],
     "merge_weight_swapped": [("merge", "return wa[:, None] * oa + wb[:, None] * ob, L",
                               "return wb[:, None] * oa + wa[:, None] * ob, L")],
+    "window_off_by_one": [("attention", "(dist >= window)", "(dist > window)")],
+    "window_not_causal": [("attention", "(dist < 0) | (dist >= window)", "(dist >= window)")],
+    "window_not_passed": [("attention", "np.arange(n), window)", "np.arange(n), 0)")],
+    "page_offset_swapped": [("paged", "cache[page, :, t % page_size, :]", "cache[page, :, t // page_size, :]")],
+    "page_index_mod": [("paged", "page = table[b, t // page_size]", "page = table[b, t % page_size]")],
+    "paged_positions_compacted": [("paged", "positions.append(t)", "positions.append(len(positions))")],
+    "paged_invalid_kept": [("paged", "if page < 0 or page >= num_pages:\n            continue",
+                            "if page < 0 or page >= num_pages:\n            page = 0")],
+    "paged_head_map": [("paged", "g = h // r", "g = h % Hkv")],
+    "paged_queries_top_left": [("paged", "q_pos = (n - Lq) + np.arange(Lq)", "q_pos = np.arange(Lq)")],
 }
 
 
