@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every entry point declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_workspace_bytes", "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_workspace_bytes",
+            "fa_status_string", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -47,6 +48,14 @@ def load_library(path: Optional[str] = None):
     lib.fa_fwd.restype = i32
     lib.fa_fwd_splits.argtypes = fwd_args + [i32]
     lib.fa_fwd_splits.restype = i32
+    # q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, window, scale, kv_lens, stream, num_splits
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, i32]
+    lib.fa_fwd_window.restype = i32
+    # q, k_cache, v_cache, o, lse, B, Hq, Hkv, Lq, D, page_table, max_pages, num_pages,
+    # page_size, kv_lens, causal, window, scale, stream, num_splits
+    lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
+                                 vp, i32, i32, f32, vp, i32]
+    lib.fa_fwd_paged.restype = i32
     lib.fa_workspace_bytes.argtypes = [i32] * 6
     lib.fa_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i32]
@@ -110,7 +119,8 @@ def fa_fwd(q, k, v, o=None, lse=None, *, causal=False, scale=None, kv_lens=None,
 
 
 class PreparedCall:
-    """fa_fwd with its arguments checked and marshalled once.
+    """fa_fwd (or fa_fwd_splits, or fa_fwd_window when ``window`` is given)
+    with its arguments checked and marshalled once.
 
     Calling the object enqueues the same forward again with no per-call
     Python checks (one ctypes call), for timing loops and serving loops where
@@ -118,19 +128,25 @@ class PreparedCall:
     the tensors alive and unchanged in shape."""
 
     def __init__(self, q, k, v, o=None, lse=None, *, causal=False, scale=None, kv_lens=None,
-                 stream=None, want_lse=True, num_splits=None):
+                 stream=None, want_lse=True, num_splits=None, window=None):
         o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, want_lse)
         scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
         s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
         self.o, self.lse = o, lse
         self._keep = (q, k, v, o, lse, kv_lens)
         lib = load_library()
-        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
-                int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), s)
-        if num_splits is None:
-            self._fn, self._args = lib.fa_fwd, args
+        if window is not None:
+            self._fn = lib.fa_fwd_window
+            self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
+                          int(window), ctypes.c_float(scale), _ptr(kv_lens), s,
+                          int(num_splits or 0))
         else:
-            self._fn, self._args = lib.fa_fwd_splits, args + (int(num_splits),)
+            args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
+                    int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), s)
+            if num_splits is None:
+                self._fn, self._args = lib.fa_fwd, args
+            else:
+                self._fn, self._args = lib.fa_fwd_splits, args + (int(num_splits),)
         self()                                   # validate now: raises on a bad argument
 
     def __call__(self):
@@ -150,3 +166,81 @@ def fa_fwd_splits(q, k, v, num_splits, o=None, lse=None, *, causal=False, scale=
     _check(lib.fa_fwd_splits(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk,
                              D, int(bool(causal)), scale, _ptr(kv_lens), s, int(num_splits)))
     return o, lse
+
+
+def fa_fwd_window(q, k, v, window, o=None, lse=None, *, scale=None, kv_lens=None, stream=None,
+                  want_lse=True, num_splits=0):
+    """Causal attention with a window of ``window`` keys (0 = plain causal)
+    through ``fa_fwd_window``; returns (o, lse)."""
+    o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    lib = load_library()
+    _check(lib.fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk,
+                             D, int(window), scale, _ptr(kv_lens), s, int(num_splits)))
+    return o, lse
+
+
+def _prepare_paged(q, k_cache, v_cache, page_table, kv_lens, o, lse, want_lse):
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+    B, Hq, Lq, D = q.shape
+    num_pages, Hkv, page_size, Dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Dk != D:
+        raise ValueError("k_cache and v_cache must be [num_pages, Hkv, page_size, D] with the D of q")
+    for name, t in (("page_table", page_table), ("kv_lens", kv_lens)):
+        if t is None or t.dtype != torch.int32 or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    if kv_lens.numel() != B:
+        raise ValueError("kv_lens must hold B entries")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device=q.device)
+    return o, lse, (B, Hq, Hkv, Lq, D, page_table.shape[1], num_pages, page_size)
+
+
+def fa_fwd_paged(q, k_cache, v_cache, page_table, kv_lens, o=None, lse=None, *, causal=False,
+                 window=0, scale=None, stream=None, want_lse=True, num_splits=0):
+    """Attention against a paged cache [num_pages, Hkv, page_size, D] through
+    ``fa_fwd_paged``; ``page_table`` is int32 [B, max_pages]; returns (o, lse)."""
+    o, lse, (B, Hq, Hkv, Lq, D, max_pages, num_pages, page_size) = _prepare_paged(
+        q, k_cache, v_cache, page_table, kv_lens, o, lse, want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    lib = load_library()
+    _check(lib.fa_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                            Lq, D, _ptr(page_table), max_pages, num_pages, page_size,
+                            _ptr(kv_lens), int(bool(causal)), int(window), scale, s,
+                            int(num_splits)))
+    return o, lse
+
+
+class PreparedPagedCall:
+    """fa_fwd_paged with its arguments checked and marshalled once (see
+    PreparedCall)."""
+
+    def __init__(self, q, k_cache, v_cache, page_table, kv_lens, o=None, lse=None, *,
+                 causal=False, window=0, scale=None, stream=None, want_lse=True, num_splits=0):
+        o, lse, (B, Hq, Hkv, Lq, D, max_pages, num_pages, page_size) = _prepare_paged(
+            q, k_cache, v_cache, page_table, kv_lens, o, lse, want_lse)
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        self.o, self.lse = o, lse
+        self._keep = (q, k_cache, v_cache, page_table, kv_lens, o, lse)
+        self._fn = load_library().fa_fwd_paged
+        self._args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq,
+                      D, _ptr(page_table), max_pages, num_pages, page_size, _ptr(kv_lens),
+                      int(bool(causal)), int(window), ctypes.c_float(scale), s, int(num_splits))
+        self()
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+        return self.o, self.lse

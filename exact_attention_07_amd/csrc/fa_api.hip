@@ -71,6 +71,23 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
     return FA_OK;
 }
 
+// Optional parts of a call beyond the contiguous fa_fwd arguments.
+struct Extra {
+    int window = 0;                 // causal window width, 0 = none
+    int requested_splits = 0;       // > 0 forces the split-KV path
+    // paged cache (page_table != nullptr): Lk of the shape is the capacity
+    const int* page_table = nullptr;
+    int max_pages = 0, num_pages = 0, page_size = 0;
+};
+
+// Keys a sequence's rows can see at most: all Lk, or under a window the
+// window's span for Lq queries plus the alignment of its start to a tile.
+int visible_span(const Shape& s, int window) {
+    if (window <= 0) return s.Lk;
+    const long long span = (long long)window + s.Lq - 1 + (kTileKeys - 1);
+    return span < s.Lk ? (int)span : s.Lk;
+}
+
 struct SplitPlan {
     int num_splits;  // partitions per sequence
     int chunk;       // keys per partition
@@ -87,11 +104,11 @@ int cu_count() {
     return cached > 0 ? cached : 256;
 }
 
-SplitPlan plan_splits(const Shape& s, int requested, int cus) {
+SplitPlan plan_splits(const Shape& s, int requested, int cus, int span) {
     SplitPlan pl;
     const int rows = (s.Hq / s.Hkv) * s.Lq;
     pl.n_groups = (rows + 31) / 32;
-    const int tiles = (s.Lk + kTileKeys - 1) / kTileKeys;
+    const int tiles = (span + kTileKeys - 1) / kTileKeys;
     int want;
     if (requested > 0) {
         want = requested;
@@ -104,14 +121,14 @@ SplitPlan plan_splits(const Shape& s, int requested, int cus) {
         const long long units = (long long)s.B * s.Hkv * pl.n_groups;
         const long long slots = 8LL * cus;
         const long long by_fill = (3 * slots + 2 * units - 1) / (2 * units);
-        const long long by_len = (s.Lk + 255) / 256;
+        const long long by_len = (span + 255) / 256;
         want = (int)(by_fill < by_len ? by_fill : by_len);
     }
     if (want > tiles) want = tiles;
     if (want < 1) want = 1;
     const int tiles_per = tiles > 0 ? (tiles + want - 1) / want : 1;
     pl.chunk = tiles_per * kTileKeys;
-    pl.num_splits = s.Lk > 0 ? (s.Lk + pl.chunk - 1) / pl.chunk : 1;
+    pl.num_splits = span > 0 ? (span + pl.chunk - 1) / pl.chunk : 1;
     return pl;
 }
 
@@ -120,8 +137,8 @@ size_t split_workspace_bytes(const Shape& s, const SplitPlan& pl) {
     return rows * pl.num_splits * ((size_t)s.D + 1) * sizeof(float);
 }
 
-bool use_split_path(const Shape& s, int requested) {
-    if (requested > 0) return true;
+bool use_split_path(const Shape& s, const Extra& x) {
+    if (x.requested_splits > 0 || x.page_table) return true;
     return s.Lq == 1;
 }
 
@@ -154,11 +171,32 @@ int get_workspace(size_t bytes, void** out) {
     return FA_OK;
 }
 
+int validate_extra(const Shape& s, int causal, const int* kv_lens, const Extra& x) {
+    if (x.requested_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    if (x.window < 0) return fail(FA_ERR_INVALID_ARG, "window must be >= 0");
+    if (x.window > 0 && !causal) return fail(FA_ERR_INVALID_ARG, "a window needs causal masking");
+    if (x.page_table) {
+        if (!kv_lens) return fail(FA_ERR_INVALID_ARG, "a paged cache needs kv_lens");
+        if (!aligned(x.page_table, 4)) return fail(FA_ERR_INVALID_ARG, "page_table must be 4-byte aligned");
+        if (x.page_size < 16 || x.page_size % 16 != 0)
+            return fail(FA_ERR_INVALID_ARG, "page_size (%d) must be a positive multiple of 16", x.page_size);
+        if (x.num_pages <= 0 || x.max_pages <= 0)
+            return fail(FA_ERR_INVALID_ARG, "num_pages (%d) and max_pages (%d) must be positive",
+                        x.num_pages, x.max_pages);
+        const long long table = (long long)s.B * x.max_pages;
+        const long long pool = (long long)x.num_pages * s.Hkv * x.page_size * s.D;
+        if (table > INT32_MAX || pool > (1LL << 46))
+            return fail(FA_ERR_INVALID_ARG, "page table or page pool too large");
+    }
+    return FA_OK;
+}
+
 int run(const void* q, const void* k, const void* v, void* o, float* lse, const Shape& s,
-        int causal, float scale, const int* kv_lens, void* stream_ptr, int requested_splits) {
+        int causal, float scale, const int* kv_lens, void* stream_ptr, const Extra& x) {
     int st = validate(q, k, v, o, lse, s, causal, scale, kv_lens);
     if (st != FA_OK) return st;
-    if (requested_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    st = validate_extra(s, causal, kv_lens, x);
+    if (st != FA_OK) return st;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
     const float c = scale * 1.4426950408889634f;  // scale * log2(e)
     const int r = s.Hq / s.Hkv;
@@ -167,7 +205,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
     const auto* vb = static_cast<const __bf16*>(v);
     auto* ob = static_cast<__bf16*>(o);
 
-    if (!use_split_path(s, requested_splits)) {
+    if (!use_split_path(s, x)) {
         fa::PrefillParams p;
         p.q = qb; p.k = kb; p.v = vb; p.o = ob; p.lse = lse; p.kv_lens = kv_lens;
         p.B = s.B; p.Hq = s.Hq; p.Hkv = s.Hkv; p.Lq = s.Lq; p.Lk = s.Lk;
@@ -175,6 +213,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
         p.n_qblocks = (s.Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
         const int units = s.B * s.Hkv;
         p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+        p.window = x.window;
         p.scale = scale;
         p.c = c;
         const long long total = (long long)s.B * s.Hq * p.n_qblocks;
@@ -184,7 +223,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
         return FA_OK;
     }
 
-    const SplitPlan pl = plan_splits(s, requested_splits, cu_count());
+    const SplitPlan pl = plan_splits(s, x.requested_splits, cu_count(), visible_span(s, x.window));
     void* ws = nullptr;
     st = get_workspace(split_workspace_bytes(s, pl), &ws);
     if (st != FA_OK) return st;
@@ -198,9 +237,12 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
     sp.B = s.B; sp.Hq = s.Hq; sp.Hkv = s.Hkv; sp.Lq = s.Lq; sp.Lk = s.Lk;
     sp.r = r; sp.rows = r * s.Lq; sp.n_groups = pl.n_groups;
     sp.num_splits = pl.num_splits; sp.chunk = pl.chunk; sp.causal = causal; sp.c = c;
+    sp.window = x.window;
+    sp.page_table = x.page_table; sp.max_pages = x.max_pages;
+    sp.num_pages = x.num_pages; sp.page_size = x.page_size;
     const long long total = (long long)s.B * s.Hkv * pl.n_groups * pl.num_splits;
     if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
-    hipError_t e = fa::launch_splitkv(s.D, sp, stream);
+    hipError_t e = fa::launch_splitkv(s.D, x.page_table != nullptr, sp, stream);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "split-KV launch: %s", hipGetErrorString(e));
 
     fa::CombineParams cp;
@@ -220,7 +262,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Lq, int Lk, int D,
            int causal, float scale, const int* kv_lens, void* stream) {
     g_last_error[0] = '\0';
-    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream, 0);
+    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream, Extra{});
 }
 
 int fa_fwd_splits(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -228,8 +270,42 @@ int fa_fwd_splits(const void* q, const void* k, const void* v, void* o, float* l
                   int causal, float scale, const int* kv_lens, void* stream,
                   int num_splits) {
     g_last_error[0] = '\0';
-    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream,
-               num_splits);
+    Extra x;
+    x.requested_splits = num_splits;
+    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream, x);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                  int window, float scale, const int* kv_lens, void* stream, int num_splits) {
+    g_last_error[0] = '\0';
+    Extra x;
+    x.window = window;
+    x.requested_splits = num_splits;
+    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, 1, scale, kv_lens, stream, x);
+}
+
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int D,
+                 const int* page_table, int max_pages, int num_pages, int page_size,
+                 const int* kv_lens, int causal, int window, float scale, void* stream,
+                 int num_splits) {
+    g_last_error[0] = '\0';
+    if (max_pages <= 0 || page_size <= 0 || (long long)max_pages * page_size > INT32_MAX / 2)
+        return fail(FA_ERR_INVALID_ARG, "max_pages (%d) and page_size (%d) must be positive and "
+                    "their product must fit 30 bits", max_pages, page_size);
+    if (!page_table) return fail(FA_ERR_INVALID_ARG, "page_table must not be NULL");
+    if (!k_cache || !v_cache) return fail(FA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL");
+    Extra x;
+    x.window = window;
+    x.requested_splits = num_splits;
+    x.page_table = page_table;
+    x.max_pages = max_pages;
+    x.num_pages = num_pages;
+    x.page_size = page_size;
+    const int capacity = max_pages * page_size;
+    return run(q, k_cache, v_cache, o, lse, Shape{B, Hq, Hkv, Lq, capacity, D}, causal, scale,
+               kv_lens, stream, x);
 }
 
 size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
@@ -238,8 +314,8 @@ size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
     memcpy(saved, g_last_error, sizeof(saved));
     const int st = validate_shape(s);
     memcpy(g_last_error, saved, sizeof(saved));
-    if (st != FA_OK || !use_split_path(s, 0)) return 0;
-    return split_workspace_bytes(s, plan_splits(s, 0, cu_count()));
+    if (st != FA_OK || !use_split_path(s, Extra{})) return 0;
+    return split_workspace_bytes(s, plan_splits(s, 0, cu_count(), s.Lk));
 }
 
 const char* fa_status_string(int status) {

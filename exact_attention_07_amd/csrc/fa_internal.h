@@ -21,13 +21,14 @@ struct PrefillParams {
     int r;                 // query heads per KV head
     int n_qblocks;         // ceil(Lq / kPrefillRows)
     int xcd_units;         // (B * Hkv) / 8 when divisible by 8, else 0
+    int window;            // causal window width (keys j with 0 <= pos_i - j < window); 0 = none
     float scale;           // softmax scale
     float c;               // scale * log2(e): scores enter exp2 as s * c
 };
 
 struct SplitParams {
     const __bf16* q;
-    const __bf16* k;
+    const __bf16* k;       // contiguous [B, Hkv, Lk, D], or the paged cache [num_pages, Hkv, page_size, D]
     const __bf16* v;
     float* part_o;         // [B * Hq * Lq, num_splits, D] fp32, normalised partial outputs
     float* part_lse;       // [B * Hq * Lq, num_splits] fp32, base-2 log-sum-exp of each partial
@@ -39,6 +40,14 @@ struct SplitParams {
     int num_splits;        // partitions per sequence
     int chunk;             // keys per partition (multiple of 32)
     int causal;
+    int window;            // causal window width, 0 = none (implies causal when > 0)
+    // Paged cache (used by the paged instantiation only): logical token t of
+    // sequence b lives in page page_table[b * max_pages + t / page_size], row
+    // t % page_size.  Lk is the capacity max_pages * page_size.
+    const int* page_table;
+    int max_pages;
+    int num_pages;
+    int page_size;         // a multiple of 16
     float c;
 };
 
@@ -55,7 +64,7 @@ struct CombineParams {
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream);
-hipError_t launch_splitkv(int D, const SplitParams& p, hipStream_t stream);
+hipError_t launch_splitkv(int D, bool paged, const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
 
 }  // namespace fa

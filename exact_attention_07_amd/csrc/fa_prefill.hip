@@ -55,7 +55,11 @@
 //
 // Causal work (section 7.3; FlashAttention-4 summary, "LPT scheduling for
 // imbalanced grids"): KV tiles past the block's last visible key are never
-// visited, elementwise masks are applied only on tiles that cross the
+// visited, nor, under a causal window of width w (section 12: a key is
+// allowed when it is at most w - 1 positions before the query), the tiles
+// wholly before the window of the block's first row; tile indices below are
+// counted from that first visited tile, so the LDS stage of a tile stays a
+// compile-time function of the loop position, elementwise masks are applied only on tiles that cross the
 // diagonal or the valid length, and query blocks are launched last-first so
 // the longest workgroups start earliest.  Workgroups of the query heads that
 // share a KV head are adjacent, and when B * Hkv is a multiple of 8 each of
@@ -75,7 +79,7 @@ struct Const { static constexpr int value = N; };
 constexpr float kTau = 8.0f;
 constexpr float kTauSum = 256.0f;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
     constexpr int NW = 8;                   // wavefronts: two groups of four
@@ -91,6 +95,7 @@ prefill_kernel(PrefillParams p) {
     constexpr int NB = 3;                   // LDS stages per operand (the tile loop is unrolled by NB)
     static_assert(BM == kPrefillRows, "host and kernel disagree on the query block");
     static_assert(NI >= 1 && (BN * CH) % NT == 0, "a tile must split evenly over the workgroup");
+    static_assert(CAUSAL || !WINDOW, "the window is causal");
 
     // K buffers at [0, NB TILE), V buffers at [NB TILE, 2 NB TILE).
     __shared__ __attribute__((aligned(16))) bf16 smem[2 * NB * TILE];
@@ -137,7 +142,11 @@ prefill_kernel(PrefillParams p) {
         const int last = min(q0 + BM, p.Lq) + off;  // keys < last are visible to some row
         kv_end = min(n, max(last, 0));
     }
-    const int ntiles = (kv_end + BN - 1) / BN;
+    // First visited tile: under a window, the one holding the lowest key
+    // visible to the block's first row (q0 + off - w + 1).
+    int tb = 0;
+    if (WINDOW) tb = max(q0 + off - p.window + 1, 0) / BN;
+    const int ntiles = (kv_end + BN - 1) / BN - tb;   // tiles visited, counted from tb
 
     const size_t qoff = (size_t)(b * p.Hq + h) * p.Lq * D;
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
@@ -165,8 +174,9 @@ prefill_kernel(PrefillParams p) {
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)smem);
     auto copy_tile = [&](const bf16* base, int t, int buf, const uint32_t (&offs)[NI]) __attribute__((always_inline)) {
-        const int rows = n - t * BN;        // valid rows from the tile start; <= 0 past the end
-        const i32x4 d = make_desc(base + kvoff + (size_t)(rows > 0 ? t : 0) * BN * D,
+        const int ta = tb + t;              // absolute tile index
+        const int rows = n - ta * BN;       // valid rows from the tile start; <= 0 past the end
+        const i32x4 d = make_desc(base + kvoff + (size_t)(rows > 0 ? ta : 0) * BN * D,
                                   (uint32_t)(rows > 0 ? rows : 0) * D * 2);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
@@ -216,8 +226,12 @@ prefill_kernel(PrefillParams p) {
     // Vector phase for tile t (scores in s): mask where needed, p -> pe and the
     // fp32 row sum, and the rare reference move.
     auto softmax_tile = [&](int t) __attribute__((always_inline)) {
-        const int k0 = t * BN;
-        const bool need = (k0 + BN > n) || (CAUSAL && (k0 + BN - 1 > qw0 + off));
+        const int k0 = (tb + t) * BN;
+        // Elementwise masks only where some pair of this wavefront's rows and
+        // the tile is out: past n, above the diagonal, or (window) at least w
+        // positions before the wavefront's last row.
+        const bool need = (k0 + BN > n) || (CAUSAL && (k0 + BN - 1 > qw0 + off)) ||
+                          (WINDOW && (qw0 + 31 + off - k0 >= p.window));
         if (need) {
             const int qpos = qrow + off;
 #pragma unroll
@@ -225,8 +239,9 @@ prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int key = k0 + kb * 32 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                    const bool ok = key < n && (!CAUSAL || key <= qpos);
-                    if (!ok) s[kb][v] = kNegInf;
+                    const bool ok = (key < n) & (!CAUSAL | (key <= qpos)) &
+                                    (!WINDOW | (qpos - key < p.window));
+                    s[kb][v] = ok ? s[kb][v] : kNegInf;   // a select, no branch
                 }
         }
         // p = 2^(s c - r), the tile's sums and P -> bf16, against the current
@@ -409,16 +424,20 @@ prefill_kernel(PrefillParams p) {
     }
 }
 
+template <int D>
+void launch_prefill_d(bool causal, bool window, const PrefillParams& p, dim3 grid, dim3 block,
+                      hipStream_t stream) {
+    if (window)      hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, block, 0, stream, p);
+    else if (causal) hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, block, 0, stream, p);
+    else             hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, block, 0, stream, p);
+}
+
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream) {
     const long long total = (long long)p.B * p.Hq * p.n_qblocks;
     const dim3 grid((unsigned)total), block(512);
-    if (D == 64) {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<64, false>), grid, block, 0, stream, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<128, false>), grid, block, 0, stream, p);
-    }
+    const bool window = causal && p.window > 0;
+    if (D == 64) launch_prefill_d<64>(causal, window, p, grid, block, stream);
+    else         launch_prefill_d<128>(causal, window, p, grid, block, stream);
     return hipGetLastError();
 }
 

@@ -28,6 +28,22 @@
 // starts past the sequence's valid length writes part_lse = -inf and nothing
 // else, so the combine needs no lengths.
 //
+// Causal window (section 12, width w: key j is allowed for the query at
+// position i when 0 <= i - j < w): partitions start at the 32-key tile that
+// holds the lowest key any packed row can see, n - Lq - w + 1, so the
+// partition plan covers only the window's span; keys before a row's own
+// window are masked in the tiles that cross it.
+//
+// Paged cache (section 9.3, "Paging changes where keys live"): logical token
+// t of sequence b lives in physical page table[b][t / P], row t % P, of a
+// cache laid out [num_pages, Hkv, P, D].  With P a multiple of 16 and tiles
+// starting at multiples of 32, each 16-key half of a tile lies in one page:
+// the loader looks up that page (a wave-uniform scalar load) and reads the
+// half through its own range-checked descriptor, so the loads stay 16-byte
+// and coalesced and everything after the loader is the contiguous kernel.
+// A table entry outside [0, num_pages) is never dereferenced: its keys are
+// read as zeros and masked.
+//
 // combine kernel: one wavefront per output row.  Lanes load the partition
 // log-sum-exps together, reduce their max and the weight sum across the
 // wavefront, then every lane accumulates its columns over all partitions with
@@ -39,7 +55,7 @@
 
 namespace fa {
 
-template <int D>
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(64, 2) splitkv_kernel(SplitParams p) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -71,7 +87,9 @@ __global__ void __launch_bounds__(64, 2) splitkv_kernel(SplitParams p) {
     const int rho = rg * 32 + (l & 31);     // packed row of this lane's column
     const bool row_ok = rho < p.rows;
     const size_t grow = (size_t)(b * p.Hq + g * p.r) * p.Lq + rho;  // row in [B*Hq*Lq]
-    const int kbeg = s * p.chunk;
+    int lo = 0;                             // first key of partition 0
+    if (p.window > 0) lo = max(n - p.Lq - p.window + 1, 0) & ~(BN - 1);
+    const int kbeg = lo + s * p.chunk;
     if (kbeg >= n) {                        // an empty partition: weight 0 in the combine
         if (row_ok && hi == 0) p.part_lse[grow * p.num_splits + s] = kNegInf;
         return;
@@ -93,17 +111,50 @@ __global__ void __launch_bounds__(64, 2) splitkv_kernel(SplitParams p) {
     // Tile t as 16-byte chunks: chunk i * 64 + lane of the row-major K and V
     // tiles; past kend the range is 0.
     bf16x8 kr[NV], vr[NV];
-    auto load_tile = [&](int t) {
+    int pv_next = 3;                        // paged: bit h = half h of the loaded tile is usable
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
         const int k0 = kbeg + t * BN;
-        const int rows = kend - k0;
-        const uint32_t bytes = (uint32_t)(rows > 0 ? rows : 0) * D * 2;
-        const size_t src = kvoff + (size_t)(rows > 0 ? k0 : 0) * D;
-        const rsrc_t kb = make_rsrc(p.k + src, bytes);
-        const rsrc_t vb = make_rsrc(p.v + src, bytes);
+        if constexpr (!PAGED) {
+            const int rows = kend - k0;
+            const uint32_t bytes = (uint32_t)(rows > 0 ? rows : 0) * D * 2;
+            const size_t src = kvoff + (size_t)(rows > 0 ? k0 : 0) * D;
+            const rsrc_t kb = make_rsrc(p.k + src, bytes);
+            const rsrc_t vb = make_rsrc(p.v + src, bytes);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) kr[i] = load16_stream(kb, (uint32_t)(i * 64 + l) * 16);
+            for (int i = 0; i < NV; ++i) kr[i] = load16_stream(kb, (uint32_t)(i * 64 + l) * 16);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) vr[i] = load16_stream(vb, (uint32_t)(i * 64 + l) * 16);
+            for (int i = 0; i < NV; ++i) vr[i] = load16_stream(vb, (uint32_t)(i * 64 + l) * 16);
+        } else {
+            // Load i covers tile rows 64 i / CH ..: the first NV / 2 loads
+            // read rows 0-15, the rest rows 16-31.
+            constexpr int NH = NV / 2;
+            rsrc_t kb[2], vb[2];
+            int pv = 0;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int r0 = k0 + 16 * hf;
+                // Wave-uniform by construction; readfirstlane keeps the
+                // descriptor in scalar registers (a clamp folded into a
+                // vector op would otherwise force a per-lane loop).
+                int rows = __builtin_amdgcn_readfirstlane(min(kend - r0, 16));
+                int page = 0;
+                if (rows > 0)
+                    page = __builtin_amdgcn_readfirstlane(p.page_table[(size_t)b * p.max_pages + r0 / p.page_size]);
+                const bool ok = (page >= 0) & (page < p.num_pages);
+                if (ok || rows <= 0) pv |= 1 << hf;
+                if (!ok) { page = 0; rows = 0; }
+                const size_t src = ((size_t)page * p.Hkv + g) * p.page_size * D +
+                                   (size_t)(r0 % p.page_size) * D;
+                const uint32_t bytes = (uint32_t)(rows > 0 ? rows : 0) * D * 2;
+                kb[hf] = make_rsrc(p.k + src, bytes);
+                vb[hf] = make_rsrc(p.v + src, bytes);
+            }
+            pv_next = pv;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) kr[i] = load16_stream(kb[i / NH], (uint32_t)((i % NH) * 64 + l) * 16);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) vr[i] = load16_stream(vb[i / NH], (uint32_t)((i % NH) * 64 + l) * 16);
+        }
     };
     // Chunk i * 64 + lane of either tile goes to row P / CH, chunk P % CH xor the swizzle.
     auto store_tile = [&](bf16* tile, const bf16x8 (&r)[NV], auto swz) {
@@ -130,6 +181,7 @@ __global__ void __launch_bounds__(64, 2) splitkv_kernel(SplitParams p) {
     load_tile(0);
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = kbeg + t * BN;
+        const int pv = pv_next;
         // K(t) and V(t) into the LDS tiles (the previous tile's reads are
         // ordered before these writes: one wavefront's LDS operations execute
         // in order), then the registers take tile t + 1.
@@ -144,13 +196,17 @@ __global__ void __launch_bounds__(64, 2) splitkv_kernel(SplitParams p) {
             sacc = mfma_32x32x16(a, qf[ks], sacc);
         }
 
-        const bool need_mask = (k0 + BN > kend) || (p.causal && k0 + BN - 1 > n - p.Lq);
+        const bool need_mask = (k0 + BN > kend) || (p.causal && k0 + BN - 1 > n - p.Lq) ||
+                               (p.window > 0 && n - 1 - k0 >= p.window) || (PAGED && pv != 3);
         if (need_mask) {
+            // Branch-free per element (bitwise &, then a select): every
+            // element's test is a straight-line select.
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int key = k0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                const bool ok = key < kend && (!p.causal || key <= qpos);
-                if (!ok) sacc[v] = kNegInf;
+                const bool ok = (key < kend) & (!p.causal | (key <= qpos)) &
+                                ((p.window == 0) | (qpos - key < p.window)) & (((pv >> (v >> 3)) & 1) != 0);
+                sacc[v] = ok ? sacc[v] : kNegInf;
             }
         }
         float mx = kNegInf;
@@ -280,11 +336,16 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineParams p) {
     if (p.lse && l == 0) p.lse[row] = lse;
 }
 
-hipError_t launch_splitkv(int D, const SplitParams& p, hipStream_t stream) {
+hipError_t launch_splitkv(int D, bool paged, const SplitParams& p, hipStream_t stream) {
     const long long total = (long long)p.B * p.Hkv * p.n_groups * p.num_splits;
     const dim3 grid((unsigned)total), block(64);
-    if (D == 64) hipLaunchKernelGGL((splitkv_kernel<64>), grid, block, 0, stream, p);
-    else         hipLaunchKernelGGL((splitkv_kernel<128>), grid, block, 0, stream, p);
+    if (D == 64) {
+        if (paged) hipLaunchKernelGGL((splitkv_kernel<64, true>), grid, block, 0, stream, p);
+        else       hipLaunchKernelGGL((splitkv_kernel<64, false>), grid, block, 0, stream, p);
+    } else {
+        if (paged) hipLaunchKernelGGL((splitkv_kernel<128, true>), grid, block, 0, stream, p);
+        else       hipLaunchKernelGGL((splitkv_kernel<128, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

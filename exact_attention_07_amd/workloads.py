@@ -22,6 +22,12 @@ Generation recipe (fixed; never changed to make a comparison pass):
   * the decode workload then draws ``kv_lens`` uniformly in [512, 8192] with
     ``torch.randint(512, 8193)``; K and V are allocated at the full capacity
     of 8192 rows per sequence and only the first ``kv_lens[b]`` are valid.
+
+Follow-on workloads reuse the draws of a base workload (its seed index) and
+change one thing: a causal window (FlashAttention from Scratch, §12) or a
+paged cache layout (§9.3).  ``page_kv`` scatters contiguous K and V into a
+page pool through a seeded random page table; it moves rows and computes
+nothing.
 """
 from __future__ import annotations
 
@@ -47,6 +53,8 @@ class Workload:
     q_boost: float = 1.0
     ragged: Optional[tuple] = None  # (lo, hi) inclusive range of kv_lens, else None
     description: str = ""
+    window: int = 0             # causal window width (0 = none)
+    page_size: int = 0          # > 0: K and V are served from a paged cache
 
     @property
     def seed(self) -> int:
@@ -70,6 +78,13 @@ WORKLOADS = [
     Workload("decode_b64_hq32_hkv8_d128_ragged", 64, 32, 8, 1, 8192, 128, False, 4,
              ragged=(512, 8192),
              description="split-KV decode, ragged kv_lens in [512, 8192]"),
+    # Follow-on variants (same draws as the base workload of the same index).
+    Workload("gqa_window4096_b1_hq32_hkv8_l16384_d128", 1, 32, 8, 16384, 16384, 128, True, 3,
+             q_boost_every=8, q_boost=4.0, window=4096,
+             description="long-context GQA forward with a causal window of 4096 keys"),
+    Workload("decode_paged16_b64_hq32_hkv8_d128_ragged", 64, 32, 8, 1, 8192, 128, False, 4,
+             ragged=(512, 8192), page_size=16,
+             description="split-KV decode from a paged cache (16-token pages, shuffled)"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -97,7 +112,50 @@ def make_inputs(w: Workload) -> Inputs:
     if w.ragged is not None:
         lo, hi = w.ragged
         kv_lens = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
-    return Inputs(q, k, v, kv_lens, w.scale, w.causal, {"workload": w.name, "seed": w.seed})
+    meta = {"workload": w.name, "seed": w.seed}
+    if w.window:
+        meta["window"] = w.window
+    if w.page_size:
+        # The paged copy of the same K and V; the contiguous tensors stay for reference.
+        meta["paged"] = page_kv(k, v, kv_lens, w.page_size, seed=w.seed + 7919)
+    return Inputs(q, k, v, kv_lens, w.scale, w.causal, meta)
+
+
+def page_kv(k: torch.Tensor, v: torch.Tensor, kv_lens, page_size: int, seed: int,
+            spare_pages: int = 7, fill: float = float("nan")):
+    """Scatter contiguous K, V [B, Hkv, Lk, D] into a page pool.
+
+    Returns (k_cache, v_cache, page_table): caches [num_pages, Hkv, P, D] of
+    k's dtype, table int32 [B, ceil(Lk / P)].  Sequence b's first kv_lens[b]
+    tokens go, page by page, to physical pages in a seeded random order; the
+    pool has ``spare_pages`` more pages than needed.  Unused pages and the
+    tail of each sequence's last page hold ``fill``; table entries past a
+    sequence's last page point at random pages of the pool (never meant to be
+    read).
+    """
+    B, Hkv, Lk, D = k.shape
+    lens = [Lk] * B if kv_lens is None else [min(max(int(x), 0), Lk) for x in kv_lens]
+    max_pages = max(1, -(-Lk // page_size))
+    need = [-(-n // page_size) for n in lens]
+    num_pages = sum(need) + spare_pages
+    g = torch.Generator().manual_seed(seed)
+    order = torch.randperm(num_pages, generator=g)
+    table = torch.randint(0, num_pages, (B, max_pages), generator=g, dtype=torch.int64)
+    kc = torch.full((num_pages, Hkv, page_size, D), fill, dtype=torch.float32).to(k.dtype)
+    vc = torch.full((num_pages, Hkv, page_size, D), fill, dtype=torch.float32).to(v.dtype)
+    nxt = 0
+    for b in range(B):
+        m, n = need[b], lens[b]
+        if m == 0:
+            continue
+        pages = order[nxt:nxt + m]
+        nxt += m
+        table[b, :m] = pages
+        for src, dst in ((k, kc), (v, vc)):
+            rows = torch.full((Hkv, m * page_size, D), fill, dtype=torch.float32).to(src.dtype)
+            rows[:, :n] = src[b, :, :n]
+            dst[pages] = rows.view(Hkv, m, page_size, D).transpose(0, 1)
+    return kc, vc, table.to(torch.int32)
 
 
 def random_case(seed: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D: int,
@@ -133,20 +191,24 @@ def valid_lengths(w_or_shape, kv_lens=None):
     return [min(max(int(x), 0), Lk) for x in kv_lens]
 
 
-def allowed_pairs(Lq: int, n: int, causal: bool) -> int:
+def allowed_pairs(Lq: int, n: int, causal: bool, window: int = 0) -> int:
     """Number of allowed (query, key) pairs in one head.
 
     Causal masking is bottom-right aligned: query i sits at absolute position
     n - Lq + i and sees keys j <= that position (FlashAttention from Scratch,
-    §5 "Rectangular causal masking is a correctness issue").
+    §5 "Rectangular causal masking is a correctness issue"); a causal window
+    of width w also drops keys j <= position - w (§12).
     """
-    if not causal:
+    if not causal and window <= 0:
         return Lq * n
     tot = 0
     off = n - Lq
-    # rows with position p = off + i see min(max(p + 1, 0), n) keys
+    # rows with position p = off + i see keys max(0, p - w + 1) .. min(p, n - 1)
     for i in range(Lq):
-        tot += min(max(off + i + 1, 0), n)
+        p = off + i
+        hi = min(p + 1, n)
+        lo = max(p - window + 1, 0) if window > 0 else 0
+        tot += max(hi - lo, 0)
     return tot
 
 
@@ -154,17 +216,20 @@ def algorithmic_flops(w, kv_lens=None) -> int:
     """4 * D FLOPs per allowed pair: two matrix products with multiply and add
     counted separately (FlashAttention from Scratch, §11.1 counts 4MNd per tile)."""
     ns = valid_lengths(w, kv_lens)
-    return sum(4 * w.D * allowed_pairs(w.Lq, n, w.causal) * w.Hq for n in ns)
+    return sum(4 * w.D * allowed_pairs(w.Lq, n, w.causal, w.window) * w.Hq for n in ns)
 
 
 def compulsory_bytes(w, kv_lens=None) -> int:
-    """Bytes that must cross HBM once: Q read, valid K and V rows read once per
-    KV head, O written (bf16) and the LSE written (fp32)."""
+    """Bytes that must cross HBM once: Q read, the K and V rows some query can
+    see read once per KV head, O written (bf16) and the LSE written (fp32);
+    with a paged cache also the page-table entries of those rows (int32)."""
     ns = valid_lengths(w, kv_lens)
     qo = 2 * w.B * w.Hq * w.Lq * w.D * 2
     lse = w.B * w.Hq * w.Lq * 4
-    kv = sum(2 * w.Hkv * n * w.D * 2 for n in ns)
-    return qo + lse + kv
+    seen = [min(n, w.window + w.Lq - 1) if w.window > 0 else n for n in ns]
+    kv = sum(2 * w.Hkv * m * w.D * 2 for m in seen)
+    table = sum(4 * -(-n // w.page_size) for n in ns) if w.page_size > 0 else 0
+    return qo + lse + kv + table
 
 
 def paper_tiled_traffic_bytes(N: int, d: int, tile: int, elem_bytes: int = 2) -> int:

@@ -69,7 +69,7 @@ typedef enum fa_status {
  * of each sequence are cut into partitions, each partition's normalised
  * output and LSE go to a library-held workspace, and a second kernel merges
  * them by their LSEs (section 4.3).  Otherwise one workgroup per (batch,
- * query head, 128-row query block) runs the whole KV loop on chip.
+ * query head, 256-row query block) runs the whole KV loop on chip.
  * The split-KV workspace is allocated by the library on first need per
  * device and grown (synchronously, with a device synchronisation) when a
  * larger one is needed; concurrent split-KV calls on different streams of
@@ -92,6 +92,51 @@ int fa_fwd_splits(const void* q, const void* k, const void* v, void* o, float* l
                   int B, int Hq, int Hkv, int Lq, int Lk, int D,
                   int causal, float scale, const int* kv_lens, void* stream,
                   int num_splits);
+
+/*
+ * Causal attention restricted to a window (FlashAttention from Scratch,
+ * section 12 "Programmable attention", a causal window of width w): query i,
+ * at absolute position p_i = n_b - Lq + i, sees key j iff 0 <= p_i - j < w and
+ * j < n_b.  (The page's formula is lost in extraction; w is read as the
+ * number of keys a row sees once it is at least w positions in.)  window = 0
+ * means no window, i.e. plain causal attention, the same as fa_fwd with
+ * causal = 1; window < 0 is FA_ERR_INVALID_ARG.  Every other argument, the
+ * layout and the path choice are those of fa_fwd_splits (num_splits = 0:
+ * decode takes the split-KV path, longer query blocks the prefill kernel).
+ * KV tiles wholly outside every row's window are never read; the split-KV
+ * partitions cover only the window's span of each sequence.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                  int window, float scale, const int* kv_lens, void* stream, int num_splits);
+
+/*
+ * Attention against a paged KV cache (FlashAttention from Scratch, section
+ * 9.3 "Paging changes where keys live"): logical token t of sequence b lives
+ * in physical page page_table[b * max_pages + t / page_size], at row
+ * t % page_size of that page.  The result is that of fa_fwd over the logical
+ * sequence (same masks, bottom-right causal alignment, GQA mapping, optional
+ * causal window as in fa_fwd_window, window = 0 for none).
+ *   k_cache, v_cache: bf16, device, contiguous [num_pages, Hkv, page_size, D]
+ *                     (each page holds page_size consecutive tokens of every
+ *                     KV head, one head's rows contiguous), 16-byte aligned;
+ *   page_table: int32, device, [B, max_pages], 4-byte aligned; only the
+ *               entries of pages that hold one of the first n_b tokens are
+ *               read.  An entry outside [0, num_pages) is never dereferenced:
+ *               its tokens count as masked (they keep their positions);
+ *   kv_lens: int32, device, [B], required; n_b = kv_lens[b] clamped to
+ *            [0, max_pages * page_size];
+ *   page_size: a positive multiple of 16; max_pages, num_pages > 0;
+ *   q, o, lse, scale, causal, D, B, Hq, Hkv, Lq, stream: as in fa_fwd.
+ * Every Lq runs on the split-KV kernels (the paged loader lives there); the
+ * automatic partition count (num_splits = 0) is fa_fwd's.  The library's
+ * split-KV workspace is shared with fa_fwd (same rules).
+ */
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int D,
+                 const int* page_table, int max_pages, int num_pages, int page_size,
+                 const int* kv_lens, int causal, int window, float scale, void* stream,
+                 int num_splits);
 
 /* Bytes of split-KV workspace fa_fwd would use for this shape (0 when it
  * takes the prefill path, or for invalid sizes). */

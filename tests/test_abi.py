@@ -103,3 +103,61 @@ def test_binding_requires_gpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         binding._prepare(q, q, q, None, None, None, True)
+
+
+def call_window(lib, window, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Lq=4, Lk=8, D=64,
+                scale=0.125, kv_lens=None, splits=0):
+    return lib.fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, window,
+                             ctypes.c_float(scale), kv_lens, None, splits)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(window=4, D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(window=4, splits=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(window=4, q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(window=4, scale=0.0), binding.FA_ERR_INVALID_ARG),
+])
+def test_window_validation(lib, kw, status):
+    got = call_window(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
+
+
+def call_paged(lib, q=P, kc=P, vc=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Lq=1, D=64, table=P,
+               max_pages=4, num_pages=8, page_size=16, kv_lens=P, causal=0, window=0,
+               scale=0.125, splits=0):
+    return lib.fa_fwd_paged(q, kc, vc, o, lse, B, Hq, Hkv, Lq, D, table, max_pages, num_pages,
+                            page_size, kv_lens, causal, window, ctypes.c_float(scale), None, splits)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(table=None), binding.FA_ERR_INVALID_ARG),
+    (dict(kv_lens=None), binding.FA_ERR_INVALID_ARG),
+    (dict(kc=None), binding.FA_ERR_INVALID_ARG),
+    (dict(page_size=8), binding.FA_ERR_INVALID_ARG),
+    (dict(page_size=24), binding.FA_ERR_INVALID_ARG),
+    (dict(page_size=0), binding.FA_ERR_INVALID_ARG),
+    (dict(num_pages=0), binding.FA_ERR_INVALID_ARG),
+    (dict(max_pages=0), binding.FA_ERR_INVALID_ARG),
+    (dict(max_pages=1 << 20, page_size=1 << 12), binding.FA_ERR_INVALID_ARG),
+    (dict(window=8), binding.FA_ERR_INVALID_ARG),            # a window needs causal
+    (dict(window=-2, causal=1), binding.FA_ERR_INVALID_ARG),
+    (dict(table=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(kc=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(D=80), binding.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), binding.FA_ERR_INVALID_ARG),
+])
+def test_paged_validation(lib, kw, status):
+    got = call_paged(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_paged_binding_requires_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(4, 1, 16, 64, dtype=torch.bfloat16)
+    t = torch.zeros(1, 4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        binding._prepare_paged(q, kc, kc, t, t[0, :1], None, None, True)

@@ -1,0 +1,227 @@
+"""GPU parity of the follow-on variants: the causal window (FlashAttention
+from Scratch, §12) and the paged KV cache (§9.3), through the C ABI against
+the fp64 oracle.
+
+Window cases span several KV tiles and query blocks with ragged tails, widths
+that are and are not multiples of the tile sizes, width 1 (each row returns
+its own value row), widths past the sequence (identical to plain causal
+attention, bit for bit), decode through the split-KV path, forced split
+counts, and the long-context GQA window workload on sampled rows.
+
+Paged cases: page sizes 16 to 256 (including 48, which is not a multiple of
+the 32-key tile), ragged lengths with partial last pages, GQA, short query
+chunks, NaN in every unused page and page tail, random valid pages in unused
+table entries, out-of-range entries (masked), the section's experiment
+(permute the physical pages, the table follows: identical bits), and the
+full-size paged decode workload, which must equal the contiguous decode bit
+for bit and the oracle within tolerance.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_07_amd import binding, workloads as W
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity import compare, sample_rows  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    if not os.path.exists(binding.LIB_PATH):
+        from exact_attention_07_amd import build
+        build.build()
+    binding.load_library()
+    return torch.device("cuda:0")
+
+
+def report(name, metrics):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}"
+                                          for k, v in metrics.items()), flush=True)
+
+
+def run_window(case, window, dev, splits=0):
+    kl = None if case.kv_lens is None else case.kv_lens.to(dev)
+    o, lse = binding.fa_fwd_window(case.q.to(dev), case.k.to(dev), case.v.to(dev), window,
+                                   scale=case.scale, kv_lens=kl, num_splits=splits)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+# ---------------------------------------------------------------------------
+# Causal window
+# ---------------------------------------------------------------------------
+
+WINDOW_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, window, kv_lens
+    (2, 4, 2, 300, 333, 64, 50, None),
+    (2, 4, 2, 300, 333, 128, 64, None),
+    (2, 4, 2, 600, 700, 64, 65, "ragged"),
+    (2, 4, 2, 600, 700, 128, 257, "ragged"),
+    (1, 8, 2, 700, 700, 128, 100, None),
+    (1, 2, 2, 257, 64, 128, 20, None),          # more queries than keys: leading rows empty
+    (4, 8, 2, 1, 1000, 128, 100, "ragged"),     # decode through the split path
+    (2, 8, 1, 1, 515, 64, 33, [515, 10]),       # decode, window longer than one sequence
+]
+
+
+@pytest.mark.parametrize("shape", WINDOW_CASES, ids=lambda s: "x".join(map(str, s[:7])) + f"_{s[7] is not None}")
+def test_window_small_cases(dev, shape):
+    B, Hq, Hkv, Lq, Lk, D, w, lens = shape
+    case = W.random_case(300 + Lq + Lk + D + w, B, Hq, Hkv, Lq, Lk, D, True, lens)
+    o, lse = run_window(case, w, dev)
+    ref_o, ref_lse = oracle.attention_forward(case.q, case.k, case.v, case.scale, True,
+                                              case.kv_lens, window=w)
+    report(f"window {shape}", compare(o, lse, ref_o, ref_lse))
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 3, 900, 128, 130, "ragged"),
+                                   (1, 4, 4, 40, 600, 64, 77, None)])
+def test_window_split_path(dev, shape, splits):
+    B, Hq, Hkv, Lq, Lk, D, w, lens = shape
+    case = W.random_case(400 + Lq + splits, B, Hq, Hkv, Lq, Lk, D, True, lens)
+    o, lse = run_window(case, w, dev, splits=splits)
+    ref_o, ref_lse = oracle.attention_forward(case.q, case.k, case.v, case.scale, True,
+                                              case.kv_lens, window=w)
+    report(f"window split {splits} {shape}", compare(o, lse, ref_o, ref_lse))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_window_of_one_returns_own_value_row(dev, D):
+    case = W.random_case(500 + D, 1, 2, 2, 300, 300, D, True, None)
+    o, lse = run_window(case, 1, dev)
+    # Width 1: the only key of row i is key i, so O is V's row rounded to bf16
+    # through p = 1 (exact) and division by 1.
+    assert torch.equal(o, case.v)
+    s = case.scale * (case.q.double() * case.k.double()).sum(-1)
+    assert float((lse.double() - s).abs().max()) <= 1e-3
+
+
+@pytest.mark.parametrize("Lq,Lk,D", [(300, 333, 64), (513, 513, 128), (1, 700, 128)])
+def test_window_past_sequence_equals_causal_bitwise(dev, Lq, Lk, D):
+    case = W.random_case(600 + Lq, 2, 4, 2, Lq, Lk, D, True, "ragged")
+    kl = case.kv_lens.to(dev)
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    o1, l1 = binding.fa_fwd(q, k, v, causal=True, kv_lens=kl)
+    for w in (Lk, Lk + 1000, 0):
+        o2, l2 = binding.fa_fwd_window(q, k, v, w, kv_lens=kl)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), w
+
+
+def test_window_gqa_long_context_sampled(dev):
+    w = W.BY_NAME["gqa_window4096_b1_hq32_hkv8_l16384_d128"]
+    case = W.make_inputs(w)
+    o, lse = run_window(case, w.window, dev)
+    rows = sample_rows(w.Lq, seed=7)
+    go, gl, ro, rl = [], [], [], []
+    for h in range(w.Hq):
+        ref_o, ref_lse = oracle.attention_rows(case.q, case.k, case.v, case.scale, True, None, 0, h,
+                                               rows, window=w.window)
+        go.append(o[0, h, rows]); gl.append(lse[0, h, rows]); ro.append(ref_o); rl.append(ref_lse)
+    report(w.name, compare(torch.stack(go), torch.stack(gl), np.stack(ro), np.stack(rl)))
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache
+# ---------------------------------------------------------------------------
+
+def run_paged(case, kc, vc, table, dev, causal=False, window=0, splits=0):
+    o, lse = binding.fa_fwd_paged(case.q.to(dev), kc.to(dev), vc.to(dev), table.to(dev),
+                                  case.kv_lens.to(dev), causal=causal, window=window,
+                                  scale=case.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+PAGED_CASES = [
+    # B, Hq, Hkv, Lq, Lk (capacity), D, page_size, causal, window
+    (4, 8, 2, 1, 1000, 128, 16, False, 0),
+    (4, 8, 2, 1, 1000, 64, 16, False, 0),
+    (3, 4, 4, 1, 777, 128, 32, False, 0),
+    (3, 8, 1, 1, 1024, 128, 48, False, 0),
+    (2, 8, 2, 1, 2048, 64, 256, False, 0),
+    (3, 4, 2, 5, 640, 128, 64, True, 0),        # a short causal query chunk
+    (3, 8, 2, 1, 1500, 128, 16, True, 200),     # decode with a causal window
+    (2, 4, 2, 7, 900, 64, 32, True, 45),
+]
+
+
+@pytest.mark.parametrize("shape", PAGED_CASES, ids=lambda s: "x".join(map(str, s)))
+def test_paged_small_cases(dev, shape):
+    B, Hq, Hkv, Lq, Lk, D, P, causal, w = shape
+    case = W.random_case(700 + Lk + P + D, B, Hq, Hkv, Lq, Lk, D, causal, "ragged")
+    kc, vc, table = W.page_kv(case.k, case.v, case.kv_lens, P, seed=P + Lk)
+    o, lse = run_paged(case, kc, vc, table, dev, causal, w)
+    ref_o, ref_lse = oracle.paged_attention_forward(case.q, kc, vc, table, case.kv_lens, P,
+                                                    case.scale, causal, w)
+    report(f"paged {shape}", compare(o, lse, ref_o, ref_lse))
+    # Paging changes only where keys live: the contiguous definition agrees.
+    ref2_o, ref2_lse = oracle.attention_forward(case.q, case.k, case.v, case.scale, causal,
+                                                case.kv_lens, window=w)
+    assert np.array_equal(ref_o, ref2_o) and np.array_equal(ref_lse, ref2_lse)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_paged_any_partition_count(dev, splits):
+    case = W.random_case(800 + splits, 3, 8, 2, 1, 1200, 128, False, "ragged")
+    kc, vc, table = W.page_kv(case.k, case.v, case.kv_lens, 16, seed=splits)
+    o, lse = run_paged(case, kc, vc, table, dev, splits=splits)
+    ref_o, ref_lse = oracle.paged_attention_forward(case.q, kc, vc, table, case.kv_lens, 16,
+                                                    case.scale)
+    report(f"paged splits {splits}", compare(o, lse, ref_o, ref_lse))
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_paged_permuting_physical_pages_changes_nothing(dev, P):
+    # The experiment of "Paging changes where keys live": move every physical
+    # page, let the table follow, and the outputs stay identical bit for bit.
+    case = W.random_case(900 + P, 4, 8, 2, 1, 1500, 128, False, "ragged")
+    kc, vc, table = W.page_kv(case.k, case.v, case.kv_lens, P, seed=P)
+    o1, l1 = run_paged(case, kc, vc, table, dev)
+    perm = torch.randperm(kc.shape[0], generator=torch.Generator().manual_seed(P))
+    kp, vp = torch.empty_like(kc), torch.empty_like(vc)
+    kp[perm], vp[perm] = kc, vc
+    o2, l2 = run_paged(case, kp, vp, perm[table.long()].to(torch.int32), dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref_o, ref_lse = oracle.paged_attention_forward(case.q, kc, vc, table, case.kv_lens, P, case.scale)
+    report(f"paged permutation P={P}", compare(o1, l1, ref_o, ref_lse))
+
+
+def test_paged_out_of_range_entries_are_masked(dev):
+    case = W.random_case(950, 3, 4, 2, 2, 512, 64, True, [512, 300, 200])
+    kc, vc, table = W.page_kv(case.k, case.v, case.kv_lens, 32, seed=3)
+    num_pages = kc.shape[0]
+    table = table.clone()
+    table[0, 3] = -1                    # tokens 96..127 of sequence 0
+    table[0, 15] = num_pages            # its last 32 tokens, the queries' own positions
+    table[1, 0] = num_pages + 1000      # tokens 0..31 of sequence 1
+    table[2, :7] = -5                   # every page of sequence 2 (200 tokens)
+    o, lse = run_paged(case, kc, vc, table, dev, causal=True)
+    ref_o, ref_lse = oracle.paged_attention_forward(case.q, kc, vc, table, case.kv_lens, 32,
+                                                    case.scale, True)
+    assert np.all(ref_lse[2] == -np.inf)   # every page of sequence 2 is out of range
+    report("paged out-of-range entries", compare(o, lse, ref_o, ref_lse))
+
+
+def test_paged_decode_workload_matches_contiguous_bitwise(dev):
+    w = W.BY_NAME["decode_paged16_b64_hq32_hkv8_d128_ragged"]
+    case = W.make_inputs(w)
+    kc, vc, table = case.meta["paged"]
+    o, lse = run_paged(case, kc, vc, table, dev)
+    kl = case.kv_lens.to(dev)
+    o2, l2 = binding.fa_fwd(case.q.to(dev), case.k.to(dev), case.v.to(dev), kv_lens=kl)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2.cpu()) and torch.equal(lse, l2.cpu())
+    ref_o, ref_lse = oracle.attention_forward(case.q, case.k, case.v, case.scale, False, case.kv_lens)
+    report(w.name, compare(o, lse, ref_o, ref_lse))
