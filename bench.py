@@ -6,8 +6,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extr
 A step is one fa_fwd call over one batch of the workload's seeded synthetic
 input, resident in HBM before timing starts.  The headline workload is the
 non-causal prefill B=4, Hq=Hkv=16, Lq=Lk=1024, D=64; the causal, long-context
-GQA and split-KV decode workloads are timed the same way and reported under
-"workloads".  Time is taken with HIP events on the stream the kernels are
+GQA and split-KV decode workloads, and the follow-on variants (the GQA
+workload under a causal window of 4096 keys; the decode workload served from
+a shuffled paged cache with 16-token pages), are timed the same way and
+reported under "workloads".  Time is taken with HIP events on the stream the kernels are
 launched on (torch's current stream), bracketed by device synchronisation.
 
 Printed: one JSON line with the metric, throughput, a roofline object for the
@@ -65,13 +67,22 @@ def time_workload(w, steps, warmup, dev):
     from exact_attention_07_amd import binding, workloads as W
 
     inp = W.make_inputs(w)
-    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    q = inp.q.to(dev)
     kl = None if inp.kv_lens is None else inp.kv_lens.to(dev)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.Lq, dtype=torch.float32, device=dev)
     # Arguments are checked and marshalled once; each step is one C-ABI call,
     # so host overhead stays below the kernel time.
-    call = binding.PreparedCall(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=kl)
+    if w.page_size:
+        # Only the paged copy of K and V is resident for a paged workload.
+        kc, vc, table = (t.to(dev) for t in inp.meta["paged"])
+        k, v = kc, vc
+        call = binding.PreparedPagedCall(q, kc, vc, table.contiguous(), kl, o, lse, causal=w.causal,
+                                         window=w.window, scale=w.scale)
+    else:
+        k, v = inp.k.to(dev), inp.v.to(dev)
+        call = binding.PreparedCall(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=kl,
+                                    window=w.window if w.window else None)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -111,17 +122,19 @@ def cpu_baseline(w, inp, seconds):
     heads = 0
     t0 = time.perf_counter()
     total_heads = w.B * w.Hq
-    for idx in range(total_heads):
-        b, h = divmod(idx, w.Hq)
-        oracle.attention_rows(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens, b, h)
-        pairs = W.allowed_pairs(w.Lq, ns[b], w.causal)
+    # (batch, query head) units in order, wrapping around the workload until
+    # about ``seconds`` of CPU work is done.
+    while time.perf_counter() - t0 < seconds:
+        b, h = divmod(heads % total_heads, w.Hq)
+        oracle.attention_rows(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens, b, h,
+                              window=w.window)
+        pairs = W.allowed_pairs(w.Lq, ns[b], w.causal, w.window)
         done_flops += 4 * w.D * pairs
         done_bytes += (2 * w.Lq * w.D * 2 + w.Lq * 4) + 2 * ns[b] * w.D * 2 // (w.Hq // w.Hkv)
         heads += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
     dt = time.perf_counter() - t0
-    sample = f"{heads} of {total_heads} (batch, query head) units, all rows, fp64, {dt:.1f} s"
+    sample = (f"{heads} (batch, query head) units of {total_heads} in the workload "
+              f"({heads / total_heads:.2f} passes), all rows, fp64, {dt:.1f} s")
     if w.Lq == 1:
         return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": sample}
