@@ -19,6 +19,8 @@ streaming.streaming_head
 merge
     The partition-state merge and the log-sum-exp merge of normalised
     partials, used to pin the split-KV algebra.
+backward.dense_backward_head / attention_backward
+    The gradients dQ, dK, dV written out densely (S, P, dP, dS materialised).
 paged.paged_attention_forward / gather_sequence
     Attention against a paged KV cache: the logical rows are gathered through
     the page table, then evaluated by the dense definition.
@@ -31,9 +33,11 @@ from .attention import as_f64, dense_head, attention_forward, attention_rows
 from .streaming import streaming_head
 from .merge import partition_state, merge_states, finish_state, merge_normalized
 from .paged import gather_sequence, paged_attention_forward
+from .backward import dense_backward_head, attention_backward
 
 __all__ = [
     "as_f64", "dense_head", "attention_forward", "attention_rows",
     "streaming_head", "partition_state", "merge_states", "finish_state",
     "merge_normalized", "gather_sequence", "paged_attention_forward",
+    "dense_backward_head", "attention_backward",
 ]

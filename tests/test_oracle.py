@@ -55,7 +55,7 @@ def oracle_namespace(mutations=()):
     """Load fresh copies of the oracle modules, optionally with textual
     mutations (module, old, new) applied, and expose their functions."""
     mods = {}
-    for name in ("attention", "streaming", "merge", "paged"):
+    for name in ("attention", "streaming", "merge", "paged", "backward"):
         path = os.path.join(ORACLE_DIR, name + ".py")
         with open(path) as f:
             src = f.read()
@@ -71,16 +71,23 @@ def oracle_namespace(mutations=()):
             assert imp in src
             src = src.replace(imp, "")
             mod.as_f64, mod.dense_head = mods["attention"].as_f64, mods["attention"].dense_head
+        if name == "backward":
+            imp = "from .attention import as_f64\n"
+            assert imp in src
+            src = src.replace(imp, "")
+            mod.as_f64 = mods["attention"].as_f64
         exec(compile(src, path, "exec"), mod.__dict__)
         mods[name] = mod
-    a, s, m, pg = mods["attention"], mods["streaming"], mods["merge"], mods["paged"]
+    a, s, m, pg, bw = (mods["attention"], mods["streaming"], mods["merge"], mods["paged"],
+                       mods["backward"])
     return types.SimpleNamespace(
         dense_head=a.dense_head, attention_forward=a.attention_forward,
         attention_rows=a.attention_rows, streaming_head=s.streaming_head,
         partition_state=m.partition_state, merge_states=m.merge_states,
         finish_state=m.finish_state, merge_normalized=m.merge_normalized,
         gather_sequence=pg.gather_sequence,
-        paged_attention_forward=pg.paged_attention_forward)
+        paged_attention_forward=pg.paged_attention_forward,
+        dense_backward_head=bw.dense_backward_head, attention_backward=bw.attention_backward)
 
 
 def row_inputs(scores, values):
@@ -574,12 +581,127 @@ def check_paged_invalid_entries(orc):
                 assert abs(out[0, 0, i, c] - bo[c]) <= 1e-12 * (1 + abs(bo[c]))
 
 
+# ---------------------------------------------------------------------------
+# Backward (FlashAttention from Scratch, §8)
+# ---------------------------------------------------------------------------
+
+def _torch_masked_attention(q, k, v, scale, allowed):
+    """Dense softmax attention in torch fp64 with a boolean allowed mask
+    (no empty rows), for autograd."""
+    s = scale * (q @ k.transpose(-1, -2))
+    s = s.masked_fill(~allowed, -math.inf)
+    return torch.softmax(s, dim=-1) @ v
+
+
+def check_backward_page_experiment(orc):
+    # §8's own check, re-derived: seed 8, q 5x7, k 9x7, v 9x3, causal with
+    # the queries at positions 4..8; the gradients must match autograd
+    # through a dense softmax to 1e-10.
+    torch.manual_seed(8)
+    qg = torch.randn(5, 7, dtype=torch.float64, requires_grad=True)
+    kg = torch.randn(9, 7, dtype=torch.float64, requires_grad=True)
+    vg = torch.randn(9, 3, dtype=torch.float64, requires_grad=True)
+    qp, kp = torch.arange(4, 9), torch.arange(9)
+    allowed = kp[None, :] <= qp[:, None]
+    scale = 1.0 / math.sqrt(7)
+    og = _torch_masked_attention(qg, kg, vg, scale, allowed)
+    g = torch.randn_like(og)
+    expected = torch.autograd.grad(og, (qg, kg, vg), g)
+    got = orc.dense_backward_head(qg.detach(), kg.detach(), vg.detach(), g, scale, True,
+                                  q_pos=qp.numpy(), k_pos=kp.numpy())
+    for a, b in zip(got, expected):
+        close(a, b.numpy(), 1e-10)
+
+
+def check_backward_vs_autograd(orc):
+    # Batched, GQA, kv_lens, causal / window, against torch autograd through
+    # a dense masked softmax (every row keeps at least one key).
+    g0 = torch.Generator().manual_seed(61)
+    B, Hq, Hkv, Lq, Lk, D = 2, 6, 2, 4, 9, 5
+    q = torch.randn(B, Hq, Lq, D, generator=g0, dtype=torch.float64)
+    k = torch.randn(B, Hkv, Lk, D, generator=g0, dtype=torch.float64)
+    v = torch.randn(B, Hkv, Lk, D, generator=g0, dtype=torch.float64)
+    gout = torch.randn(B, Hq, Lq, D, generator=g0, dtype=torch.float64)
+    lens = [9, 6]
+    scale = 0.4
+    for causal, w in ((False, 0), (True, 0), (True, 3)):
+        qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+        r = Hq // Hkv
+        outs = []
+        for b in range(B):
+            n = lens[b]
+            qp, kp = torch.arange(n - Lq, n), torch.arange(n)
+            allowed = torch.ones(Lq, n, dtype=torch.bool)
+            if causal:
+                allowed &= kp[None, :] <= qp[:, None]
+            if w:
+                allowed &= (qp[:, None] - kp[None, :]) < w
+            for h in range(Hq):
+                outs.append(_torch_masked_attention(qq[b, h], kk[b, h // r, :n], vv[b, h // r, :n],
+                                                    scale, allowed))
+        o = torch.stack(outs).view(B, Hq, Lq, D)
+        expected = torch.autograd.grad(o, (qq, kk, vv), gout)
+        got = orc.attention_backward(q, k, v, gout, scale, causal, lens, window=w)
+        for a, e in zip(got, expected):
+            close(a, e.numpy(), 1e-12)
+
+
+def check_backward_finite_differences(orc):
+    # Central differences of L = sum(G * O) through the forward definition
+    # (attention.dense_head), on a tiny causal case with an empty row.
+    r = np.random.default_rng(67)
+    Lq, Lk, D = 3, 4, 2
+    q, k, v = r.standard_normal((Lq, D)), r.standard_normal((Lk, D)), r.standard_normal((Lk, D))
+    g = r.standard_normal((Lq, D))
+    qp = np.array([-1, 1, 3])           # row 0 sees no key
+    scale, eps = 0.7, 1e-6
+
+    def loss(qq, kk, vv):
+        o, _ = orc.dense_head(qq, kk, vv, scale, True, q_pos=qp)
+        return float((g * o).sum())
+
+    got = orc.dense_backward_head(q, k, v, g, scale, True, q_pos=qp)
+    for idx, x in enumerate((q, k, v)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(*x.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[idx][pos] += eps
+            args_m[idx][pos] -= eps
+            num[pos] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        close(got[idx], num, 1e-7)
+    assert np.all(got[0][0] == 0.0)     # the empty row has no gradient
+
+
+def check_backward_gqa_and_lengths(orc):
+    # A shared KV head's gradient is the sum of the gradients each query head
+    # gives it; keys at or past kv_lens get zero gradient and the rest equal
+    # the gradients of the truncated problem.
+    r = np.random.default_rng(71)
+    B, Hq, Hkv, L, D = 1, 4, 2, 6, 3
+    q, k, v, g = (r.standard_normal((B, h, L, D)) for h in (Hq, Hkv, Hkv, Hq))
+    dq, dk, dv = orc.attention_backward(q, k, v, g, 0.5, True)
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    dq2, dk2, dv2 = orc.attention_backward(q, kr, vr, g, 0.5, True)
+    close(dq, dq2, 1e-14)
+    close(dk, dk2.reshape(B, Hkv, 2, L, D).sum(axis=2), 1e-14)
+    close(dv, dv2.reshape(B, Hkv, 2, L, D).sum(axis=2), 1e-14)
+    dq3, dk3, dv3 = orc.attention_backward(q, k, v, g, 0.5, True, kv_lens=[4])
+    assert np.all(dk3[:, :, 4:] == 0.0) and np.all(dv3[:, :, 4:] == 0.0)
+    dq4, dk4, dv4 = orc.attention_backward(q, k[:, :, :4], v[:, :, :4], g, 0.5, True)
+    close(dq3, dq4, 1e-15)
+    close(dk3[:, :, :4], dk4, 1e-15)
+    close(dv3[:, :, :4], dv4, 1e-15)
+
+
 CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, check_two_tile,
           check_mask_table, check_streaming_vs_dense, check_merge_trees,
           check_page_streaming_experiment, check_page_split_experiment, check_brute_force,
           check_closed_forms, check_vs_sdpa, check_gqa_vs_repeated, check_kv_lens,
           check_fully_masked_rows, check_window_closed_forms, check_window_brute_force,
-          check_paged_matches_contiguous, check_paged_permutation, check_paged_invalid_entries]
+          check_paged_matches_contiguous, check_paged_permutation, check_paged_invalid_entries,
+          check_backward_page_experiment, check_backward_vs_autograd, check_backward_finite_differences,
+          check_backward_gqa_and_lengths]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -625,6 +747,15 @@ MUTANTS = {
                             "if page < 0 or page >= num_pages:\n            page = 0")],
     "paged_head_map": [("paged", "g = h // r", "g = h % Hkv")],
     "paged_queries_top_left": [("paged", "q_pos = (n - Lq) + np.arange(Lq)", "q_pos = np.arange(Lq)")],
+    "bwd_delta_dropped": [("backward", "dS = P * (dP - delta[:, None])", "dS = P * dP")],
+    "bwd_delta_wrong": [("backward", "delta = (g * O).sum(axis=1)", "delta = g.sum(axis=1)")],
+    "bwd_dq_unscaled": [("backward", "dQ = scale * (dS @ k)", "dQ = (dS @ k)")],
+    "bwd_dk_sign": [("backward", "dK = scale * (dS.T @ q)", "dK = -scale * (dS.T @ q)")],
+    "bwd_dv_from_ds": [("backward", "dV = P.T @ g", "dV = dS.T @ g")],
+    "bwd_gqa_not_summed": [("backward", "dk[b, gk, :n] += dkh", "dk[b, gk, :n] = dkh")],
+    "bwd_causal_dropped": [("backward", "allowed &= k_pos[None, :] <= q_pos[:, None]", "allowed &= True")],
+    "bwd_top_left": [("backward", "q_pos = (n - Lq) + np.arange(Lq)", "q_pos = np.arange(Lq)")],
+    "bwd_window_off_by_one": [("backward", "(dist < window)", "(dist <= window)")],
 }
 
 
