@@ -4,7 +4,7 @@
 ``exact_attention_07_amd.binding``).  Importing the package loads nothing;
 the first call into the library loads it and raises if it has not been built.
 """
-_EXPORTS = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_workspace_bytes",
+_EXPORTS = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_bwd", "fa_workspace_bytes",
             "fa_status_string", "load_library", "FaError", "PreparedCall", "PreparedPagedCall")
 
 

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every entry point declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_workspace_bytes",
-            "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_bwd",
+            "fa_workspace_bytes", "fa_status_string", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -56,6 +56,9 @@ def load_library(path: Optional[str] = None):
     lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
                                  vp, i32, i32, f32, vp, i32]
     lib.fa_fwd_paged.restype = i32
+    # q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, causal, window, scale, kv_lens, stream
+    lib.fa_bwd.argtypes = [vp] * 9 + [i32] * 8 + [f32, vp, vp]
+    lib.fa_bwd.restype = i32
     lib.fa_workspace_bytes.argtypes = [i32] * 6
     lib.fa_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i32]
@@ -244,3 +247,26 @@ class PreparedPagedCall:
         if status != FA_OK:
             _check(status)
         return self.o, self.lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, *, causal=False, window=0, scale=None,
+           kv_lens=None, stream=None):
+    """dQ, dK, dV of the attention forward through ``fa_bwd``; ``o`` and ``lse``
+    are the forward's outputs for the same arguments.  Returns (dq, dk, dv)."""
+    _, _, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, True)
+    for name, t in (("o", o), ("dout", dout)):
+        if t is None or t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(q.shape) \
+                or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor shaped like q")
+    if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq) \
+            or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, Hq, Lq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    _check(load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Lq, Lk, D,
+                                 int(bool(causal)), int(window), scale, _ptr(kv_lens), s))
+    return dq, dk, dv

@@ -308,6 +308,49 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
                kv_lens, stream, x);
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Lq, int Lk, int D,
+           int causal, int window, float scale, const int* kv_lens, void* stream) {
+    g_last_error[0] = '\0';
+    const Shape s{B, Hq, Hkv, Lq, Lk, D};
+    int st = validate(q, k, v, dq, nullptr, s, causal, scale, kv_lens);
+    if (st != FA_OK) return st;
+    if (!o || !dout || !lse || !dk || !dv)
+        return fail(FA_ERR_INVALID_ARG, "o, dout, lse, dk and dv must not be NULL");
+    if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+        return fail(FA_ERR_INVALID_ARG, "o, dout, dk and dv must be 16-byte aligned, lse 4-byte aligned");
+    if (window < 0) return fail(FA_ERR_INVALID_ARG, "window must be >= 0");
+    if (window > 0 && !causal) return fail(FA_ERR_INVALID_ARG, "a window needs causal masking");
+    void* ws = nullptr;
+    st = get_workspace((size_t)B * Hq * Lq * sizeof(float), &ws);
+    if (st != FA_OK) return st;
+    fa::BwdParams p;
+    p.q = static_cast<const __bf16*>(q);
+    p.k = static_cast<const __bf16*>(k);
+    p.v = static_cast<const __bf16*>(v);
+    p.o = static_cast<const __bf16*>(o);
+    p.dout = static_cast<const __bf16*>(dout);
+    p.lse = lse;
+    p.delta = static_cast<float*>(ws);
+    p.dq = static_cast<__bf16*>(dq);
+    p.dk = static_cast<__bf16*>(dk);
+    p.dv = static_cast<__bf16*>(dv);
+    p.kv_lens = kv_lens;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk;
+    p.r = Hq / Hkv;
+    p.causal = causal;
+    p.window = window;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    const long long nq = (long long)B * Hq * ((Lq + 31) / 32);
+    const long long nk = (long long)B * Hkv * ((Lk + 31) / 32);
+    if (nq > INT32_MAX || nk > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    hipError_t e = fa::launch_backward(D, p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
 size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
     const Shape s{B, Hq, Hkv, Lq, Lk, D};
     char saved[sizeof(g_last_error)];

@@ -62,9 +62,31 @@ struct CombineParams {
     int chunk;
 };
 
+struct BwdParams {
+    const __bf16* q;       // [B, Hq, Lq, D]
+    const __bf16* k;       // [B, Hkv, Lk, D]
+    const __bf16* v;
+    const __bf16* o;       // the forward's output [B, Hq, Lq, D]
+    const __bf16* dout;    // dL/dO [B, Hq, Lq, D]
+    const float* lse;      // the forward's natural-log LSE [B, Hq, Lq]
+    float* delta;          // workspace [B, Hq, Lq]: rowsum(dO * O), written by the dq kernel
+    __bf16* dq;            // [B, Hq, Lq, D]
+    __bf16* dk;            // [B, Hkv, Lk, D]
+    __bf16* dv;
+    const int* kv_lens;    // may be null
+    int B, Hq, Hkv, Lq, Lk;
+    int r;                 // query heads per KV head
+    int causal;
+    int window;            // causal window width, 0 = none
+    float scale;           // softmax scale c
+    float c;               // scale * log2(e)
+};
+
 // Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream);
 hipError_t launch_splitkv(int D, bool paged, const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
+// The dq kernel (which also writes delta) then the dk/dv kernel.
+hipError_t launch_backward(int D, const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

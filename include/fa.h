@@ -138,6 +138,31 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
                  const int* kv_lens, int causal, int window, float scale, void* stream,
                  int num_splits);
 
+/*
+ * Backward of the attention forward by recomputation (FlashAttention from
+ * Scratch, section 8 "Backward: spend arithmetic to save memory"): given the
+ * forward's inputs, its output o and natural-log lse (as written by fa_fwd or
+ * fa_fwd_window with the same arguments), and dout = dL/dO, writes
+ *     dq = dL/dQ [B, Hq, Lq, D], dk = dL/dK and dv = dL/dV [B, Hkv, Lk, D]
+ * (bf16, device, contiguous, 16-byte aligned; every element is written: keys
+ * at or past n_b and rows of no allowed pair get zero).  With c = scale:
+ * P_ij = exp(c q_i.k_j - lse_i) on allowed pairs, dV = P^T dO, dP = dO V^T,
+ * delta_i = dO_i . O_i, dS = P (dP - delta), dQ = c dS K, dK = c dS^T Q; the
+ * gradients of a KV head sum over the Hq/Hkv query heads that read it.
+ *   q, k, v, o, dout: bf16 device tensors in the layouts of fa_fwd;
+ *   lse: fp32 [B, Hq, Lq] (required);
+ *   causal, window, scale, kv_lens: the forward's (window = 0: none; a window
+ *   needs causal = 1).
+ * Two kernels run on `stream`: a query-owned one for dq (which also forms
+ * delta into the library workspace, shared with the split-KV path and with
+ * the same rules) and a KV-owned one for dk and dv.  No atomics: the result is
+ * deterministic.  Errors as for fa_fwd.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Lq, int Lk, int D,
+           int causal, int window, float scale, const int* kv_lens, void* stream);
+
 /* Bytes of split-KV workspace fa_fwd would use for this shape (0 when it
  * takes the prefill path, or for invalid sizes). */
 size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);

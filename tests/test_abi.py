@@ -161,3 +161,31 @@ def test_paged_binding_requires_gpu_tensors():
     t = torch.zeros(1, 4, dtype=torch.int32)
     with pytest.raises(ValueError):
         binding._prepare_paged(q, kc, kc, t, t[0, :1], None, None, True)
+
+
+def call_bwd(lib, q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, Lq=4, Lk=8,
+             D=64, causal=0, window=0, scale=0.125, kv_lens=None):
+    return lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, causal, window,
+                      ctypes.c_float(scale), kv_lens, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=None), binding.FA_ERR_INVALID_ARG),
+    (dict(dout=None), binding.FA_ERR_INVALID_ARG),
+    (dict(dq=None), binding.FA_ERR_INVALID_ARG),
+    (dict(dk=None), binding.FA_ERR_INVALID_ARG),
+    (dict(dv=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(dout=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(window=4), binding.FA_ERR_INVALID_ARG),
+    (dict(window=-1, causal=1), binding.FA_ERR_INVALID_ARG),
+    (dict(D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=3), binding.FA_ERR_INVALID_ARG),
+])
+def test_backward_validation(lib, kw, status):
+    got = call_bwd(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
