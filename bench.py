@@ -8,7 +8,8 @@ input, resident in HBM before timing starts.  The headline workload is the
 non-causal prefill B=4, Hq=Hkv=16, Lq=Lk=1024, D=64; the causal, long-context
 GQA and split-KV decode workloads, and the follow-on variants (the GQA
 workload under a causal window of 4096 keys; the decode workload served from
-a shuffled paged cache with 16-token pages), are timed the same way and
+a shuffled paged cache with 16-token pages; the backward of the causal 4K and
+1K prefill workloads, one fa_bwd call per step), are timed the same way and
 reported under "workloads".  Time is taken with HIP events on the stream the kernels are
 launched on (torch's current stream), bracketed by device synchronisation.
 
@@ -73,7 +74,14 @@ def time_workload(w, steps, warmup, dev):
     lse = torch.empty(w.B, w.Hq, w.Lq, dtype=torch.float32, device=dev)
     # Arguments are checked and marshalled once; each step is one C-ABI call,
     # so host overhead stays below the kernel time.
-    if w.page_size:
+    if w.backward:
+        k, v = inp.k.to(dev), inp.v.to(dev)
+        fwd = binding.PreparedCall(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=kl,
+                                   window=w.window if w.window else None)
+        fwd()                                   # the forward's o and lse are the backward's inputs
+        call = binding.PreparedBwdCall(q, k, v, o, lse, inp.meta["dout"].to(dev), causal=w.causal,
+                                       window=w.window, scale=w.scale, kv_lens=kl)
+    elif w.page_size:
         # Only the paged copy of K and V is resident for a paged workload.
         kc, vc, table = (t.to(dev) for t in inp.meta["paged"])
         k, v = kc, vc
@@ -97,7 +105,7 @@ def time_workload(w, steps, warmup, dev):
     nbytes = W.compulsory_bytes(w, inp.kv_lens)
     rec = {"ms_per_step": ms, "flops": flops, "bytes": nbytes,
            "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9}
-    if w.Lq == 1:
+    if w.Lq == 1 and not w.backward:
         rec.update(bound="hbm", frac=rec["gbs"] / PEAK_HBM_GBS)
     else:
         rec.update(bound="mfma", frac=rec["tflops"] / PEAK_BF16_TFLOPS)

@@ -270,3 +270,28 @@ def fa_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, *, causal=False, wi
                                  _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Lq, Lk, D,
                                  int(bool(causal)), int(window), scale, _ptr(kv_lens), s))
     return dq, dk, dv
+
+
+class PreparedBwdCall:
+    """fa_bwd with its arguments checked and marshalled once (see PreparedCall)."""
+
+    def __init__(self, q, k, v, o, lse, dout, *, causal=False, window=0, scale=None, kv_lens=None,
+                 stream=None):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal=causal, window=window, scale=scale,
+               kv_lens=kv_lens, stream=stream)               # validates; raises on a bad argument
+        D = q.shape[3]
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        self.grads = (dq, dk, dv)
+        self._keep = (q, k, v, o, lse, dout, dq, dk, dv, kv_lens)
+        self._fn = load_library().fa_bwd
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                      _ptr(dv), q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2], D,
+                      int(bool(causal)), int(window), ctypes.c_float(scale), _ptr(kv_lens), s)
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+        return self.grads

@@ -10,9 +10,14 @@
 // dK and dV.  Here each gets its own kernel, so neither needs atomics and the
 // result is deterministic:
 //
-// dq kernel: one wavefront per (batch, query head, 32 queries).  Q and G of
-// the wavefront's queries stay in registers as B operands; K and V tiles of 32
-// keys go through wavefront-private LDS.  Per tile, on v_mfma_f32_32x32x16_bf16
+// Both kernels run workgroups of four wavefronts that share 32-row tiles:
+// the workgroup streams the tiles through two LDS stages with direct HBM ->
+// LDS copies (range-checked, so rows past the valid length arrive as zeros),
+// issued one tile ahead of their use, with one barrier per tile.
+//
+// dq kernel: one workgroup per (batch, query head, 128 queries), each
+// wavefront owning 32 of them.  Q and G of a wavefront's queries stay in
+// registers as B operands; K and V tiles of 32 keys are shared.  Per tile, on v_mfma_f32_32x32x16_bf16
 // with fp32 accumulation: S^T = K Q^T and dP^T = V G^T (K and V rows fed
 // through the bit-2/3 swap, as in the forward, so that key 16*(v/8) + 8*hi +
 // (v%8) sits in accumulator entry v), P^T and dS^T elementwise with one query
@@ -21,12 +26,13 @@
 // The wavefront also forms delta_i = G_i . O_i for its queries (one dot
 // product per lane pair) and stores it for the second kernel.
 //
-// dk/dv kernel: one wavefront per (batch, KV head, 32 keys).  K and V of the
-// wavefront's keys stay in registers as B operands; it visits every query
-// tile of every query head that reads this KV head (section 9.2's grouping,
-// so the GQA sum happens in registers) and skips tiles no query of which can
-// see the block (causal, window).  Per 32-query tile, through wavefront-private
-// LDS: S = Q K^T and dP = G V^T with the query rows fed through the bit-2/3
+// dk/dv kernel: one workgroup per (batch, KV head, 128 keys), each wavefront
+// owning 32 of them.  K and V of a wavefront's keys stay in registers as B
+// operands; the workgroup visits every query tile of every query head that
+// reads this KV head (section 9.2's grouping, so the GQA sum happens in
+// registers) and skips tiles no query of which can see its keys (causal,
+// window).  Per shared 32-query tile (Q, G, and the rows' LSE and delta):
+// S = Q K^T and dP = G V^T with the query rows fed through the bit-2/3
 // swap, which makes the P and dS accumulators, rounded to bf16, exactly the A
 // operands of dV += P^T G and dK += dS^T Q; G and Q enter those as B operands
 // through the transposing LDS read.  Keys past a sequence's valid length get
@@ -45,23 +51,36 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// A 32-row tile of a [rows, D] bf16 tensor into wavefront-private LDS,
-// row-major with the K swizzle: every lane loads D/16 16-byte chunks
-// (coalesced, range-checked: rows past `valid` read as zero) and stores them.
-template <int D>
-__device__ __forceinline__ void stage_tile(bf16* tile, const bf16* src, int valid, int l) {
-    constexpr int CH = D / 8;
-    constexpr int NV = 32 * CH / 64;
-    const rsrc_t rs = make_rsrc(src, (uint32_t)(valid > 0 ? valid : 0) * D * 2);
-    bf16x8 r[NV];
+// Direct HBM -> LDS copies of a 32-row tile of a [rows, D] bf16 tensor by the
+// workgroup's NT threads into a tile buffer laid out row-major with the K
+// swizzle.  Copy i of wavefront w fills 16-byte chunk position
+// P = (w * NI + i) * 64 + lane of the buffer, so each thread reads chunk
+// (P % CH) ^ swizzle(row) of row P / CH: the fixed per-lane source offsets
+// carry the swizzle and every copy instruction writes 1 KiB of consecutive
+// LDS.  Rows past `valid` arrive as zeros and are not fetched.
+template <int D, int NT = 256>
+struct TileCopy {
+    static constexpr int CH = D / 8;
+    static constexpr int NI = 32 * CH / NT;
+    static_assert(NI >= 1 && (32 * CH) % NT == 0, "a tile must split evenly over the workgroup");
+    uint32_t off[NI];
+    __device__ __forceinline__ void init(int w, int l) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) r[i] = load16(rs, (uint32_t)(i * 64 + l) * 16);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int P = i * 64 + l;
-        const int row = P / CH;
-        *reinterpret_cast<bf16x8*>(tile + row * D + (((P % CH) ^ k_swizzle<D>(row)) * 8)) = r[i];
+        for (int i = 0; i < NI; ++i) {
+            const int P = (w * NI + i) * 64 + l;
+            const int row = P / CH;
+            off[i] = (uint32_t)(row * D + (((P % CH) ^ k_swizzle<D>(row)) * 8)) * 2;
+        }
     }
+    __device__ __forceinline__ void issue(const bf16* src, int valid, uint32_t lds_buf, int w) const {
+        const i32x4 d = make_desc(src, (uint32_t)(valid > 0 ? valid : 0) * D * 2);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) copy16_to_lds_async(d, off[i], lds_buf + (uint32_t)((w * NI + i) * 64 * 16));
+    }
+};
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
 
 // A-operand fragment: row `row` of a K-swizzled tile, 16-byte chunk `chunk`.
@@ -97,16 +116,23 @@ __device__ __forceinline__ int clamp_len(const int* kv_lens, int b, int Lk) {
 
 }  // namespace
 
+
+// Two wavefronts per SIMD: the register budget that keeps every accumulator
+// in ordinary VGPRs (no copies through the accumulation registers per tile).
 template <int D>
-__global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(BwdParams p) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(16))) bf16 kt[32 * D];
-    __shared__ __attribute__((aligned(16))) bf16 vt[32 * D];
+    constexpr int TILE = 32 * D;
+    __shared__ __attribute__((aligned(16))) bf16 kt[2 * TILE];
+    __shared__ __attribute__((aligned(16))) bf16 vt[2 * TILE];
 
-    const int l = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
     const int hi = l >> 5;
-    const int nqb = (p.Lq + 31) / 32;
+    const int nqb = (p.Lq + 127) / 128;
     const int qb = blockIdx.x % nqb;
     const int bh = blockIdx.x / nqb;           // b * Hq + h
     const int h = bh % p.Hq;
@@ -114,8 +140,8 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p) {
     const int g = h / p.r;
     const int n = clamp_len(p.kv_lens, b, p.Lk);
     const int off = n - p.Lq;                   // query i sits at key position i + off
-    const int q0 = qb * 32;
-    const int qrow = q0 + (l & 31);
+    const int qw0 = qb * 128;                   // first query of the workgroup
+    const int qrow = qw0 + 32 * w + (l & 31);
     const bool row_ok = qrow < p.Lq;
     const int qpos = qrow + off;
 
@@ -145,12 +171,22 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p) {
         if (hi == 0) p.delta[(size_t)bh * p.Lq + qrow] = delta;
     }
 
-    // Keys this block can see: [k_lo, k_hi).
+    // Keys some query of the workgroup can see: [k_lo, k_hi).
     int k_hi = n, k_lo = 0;
-    if (p.causal) k_hi = min(n, max(min(q0 + 32, p.Lq) + off, 0));
-    if (p.window > 0) k_lo = max(q0 + off - p.window + 1, 0);
+    if (p.causal) k_hi = min(n, max(min(qw0 + 128, p.Lq) + off, 0));
+    if (p.window > 0) k_lo = max(qw0 + off - p.window + 1, 0);
     const int t_lo = k_lo / 32;
-    const int t_hi = (k_hi + 31) / 32;
+    const int ntiles = max((k_hi + 31) / 32 - t_lo, 0);
+
+    TileCopy<D> cp;
+    cp.init(w, l);
+    const uint32_t lds_k = lds_address(kt), lds_v = lds_address(vt);
+    auto issue = [&](int j) __attribute__((always_inline)) {   // tile j into stage j % 2
+        const int k0 = (t_lo + j) * 32;
+        const int buf = (j & 1) * TILE * 2;
+        cp.issue(p.k + kvoff + (size_t)k0 * D, n - k0, lds_k + buf, w);
+        cp.issue(p.v + kvoff + (size_t)k0 * D, n - k0, lds_v + buf, w);
+    };
 
     const int krow = swap_bits_2_3(l & 31);
     f32x16 dq[DB];
@@ -158,34 +194,48 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p) {
     for (int db = 0; db < DB; ++db) dq[db] = zero_f32x16();
     const float c2 = p.c;
 
-    for (int t = t_lo; t < t_hi; ++t) {
-        const int k0 = t * 32;
-        // One wavefront's LDS operations run in order: the reads of the
-        // previous tile are done before these writes land.
-        stage_tile<D>(kt, p.k + kvoff + (size_t)k0 * D, n - k0, l);
-        stage_tile<D>(vt, p.v + kvoff + (size_t)k0 * D, n - k0, l);
+    if (ntiles > 0) issue(0);
+    for (int j = 0; j < ntiles; ++j) {
+        wait_all_vector_loads();                // this wavefront's copies of tile j
+        __syncthreads();                        // tile j visible; every wavefront is done with tile j - 1
+        if (j + 1 < ntiles) issue(j + 1);       // into the stage of tile j - 1
+        const int k0 = (t_lo + j) * 32;
+        const bf16* Ks = kt + (j & 1) * TILE;
+        const bf16* Vs = vt + (j & 1) * TILE;
 
         f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            s = mfma_32x32x16(read_row_chunk<D>(kt, krow, 2 * ks + hi), qf[ks], s);
-            dp = mfma_32x32x16(read_row_chunk<D>(vt, krow, 2 * ks + hi), gf[ks], dp);
+            s = mfma_32x32x16(read_row_chunk<D>(Ks, krow, 2 * ks + hi), qf[ks], s);
+            dp = mfma_32x32x16(read_row_chunk<D>(Vs, krow, 2 * ks + hi), gf[ks], dp);
+        }
+        // Elementwise masks only on tiles where some pair of this
+        // wavefront's rows and the tile is out (a wave-uniform test).
+        const int qw = qw0 + 32 * w;            // first query of this wavefront
+        const bool need = (k0 + 32 > n) || (qw + 32 > p.Lq) ||
+                          (p.causal && k0 + 31 > qw + off) ||
+                          (p.window > 0 && qw + 31 + off - k0 >= p.window);
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(s[v], c2, -lse2);
+        if (need) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = k0 + 16 * (v >> 3) + 8 * hi + (v & 7);
+                const bool ok = row_ok & (key < n) & (!p.causal | (key <= qpos)) &
+                                ((p.window == 0) | (qpos - key < p.window));
+                x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+            }
         }
         float ds[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int key = k0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-            const bool ok = row_ok & (key < n) & (!p.causal | (key <= qpos)) &
-                            ((p.window == 0) | (qpos - key < p.window));
-            const float pr = ok ? exp2_fast(__builtin_fmaf(s[v], c2, -lse2)) : 0.0f;
-            ds[v] = pr * (dp[v] - delta);
-        }
+        for (int v = 0; v < 16; ++v) ds[v] = exp2_fast(x[v]) * (dp[v] - delta);
         const bf16x8 dsb0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
         const bf16x8 dsb1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            dq[db] = mfma_32x32x16(read_transposed<D>(kt, 0, db * 32, l), dsb0, dq[db]);
-            dq[db] = mfma_32x32x16(read_transposed<D>(kt, 16, db * 32, l), dsb1, dq[db]);
+            dq[db] = mfma_32x32x16(read_transposed<D>(Ks, 0, db * 32, l), dsb0, dq[db]);
+            dq[db] = mfma_32x32x16(read_transposed<D>(Ks, 16, db * 32, l), dsb1, dq[db]);
         }
     }
 
@@ -203,104 +253,205 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p) {
     }
 }
 
+// D = 64: four wavefronts, each accumulating both dK and dV of its 32 keys
+// (two wavefronts per SIMD fit with every accumulator in ordinary VGPRs).
+// D = 128: dK and dV of 32 keys alone would take 128 registers, so the work
+// is split by role: eight wavefronts, wavefront w owning key block w % 4 --
+// w < 4 accumulates dV (products S and P^T G), w >= 4 accumulates dK
+// (products S, dP and dS^T Q), both from the same shared tiles.  Waves w and
+// w + 4 share a SIMD; S is formed twice per key block (40 products per tile
+// instead of 32) in exchange for no register spilling and two wavefronts per
+// SIMD.
 template <int D>
-__global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdParams p) {
+struct DkdvShape {
+    static constexpr bool SPLIT = D == 128;
+    static constexpr int NT = SPLIT ? 512 : 256;
+};
+
+template <int D>
+__global__ void __launch_bounds__(DkdvShape<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_kernel(BwdParams p) {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(16))) bf16 qt[32 * D];
-    __shared__ __attribute__((aligned(16))) bf16 gt[32 * D];
-    __shared__ __attribute__((aligned(16))) float stat[64];   // L2 and delta of the tile's 32 queries
+    constexpr int TILE = 32 * D;
+    constexpr bool SPLIT = DkdvShape<D>::SPLIT;
+    constexpr int NT = DkdvShape<D>::NT;
+    __shared__ __attribute__((aligned(16))) bf16 qt[2 * TILE];
+    __shared__ __attribute__((aligned(16))) bf16 gt[2 * TILE];
+    __shared__ __attribute__((aligned(16))) float stat[2 * 64];   // per stage: L2 [0, 32), delta [32, 64)
+    __shared__ __attribute__((aligned(16))) bf16 kvres[4 * 2 * TILE];  // K and V of the four key blocks
 
-    const int l = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
     const int hi = l >> 5;
-    const int nkb = (p.Lk + 31) / 32;
+    const int kblk = w & 3;                     // this wavefront's 32-key block
+    const bool do_dv = !SPLIT || w < 4;
+    const bool do_dk = !SPLIT || w >= 4;
+    const int nkb = (p.Lk + 127) / 128;
     const int kb = blockIdx.x % nkb;
     const int bg = blockIdx.x / nkb;           // b * Hkv + g
     const int g = bg % p.Hkv;
     const int b = bg / p.Hkv;
     const int n = clamp_len(p.kv_lens, b, p.Lk);
     const int off = n - p.Lq;
-    const int k0 = kb * 32;
+    const int kw0 = kb * 128;                   // first key of the workgroup
+    const int k0 = kw0 + 32 * kblk;             // first key of this wavefront
     const int key = k0 + (l & 31);              // this lane's key (accumulator column of S, dP)
-
     const size_t kvoff = (size_t)bg * p.Lk * D;
-    f32x16 dk[DB], dv[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) { dk[db] = zero_f32x16(); dv[db] = zero_f32x16(); }
 
-    if (k0 < n) {
-        // K and V of this lane's key as B operands (rows past n read as zero).
+    f32x16 acc[DB], acc2[SPLIT ? 1 : DB];       // dV (or dK for w >= 4 when split); dK when not split
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
+#pragma unroll
+    for (int db = 0; db < (SPLIT ? 1 : DB); ++db) acc2[db] = zero_f32x16();
+
+    // K and V of each key block (keys past n read as zero) in LDS, read as B
+    // operands: lane l takes row l % 32, chunk 2 ks + hi.
+    bf16* Kw = kvres + kblk * 2 * TILE;
+    bf16* Vw = Kw + TILE;
+    {
+        const bool load_k = !SPLIT || w < 4, load_v = !SPLIT || w >= 4;
         const rsrc_t kbuf = make_rsrc(p.k + kvoff, (uint32_t)n * D * 2);
         const rsrc_t vbuf = make_rsrc(p.v + kvoff, (uint32_t)n * D * 2);
-        bf16x8 kf[KS], vf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const uint32_t at = (uint32_t)(key * D + ks * 16 + hi * 8) * 2;
-            kf[ks] = load16(kbuf, at);
-            vf[ks] = load16(vbuf, at);
+            const int row = l & 31, chunk = 2 * ks + hi;
+            const int slot = row * D + ((chunk ^ k_swizzle<D>(row)) * 8);
+            if (load_k) *reinterpret_cast<bf16x8*>(Kw + slot) = load16(kbuf, at);
+            if (load_v) *reinterpret_cast<bf16x8*>(Vw + slot) = load16(vbuf, at);
         }
-        // Queries that can see some key of [k0, k0 + 32): position >= k0
-        // (causal) and position < k0 + 31 + window (window).
-        int i_lo = 0, i_hi = p.Lq;
-        if (p.causal) i_lo = max(k0 - off, 0);
-        if (p.window > 0) i_hi = min(p.Lq, max(k0 + 31 + p.window - off, 0));
-        const int qrow = swap_bits_2_3(l & 31);   // A-operand row of this lane
-        const float c2 = p.c;
+    }
 
-        for (int hh = 0; hh < p.r; ++hh) {
-            const int h = g * p.r + hh;
-            const size_t bh = (size_t)b * p.Hq + h;
-            const size_t qoff = bh * p.Lq * D;
-            for (int q0 = (i_lo / 32) * 32; q0 < i_hi; q0 += 32) {
-                stage_tile<D>(qt, p.q + qoff + (size_t)q0 * D, p.Lq - q0, l);
-                stage_tile<D>(gt, p.dout + qoff + (size_t)q0 * D, p.Lq - q0, l);
+    // Query tiles in which some query can see a key of the workgroup:
+    // position >= kw0 (causal), position < kw0 + 127 + window (window); as one
+    // flat sequence f = hh * nqt + j over the query heads of this KV head.
+    int i_lo = 0, i_hi = p.Lq;
+    if (p.causal) i_lo = max(kw0 - off, 0);
+    if (p.window > 0) i_hi = min(p.Lq, max(kw0 + 127 + p.window - off, 0));
+    const int q_first = (i_lo / 32) * 32;
+    const int nqt = (kw0 < n && i_hi > q_first) ? (i_hi - q_first + 31) / 32 : 0;
+    const int total = p.r * nqt;
+
+    TileCopy<D, NT> cp;
+    cp.init(w, l);
+    const uint32_t lds_q = lds_address(qt), lds_g = lds_address(gt);
+    float st_next = 0.0f;                       // wavefront 0: L2 (lanes < 32) or delta of a query
+    auto issue = [&](int f) __attribute__((always_inline)) {   // tile f into stage f % 2
+        const int hh = f / nqt;
+        const int q0 = q_first + (f - hh * nqt) * 32;
+        const size_t bh = (size_t)b * p.Hq + g * p.r + hh;
+        const size_t at = (bh * p.Lq + (size_t)q0) * D;
+        const int buf = (f & 1) * TILE * 2;
+        cp.issue(p.q + at, p.Lq - q0, lds_q + buf, w);
+        cp.issue(p.dout + at, p.Lq - q0, lds_g + buf, w);
+        if (w == 0) {
+            const int i = q0 + (l & 31);
+            float val = 0.0f;
+            if (i < p.Lq) {
                 if (l < 32) {
-                    const int i = q0 + l;
-                    float L2 = 0.0f, dl = 0.0f;
-                    if (i < p.Lq) {
-                        const float L = p.lse[bh * p.Lq + i];
-                        L2 = L == kNegInf ? 0.0f : L * kLog2e;
-                        dl = p.delta[bh * p.Lq + i];
-                    }
-                    stat[l] = L2;
-                    stat[32 + l] = dl;
+                    const float L = p.lse[bh * p.Lq + i];
+                    val = L == kNegInf ? 0.0f : L * kLog2e;
+                } else {
+                    val = p.delta[bh * p.Lq + i];
                 }
+            }
+            st_next = val;
+        }
+    };
 
-                f32x16 s = zero_f32x16(), dp = zero_f32x16();
+    const int qrow = swap_bits_2_3(l & 31);   // A-operand row of this lane
+    const float c2 = p.c;
+    if (total > 0) issue(0);
+    for (int f = 0; f < total; ++f) {
+        wait_all_vector_loads();                // this wavefront's copies of tile f
+        if (w == 0) stat[(f & 1) * 64 + l] = st_next;
+        __syncthreads();                        // tile f visible; every wavefront is done with tile f - 1
+        if (f + 1 < total) issue(f + 1);        // into the stage of tile f - 1
+        if (k0 >= n) continue;                  // this wavefront's keys are all past n
+        const int hh = f / nqt;
+        const int q0 = q_first + (f - hh * nqt) * 32;
+        const bf16* Qs = qt + (f & 1) * TILE;
+        const bf16* Gs = gt + (f & 1) * TILE;
+        const float* St = stat + (f & 1) * 64;
+
+        f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    s = mfma_32x32x16(read_row_chunk<D>(qt, qrow, 2 * ks + hi), kf[ks], s);
-                    dp = mfma_32x32x16(read_row_chunk<D>(gt, qrow, 2 * ks + hi), vf[ks], dp);
-                }
-                // Entry v of this lane holds query q0 + 16*(v/8) + 8*hi + (v%8).
-                float pr[16], ds[16];
+        for (int ks = 0; ks < KS; ++ks) {
+            s = mfma_32x32x16(read_row_chunk<D>(Qs, qrow, 2 * ks + hi),
+                              read_row_chunk<D>(Kw, l & 31, 2 * ks + hi), s);
+            if (do_dk)
+                dp = mfma_32x32x16(read_row_chunk<D>(Gs, qrow, 2 * ks + hi),
+                                   read_row_chunk<D>(Vw, l & 31, 2 * ks + hi), dp);
+        }
+        // Entry v of this lane holds query q0 + 16*(v/8) + 8*hi + (v%8): its
+        // L2 and delta are St[8 hi + (v%8) (+16 for v >= 8)] and St[32 + ...].
+        float x[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int qi = 16 * (v >> 3) + 8 * hi + (v & 7);
-                    const int i = q0 + qi;
-                    const int qpos = i + off;
-                    const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
-                                    ((p.window == 0) | (qpos - key < p.window));
-                    pr[v] = ok ? exp2_fast(__builtin_fmaf(s[v], c2, -stat[qi])) : 0.0f;
-                    ds[v] = pr[v] * (dp[v] - stat[32 + qi]);
-                }
-                const bf16x8 pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
-                const bf16x8 pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
-                const bf16x8 db0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-                const bf16x8 db1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dv[db] = mfma_32x32x16(pb0, read_transposed<D>(gt, 0, db * 32, l), dv[db]);
-                    dv[db] = mfma_32x32x16(pb1, read_transposed<D>(gt, 16, db * 32, l), dv[db]);
-                    dk[db] = mfma_32x32x16(db0, read_transposed<D>(qt, 0, db * 32, l), dk[db]);
-                    dk[db] = mfma_32x32x16(db1, read_transposed<D>(qt, 16, db * 32, l), dk[db]);
+            for (int qd = 0; qd < 2; ++qd) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 8 * half + 4 * qd + e;
+                    x[v] = __builtin_fmaf(s[v], c2, -a[e]);
                 }
+            }
+        // Elementwise masks only on tiles where some pair is out (wave-uniform).
+        const bool need = (q0 + 32 > p.Lq) || (k0 + 32 > n) || (p.causal && k0 + 31 > q0 + off) ||
+                          (p.window > 0 && q0 + 31 + off - k0 >= p.window);
+        if (need) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
+                const int qpos = i + off;
+                const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
+                                ((p.window == 0) | (qpos - key < p.window));
+                x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+            }
+        }
+        float pr[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(x[v]);
+        if (do_dv) {
+            const bf16x8 pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+            const bf16x8 pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc[db] = mfma_32x32x16(pb0, read_transposed<D>(Gs, 0, db * 32, l), acc[db]);
+                acc[db] = mfma_32x32x16(pb1, read_transposed<D>(Gs, 16, db * 32, l), acc[db]);
+            }
+        }
+        if (do_dk) {
+            float ds[16];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int qd = 0; qd < 2; ++qd) {
+                    const f32x4 d = *reinterpret_cast<const f32x4*>(St + 32 + 16 * half + 8 * hi + 4 * qd);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 8 * half + 4 * qd + e;
+                        ds[v] = pr[v] * (dp[v] - d[e]);
+                    }
+                }
+            const bf16x8 db0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            const bf16x8 db1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+            f32x16* dk = SPLIT ? acc : acc2;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dk[db] = mfma_32x32x16(db0, read_transposed<D>(Qs, 0, db * 32, l), dk[db]);
+                dk[db] = mfma_32x32x16(db1, read_transposed<D>(Qs, 16, db * 32, l), dk[db]);
             }
         }
     }
 
     // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
     // 32*db + (l % 32).  Keys past n hold zeros.
+    const f32x16* dvacc = acc;
+    const f32x16* dkacc = SPLIT ? acc : acc2;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int kr = k0 + 8 * (v >> 2) + 4 * hi + (v & 3);
@@ -309,22 +460,22 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdParams p) {
             bf16* dvp = p.dv + kvoff + (size_t)kr * D + (l & 31);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                dkp[db * 32] = (bf16)(dk[db][v] * p.scale);
-                dvp[db * 32] = (bf16)dv[db][v];
+                if (do_dk) dkp[db * 32] = (bf16)(dkacc[db][v] * p.scale);
+                if (do_dv) dvp[db * 32] = (bf16)dvacc[db][v];
             }
         }
     }
 }
 
 hipError_t launch_backward(int D, const BwdParams& p, hipStream_t stream) {
-    const long long nq = (long long)p.B * p.Hq * ((p.Lq + 31) / 32);
-    const long long nk = (long long)p.B * p.Hkv * ((p.Lk + 31) / 32);
+    const long long nq = (long long)p.B * p.Hq * ((p.Lq + 127) / 128);
+    const long long nk = (long long)p.B * p.Hkv * ((p.Lk + 127) / 128);
     if (D == 64) {
-        hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3((unsigned)nq), dim3(64), 0, stream, p);
-        if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3((unsigned)nk), dim3(64), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3((unsigned)nq), dim3(256), 0, stream, p);
+        if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3((unsigned)nk), dim3(DkdvShape<64>::NT), 0, stream, p);
     } else {
-        hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3((unsigned)nq), dim3(64), 0, stream, p);
-        if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3((unsigned)nk), dim3(64), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3((unsigned)nq), dim3(256), 0, stream, p);
+        if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3((unsigned)nk), dim3(DkdvShape<128>::NT), 0, stream, p);
     }
     return hipGetLastError();
 }

@@ -55,6 +55,7 @@ class Workload:
     description: str = ""
     window: int = 0             # causal window width (0 = none)
     page_size: int = 0          # > 0: K and V are served from a paged cache
+    backward: bool = False      # time the backward (fa_bwd) instead of the forward
 
     @property
     def seed(self) -> int:
@@ -85,6 +86,10 @@ WORKLOADS = [
     Workload("decode_paged16_b64_hq32_hkv8_d128_ragged", 64, 32, 8, 1, 8192, 128, False, 4,
              ragged=(512, 8192), page_size=16,
              description="split-KV decode from a paged cache (16-token pages, shuffled)"),
+    Workload("bwd_causal_b2_h16_l4096_d128", 2, 16, 16, 4096, 4096, 128, True, 2, backward=True,
+             description="backward of the causal prefill forward"),
+    Workload("bwd_prefill_b4_h16_l1024_d64", 4, 16, 16, 1024, 1024, 64, False, 1, backward=True,
+             description="backward of the prefill forward, no mask"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -113,6 +118,10 @@ def make_inputs(w: Workload) -> Inputs:
         lo, hi = w.ragged
         kv_lens = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
     meta = {"workload": w.name, "seed": w.seed}
+    if w.backward:
+        # The upstream gradient dL/dO, drawn after the forward's inputs.
+        meta["dout"] = torch.randn(w.B, w.Hq, w.Lq, w.D, generator=g,
+                                   dtype=torch.float32).to(torch.bfloat16)
     if w.window:
         meta["window"] = w.window
     if w.page_size:
@@ -213,10 +222,12 @@ def allowed_pairs(Lq: int, n: int, causal: bool, window: int = 0) -> int:
 
 
 def algorithmic_flops(w, kv_lens=None) -> int:
-    """4 * D FLOPs per allowed pair: two matrix products with multiply and add
-    counted separately (FlashAttention from Scratch, §11.1 counts 4MNd per tile)."""
+    """4 * D FLOPs per allowed pair for the forward: two matrix products with
+    multiply and add counted separately (FlashAttention from Scratch, §11.1
+    counts 4MNd per tile); 10 * D for the backward's five products (§8)."""
     ns = valid_lengths(w, kv_lens)
-    return sum(4 * w.D * allowed_pairs(w.Lq, n, w.causal, w.window) * w.Hq for n in ns)
+    per_pair = 10 * w.D if w.backward else 4 * w.D
+    return sum(per_pair * allowed_pairs(w.Lq, n, w.causal, w.window) * w.Hq for n in ns)
 
 
 def compulsory_bytes(w, kv_lens=None) -> int:
@@ -229,6 +240,9 @@ def compulsory_bytes(w, kv_lens=None) -> int:
     seen = [min(n, w.window + w.Lq - 1) if w.window > 0 else n for n in ns]
     kv = sum(2 * w.Hkv * m * w.D * 2 for m in seen)
     table = sum(4 * -(-n // w.page_size) for n in ns) if w.page_size > 0 else 0
+    if w.backward:
+        # Reads Q, O, dO and the LSE, K and V; writes dQ, dK and dV.
+        return 2 * qo + lse + 2 * kv
     return qo + lse + kv + table
 
 
