@@ -10,10 +10,19 @@
 // dK and dV.  Here each gets its own kernel, so neither needs atomics and the
 // result is deterministic:
 //
-// Both kernels run workgroups of four wavefronts that share 32-row tiles:
-// the workgroup streams the tiles through two LDS stages with direct HBM ->
-// LDS copies (range-checked, so rows past the valid length arrive as zeros),
+// Both kernels run workgroups whose wavefronts share 32-row tiles: the
+// workgroup streams the tiles through two LDS stages with direct HBM -> LDS
+// copies (range-checked, so rows past the valid length arrive as zeros),
 // issued one tile ahead of their use, with one barrier per tile.
+//
+// Launch order (FlashAttention-4 summary, "LPT scheduling for imbalanced
+// grids"): under a causal mask the last query blocks see the most keys and
+// the first key blocks are seen by the most queries, so each kernel numbers
+// its workgroups block-major with the longest blocks first, and a workgroup
+// that starts late is a short one.  Dispatch deals workgroups to the eight
+// XCDs round-robin; the numbering keeps all blocks of one (batch, head) on
+// one XCD when the head count is a multiple of eight, so the tiles that its
+// blocks re-read are shared in that XCD's L2.
 //
 // dq kernel: one workgroup per (batch, query head, 128 queries), each
 // wavefront owning 32 of them.  Q and G of a wavefront's queries stay in
@@ -27,8 +36,8 @@
 // product per lane pair) and stores it for the second kernel.
 //
 // dk/dv kernel: one workgroup per (batch, KV head, 128 keys), each wavefront
-// owning 32 of them.  K and V of a wavefront's keys stay in registers as B
-// operands; the workgroup visits every query tile of every query head that
+// working on 32 of them.  K and V of the workgroup's keys stay in LDS and
+// enter S and dP as B operands; the workgroup visits every query tile of every query head that
 // reads this KV head (section 9.2's grouping, so the GQA sum happens in
 // registers) and skips tiles no query of which can see its keys (causal,
 // window).  Per shared 32-query tile (Q, G, and the rows' LSE and delta):
@@ -78,6 +87,15 @@ struct TileCopy {
         for (int i = 0; i < NI; ++i) copy16_to_lds_async(d, off[i], lds_buf + (uint32_t)((w * NI + i) * 64 * 16));
     }
 };
+
+template <int N>
+struct Tag { static constexpr int value = N; };
+
+// Products per pipeline step are issued AHEAD steps after their operands'
+// LDS reads, with a scheduling fence after every step so the compiler keeps
+// that distance (otherwise it places each read right before its product and
+// waits for it there).
+constexpr int kAhead = 4;
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
@@ -133,8 +151,17 @@ bwd_dq_kernel(BwdParams p) {
     const int l = tid & 63;
     const int hi = l >> 5;
     const int nqb = (p.Lq + 127) / 128;
-    const int qb = blockIdx.x % nqb;
-    const int bh = blockIdx.x / nqb;           // b * Hq + h
+    const int nbh = p.B * p.Hq;
+    int rank, bh;                               // bh = b * Hq + h
+    if ((nbh & 7) == 0) {                       // XCD x gets heads [x nbh / 8, (x + 1) nbh / 8)
+        const int per = nbh >> 3, slot = blockIdx.x >> 3;
+        rank = slot / per;
+        bh = (blockIdx.x & 7) * per + (slot - rank * per);
+    } else {
+        rank = blockIdx.x / nbh;
+        bh = blockIdx.x - rank * nbh;
+    }
+    const int qb = nqb - 1 - rank;              // last query blocks first
     const int h = bh % p.Hq;
     const int b = bh / p.Hq;
     const int g = h / p.r;
@@ -203,12 +230,30 @@ bwd_dq_kernel(BwdParams p) {
         const bf16* Ks = kt + (j & 1) * TILE;
         const bf16* Vs = vt + (j & 1) * TILE;
 
+        // S^T (even steps) and dP^T (odd steps), pipelined over their K and V
+        // fragments.
+        constexpr int NOP = 2 * KS;
+        bf16x8 fr[NOP];
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            fr[i] = read_row_chunk<D>((i & 1) ? Vs : Ks, krow, 2 * (i / 2) + hi);
+        };
         f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = mfma_32x32x16(read_row_chunk<D>(Ks, krow, 2 * ks + hi), qf[ks], s);
-            dp = mfma_32x32x16(read_row_chunk<D>(Vs, krow, 2 * ks + hi), gf[ks], dp);
+        for (int i = 0; i < kAhead; ++i) rd(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NOP; ++i) {
+            if (i & 1) dp = mfma_32x32x16(fr[i], gf[i / 2], dp);
+            else       s = mfma_32x32x16(fr[i], qf[i / 2], s);
+            if (i + kAhead < NOP) rd(i + kAhead);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // K^T fragments of the dQ product, read now so that the elementwise
+        // step below covers their latency.
+        bf16x8 kT[2 * DB];
+#pragma unroll
+        for (int f = 0; f < 2 * DB; ++f) kT[f] = read_transposed<D>(Ks, 16 * (f & 1), 32 * (f >> 1), l);
+        __builtin_amdgcn_sched_barrier(0);
         // Elementwise masks only on tiles where some pair of this
         // wavefront's rows and the tile is out (a wave-uniform test).
         const int qw = qw0 + 32 * w;            // first query of this wavefront
@@ -234,8 +279,8 @@ bwd_dq_kernel(BwdParams p) {
         const bf16x8 dsb1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            dq[db] = mfma_32x32x16(read_transposed<D>(Ks, 0, db * 32, l), dsb0, dq[db]);
-            dq[db] = mfma_32x32x16(read_transposed<D>(Ks, 16, db * 32, l), dsb1, dq[db]);
+            dq[db] = mfma_32x32x16(kT[2 * db], dsb0, dq[db]);
+            dq[db] = mfma_32x32x16(kT[2 * db + 1], dsb1, dq[db]);
         }
     }
 
@@ -288,9 +333,9 @@ bwd_dkdv_kernel(BwdParams p) {
     const int kblk = w & 3;                     // this wavefront's 32-key block
     const bool do_dv = !SPLIT || w < 4;
     const bool do_dk = !SPLIT || w >= 4;
-    const int nkb = (p.Lk + 127) / 128;
-    const int kb = blockIdx.x % nkb;
-    const int bg = blockIdx.x / nkb;           // b * Hkv + g
+    const int nbg = p.B * p.Hkv;
+    const int kb = blockIdx.x / nbg;            // first key blocks first
+    const int bg = blockIdx.x - kb * nbg;       // b * Hkv + g; on XCD bg % 8 when nbg % 8 == 0
     const int g = bg % p.Hkv;
     const int b = bg / p.Hkv;
     const int n = clamp_len(p.kv_lens, b, p.Lk);
@@ -376,76 +421,107 @@ bwd_dkdv_kernel(BwdParams p) {
         const bf16* Gs = gt + (f & 1) * TILE;
         const float* St = stat + (f & 1) * 64;
 
-        f32x16 s = zero_f32x16(), dp = zero_f32x16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = mfma_32x32x16(read_row_chunk<D>(Qs, qrow, 2 * ks + hi),
-                              read_row_chunk<D>(Kw, l & 31, 2 * ks + hi), s);
-            if (do_dk)
-                dp = mfma_32x32x16(read_row_chunk<D>(Gs, qrow, 2 * ks + hi),
-                                   read_row_chunk<D>(Vw, l & 31, 2 * ks + hi), dp);
-        }
-        // Entry v of this lane holds query q0 + 16*(v/8) + 8*hi + (v%8): its
-        // L2 and delta are St[8 hi + (v%8) (+16 for v >= 8)] and St[32 + ...].
-        float x[16];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int qd = 0; qd < 2; ++qd) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = 8 * half + 4 * qd + e;
-                    x[v] = __builtin_fmaf(s[v], c2, -a[e]);
-                }
-            }
         // Elementwise masks only on tiles where some pair is out (wave-uniform).
         const bool need = (q0 + 32 > p.Lq) || (k0 + 32 > n) || (p.causal && k0 + 31 > q0 + off) ||
                           (p.window > 0 && q0 + 31 + off - k0 >= p.window);
-        if (need) {
+        // One tile for one role: S (and dP for dK), the elementwise step, then
+        // the dV and/or dK products.  WITH_DK: also dP, dS and dK += dS^T Q;
+        // WITH_DV: dV += P^T G.  Each role is its own straight-line code.
+        auto tile = [&](auto with_dk, auto with_dv) __attribute__((always_inline)) {
+            constexpr bool WDK = decltype(with_dk)::value != 0;
+            constexpr bool WDV = decltype(with_dv)::value != 0;
+            // S (even steps) and dP (odd steps when WDK), two fragments each.
+            constexpr int NOP = WDK ? 2 * KS : KS;
+            bf16x8 fa[NOP], fb[NOP];
+            auto rd = [&](int i) __attribute__((always_inline)) {
+                const bool is_dp = WDK && (i & 1);
+                const int ks = WDK ? i / 2 : i;
+                fa[i] = read_row_chunk<D>(is_dp ? Gs : Qs, qrow, 2 * ks + hi);
+                fb[i] = read_row_chunk<D>(is_dp ? Vw : Kw, l & 31, 2 * ks + hi);
+            };
+            f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                const int qpos = i + off;
-                const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
-                                ((p.window == 0) | (qpos - key < p.window));
-                x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+            for (int i = 0; i < kAhead; ++i) rd(i);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NOP; ++i) {
+                if (WDK && (i & 1)) dp = mfma_32x32x16(fa[i], fb[i], dp);
+                else                s = mfma_32x32x16(fa[i], fb[i], s);
+                if (i + kAhead < NOP) rd(i + kAhead);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        float pr[16];
+            // Transposed G (dV) and Q (dK) fragments, read now so that the
+            // elementwise step covers their latency.
+            bf16x8 gT[WDV ? 2 * DB : 1], qT[WDK ? 2 * DB : 1];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(x[v]);
-        if (do_dv) {
-            const bf16x8 pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
-            const bf16x8 pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                acc[db] = mfma_32x32x16(pb0, read_transposed<D>(Gs, 0, db * 32, l), acc[db]);
-                acc[db] = mfma_32x32x16(pb1, read_transposed<D>(Gs, 16, db * 32, l), acc[db]);
+            for (int f = 0; f < 2 * DB; ++f) {
+                if (WDV) gT[f] = read_transposed<D>(Gs, 16 * (f & 1), 32 * (f >> 1), l);
+                if (WDK) qT[f] = read_transposed<D>(Qs, 16 * (f & 1), 32 * (f >> 1), l);
             }
-        }
-        if (do_dk) {
-            float ds[16];
+            __builtin_amdgcn_sched_barrier(0);
+            // Entry v of this lane holds query q0 + 16*(v/8) + 8*hi + (v%8):
+            // its L2 and delta are St[8 hi + (v%8) (+16 for v >= 8)] and
+            // St[32 + ...].
+            float x[16];
 #pragma unroll
             for (int half = 0; half < 2; ++half)
 #pragma unroll
                 for (int qd = 0; qd < 2; ++qd) {
-                    const f32x4 d = *reinterpret_cast<const f32x4*>(St + 32 + 16 * half + 8 * hi + 4 * qd);
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int v = 8 * half + 4 * qd + e;
-                        ds[v] = pr[v] * (dp[v] - d[e]);
+                        x[v] = __builtin_fmaf(s[v], c2, -a[e]);
                     }
                 }
-            const bf16x8 db0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-            const bf16x8 db1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-            f32x16* dk = SPLIT ? acc : acc2;
+            if (need) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dk[db] = mfma_32x32x16(db0, read_transposed<D>(Qs, 0, db * 32, l), dk[db]);
-                dk[db] = mfma_32x32x16(db1, read_transposed<D>(Qs, 16, db * 32, l), dk[db]);
+                for (int v = 0; v < 16; ++v) {
+                    const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
+                    const int qpos = i + off;
+                    const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
+                                    ((p.window == 0) | (qpos - key < p.window));
+                    x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+                }
             }
-        }
+            float pr[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(x[v]);
+            if (WDV) {
+                const bf16x8 pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+                const bf16x8 pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    acc[db] = mfma_32x32x16(pb0, gT[2 * db], acc[db]);
+                    acc[db] = mfma_32x32x16(pb1, gT[2 * db + 1], acc[db]);
+                }
+            }
+            if (WDK) {
+                float ds[16];
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int qd = 0; qd < 2; ++qd) {
+                        const f32x4 d = *reinterpret_cast<const f32x4*>(St + 32 + 16 * half + 8 * hi + 4 * qd);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int v = 8 * half + 4 * qd + e;
+                            ds[v] = pr[v] * (dp[v] - d[e]);
+                        }
+                    }
+                const bf16x8 db0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+                const bf16x8 db1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+                f32x16* dk = SPLIT ? acc : acc2;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dk[db] = mfma_32x32x16(db0, qT[2 * db], dk[db]);
+                    dk[db] = mfma_32x32x16(db1, qT[2 * db + 1], dk[db]);
+                }
+            }
+        };
+        if (!SPLIT) tile(Tag<1>{}, Tag<1>{});
+        else if (w >= 4) tile(Tag<1>{}, Tag<0>{});
+        else tile(Tag<0>{}, Tag<1>{});
     }
 
     // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
