@@ -24,6 +24,10 @@ backward.dense_backward_head / attention_backward
 paged.paged_attention_forward / gather_sequence
     Attention against a paged KV cache: the logical rows are gathered through
     the page table, then evaluated by the dense definition.
+fp8.round_e4m3 / quantize_rows / fp8_attention_forward
+    E4M3 rounding, block quantization with power-of-two scales, incoherent
+    processing (Hadamard with random signs), and the attention of the
+    quantized Q and K by the dense definition.
 
 Every function cites the passage of the pages it follows.  All of them are
 pinned by ``tests/test_oracle.py`` to values the pages print, closed forms,
@@ -34,10 +38,11 @@ from .streaming import streaming_head
 from .merge import partition_state, merge_states, finish_state, merge_normalized
 from .paged import gather_sequence, paged_attention_forward
 from .backward import dense_backward_head, attention_backward
+from . import fp8
 
 __all__ = [
     "as_f64", "dense_head", "attention_forward", "attention_rows",
     "streaming_head", "partition_state", "merge_states", "finish_state",
     "merge_normalized", "gather_sequence", "paged_attention_forward",
-    "dense_backward_head", "attention_backward",
+    "dense_backward_head", "attention_backward", "fp8",
 ]

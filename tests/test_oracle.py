@@ -55,7 +55,7 @@ def oracle_namespace(mutations=()):
     """Load fresh copies of the oracle modules, optionally with textual
     mutations (module, old, new) applied, and expose their functions."""
     mods = {}
-    for name in ("attention", "streaming", "merge", "paged", "backward"):
+    for name in ("attention", "streaming", "merge", "paged", "backward", "fp8"):
         path = os.path.join(ORACLE_DIR, name + ".py")
         with open(path) as f:
             src = f.read()
@@ -76,10 +76,15 @@ def oracle_namespace(mutations=()):
             assert imp in src
             src = src.replace(imp, "")
             mod.as_f64 = mods["attention"].as_f64
+        if name == "fp8":
+            imp = "from .attention import as_f64, attention_forward\n"
+            assert imp in src
+            src = src.replace(imp, "")
+            mod.as_f64, mod.attention_forward = mods["attention"].as_f64, mods["attention"].attention_forward
         exec(compile(src, path, "exec"), mod.__dict__)
         mods[name] = mod
-    a, s, m, pg, bw = (mods["attention"], mods["streaming"], mods["merge"], mods["paged"],
-                       mods["backward"])
+    a, s, m, pg, bw, f8 = (mods["attention"], mods["streaming"], mods["merge"], mods["paged"],
+                           mods["backward"], mods["fp8"])
     return types.SimpleNamespace(
         dense_head=a.dense_head, attention_forward=a.attention_forward,
         attention_rows=a.attention_rows, streaming_head=s.streaming_head,
@@ -87,7 +92,8 @@ def oracle_namespace(mutations=()):
         finish_state=m.finish_state, merge_normalized=m.merge_normalized,
         gather_sequence=pg.gather_sequence,
         paged_attention_forward=pg.paged_attention_forward,
-        dense_backward_head=bw.dense_backward_head, attention_backward=bw.attention_backward)
+        dense_backward_head=bw.dense_backward_head, attention_backward=bw.attention_backward,
+        fp8=f8)
 
 
 def row_inputs(scores, values):
@@ -694,6 +700,128 @@ def check_backward_gqa_and_lengths(orc):
     close(dv3[:, :, :4], dv4, 1e-15)
 
 
+def _bf16(x):
+    return torch.tensor(np.asarray(x), dtype=torch.float32).to(torch.bfloat16).double().numpy()
+
+
+def check_fp8_format(orc):
+    # OCP E4M3 facts (FP8 formats for deep learning, OCP 8-bit floating point
+    # specification): 0x7E = 448 is the largest finite value, 0x7F / 0xFF are
+    # NaN, 0x08 = 2^-6 the smallest normal, 0x01 = 2^-9 the smallest
+    # subnormal, 0x38 = 1, 0x80 = -0.
+    f = orc.fp8
+    assert f.e4m3_value(0x7E) == 448.0 and f.e4m3_value(0xFE) == -448.0
+    assert np.isnan(f.e4m3_value(0x7F)) and np.isnan(f.e4m3_value(0xFF))
+    assert f.e4m3_value(0x08) == 2.0 ** -6 and f.e4m3_value(0x01) == 2.0 ** -9
+    assert f.e4m3_value(0x38) == 1.0 and f.e4m3_value(0x30) == 0.5 and f.e4m3_value(0x3C) == 1.5
+    assert f.e4m3_value(0x80) == 0.0 and np.signbit(f.e4m3_value(0x80))
+    table = np.array([f.e4m3_value(c) for c in range(256)])
+    finite = ~np.isnan(table)
+    assert finite.sum() == 254 and len(set(table[finite])) == 253    # +-0 share a value
+    # Rounding against brute force: the nearest finite value, a tie going to
+    # the even code; exact values map to themselves; the sign of a zero result
+    # follows x.
+    rng = np.random.default_rng(31)
+    pos = np.sort(table[finite & (table >= 0)])
+    mids = (pos[1:] + pos[:-1]) / 2
+    xs = np.concatenate([rng.uniform(-448, 448, 3000), rng.standard_normal(3000) * 2.0 ** rng.integers(-12, 6, 3000),
+                         mids, -mids, pos, -pos, [2.0 ** -11, -2.0 ** -11, 0.0]])
+    xs = np.clip(xs, -448, 448)
+    vals, codes = f.round_e4m3(xs)
+    for x, val, c in zip(xs, vals, codes):
+        d = np.abs(table - x)
+        d[~finite] = np.inf
+        best = d.min()
+        assert abs(val - x) == best and table[c] == val, (x, val, c)
+        tied = [cc for cc in range(256) if d[cc] == best and table[cc] != 0.0]
+        if len({table[cc] for cc in tied}) > 1:
+            assert c % 2 == 0, ("tie to even", x, c)
+        if val == 0.0:
+            assert bool(c & 0x80) == bool(np.signbit(x)), ("zero sign", x, c)
+
+
+def check_fp8_hadamard(orc):
+    # The transform: scipy's Hadamard matrix (Sylvester's construction), H H^T
+    # = D I, and the pages' invariance: with M = diag(sigma) H / sqrt(D),
+    # (Q M)(K M)^T = Q K^T before any rounding.
+    import scipy.linalg
+    f = orc.fp8
+    for D in (1, 2, 8, 64, 128):
+        H = f.sylvester_hadamard(D)
+        assert np.array_equal(H, scipy.linalg.hadamard(D))
+        assert np.array_equal(H @ H.T, D * np.eye(D))
+    rng = np.random.default_rng(33)
+    q, k = rng.standard_normal((7, 64)), rng.standard_normal((9, 64))
+    sig = rng.choice([-1.0, 1.0], 64)
+    S = f.incoherent(q, sig) @ f.incoherent(k, sig).T / 64
+    assert np.allclose(S, q @ k.T, rtol=0, atol=1e-12)
+    # The matrix of the transform, read off the unit vectors, is diag(sigma) H
+    # (the random sign flips, then the Hadamard transform).
+    assert np.array_equal(f.incoherent(np.eye(64), sig), np.diag(sig) @ scipy.linalg.hadamard(64))
+    # Exactness on small integers (every partial sum representable).
+    qi = rng.integers(-50, 50, (5, 128)).astype(np.float64)
+    assert np.array_equal(f.incoherent(qi, np.ones(128)), qi @ scipy.linalg.hadamard(128))
+
+
+def check_fp8_block_scale(orc):
+    f = orc.fp8
+    rng = np.random.default_rng(35)
+    amaxes = np.concatenate([rng.uniform(1e-6, 1e6, 200), [448.0, 449.0, 224.0, 0.875, 0.875 * 2 ** -3, 1.0, 2.0 ** -20]])
+    for a in amaxes:
+        k = f.block_scale_exponent(float(a))
+        assert a * 2.0 ** -k <= 448.0 and a * 2.0 ** -(k - 1) > 448.0, (a, k)
+    assert f.block_scale_exponent(0.0) == 0
+    # Per-block scales: powers of two, every block within half an E4M3 step,
+    # and one block's outlier leaves the other blocks' codes alone.
+    x = _bf16(rng.standard_normal((2, 300, 64)))
+    codes, scales, values = f.quantize_rows(x, 64)
+    assert scales.shape == (2, 5) and np.all(np.log2(scales) == np.round(np.log2(scales)))
+    for j in range(5):
+        blk, vb = x[:, 64 * j:64 * (j + 1)], values[:, 64 * j:64 * (j + 1)]
+        sc = scales[:, j][:, None, None]
+        assert np.all(np.abs(vb - blk) <= np.maximum(np.abs(blk) * 2.0 ** -4, sc * 2.0 ** -10) + 1e-300)
+        assert np.all(np.abs(vb / sc) <= 448.0)
+    y = x.copy()
+    y[0, 5, 3] = 3000.0
+    c2, s2, _ = f.quantize_rows(y, 64)
+    assert s2[0, 0] > scales[0, 0] and np.array_equal(s2[:, 1:], scales[:, 1:])
+    assert np.array_equal(c2[:, 64:], codes[:, 64:]) and np.array_equal(c2[1], codes[1])
+
+
+def check_fp8_attention(orc):
+    f = orc.fp8
+    rng = np.random.default_rng(37)
+    # Values already on the E4M3 grid of their block (small integers, every
+    # block reaching 448 after scaling) pass through the quantizer unchanged,
+    # so the FP8 attention equals the exact one.
+    B, H, L, D = 1, 2, 96, 16
+    q = rng.integers(-7, 8, (B, H, L, D)).astype(np.float64)
+    k = rng.integers(-7, 8, (B, H, L, D)).astype(np.float64)
+    v = rng.standard_normal((B, H, L, D))
+    O, lse, qc, qs, kc, ks = f.fp8_attention_forward(q, k, v, 0.05, causal=True, q_block=32, k_block=16)
+    O0, l0 = orc.attention_forward(q, k, v, 0.05, True)
+    assert np.array_equal(O, O0) and np.array_equal(lse, l0)
+    # With the transform, the pages' experiment: Q and K sharing outlier
+    # channels; block scales and incoherent processing cut the RMSE of O
+    # against the exact attention well below that of one per-tensor scale
+    # (the pages report 2.6x on FA3's inputs; this seed gives ~4x).
+    B, H, L, D = 1, 2, 512, 64
+    q, k, v = (rng.standard_normal((B, H, L, D)) for _ in range(3))
+    ch = rng.choice(D, 2, replace=False)
+    q[..., ch] *= 10.0
+    k[..., ch] *= 10.0
+    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    scale = 1.0 / np.sqrt(D) / 10.0
+    O0, _ = orc.attention_forward(q, k, v, scale)
+    Ot, _ = orc.attention_forward(f.quantize_per_tensor(q), f.quantize_per_tensor(k), v, scale)
+    sig = rng.choice([-1.0, 1.0], D)
+    Oi, *_ = f.fp8_attention_forward(q, k, v, scale, signs=sig)
+    rmse = lambda o: float(np.sqrt(np.mean((o - O0) ** 2)))
+    assert rmse(Oi) * 2.0 < rmse(Ot), (rmse(Oi), rmse(Ot))
+    # and the quantized attention stays close to the exact one
+    assert rmse(Oi) < 0.02
+
+
 CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, check_two_tile,
           check_mask_table, check_streaming_vs_dense, check_merge_trees,
           check_page_streaming_experiment, check_page_split_experiment, check_brute_force,
@@ -701,7 +829,8 @@ CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, che
           check_fully_masked_rows, check_window_closed_forms, check_window_brute_force,
           check_paged_matches_contiguous, check_paged_permutation, check_paged_invalid_entries,
           check_backward_page_experiment, check_backward_vs_autograd, check_backward_finite_differences,
-          check_backward_gqa_and_lengths]
+          check_backward_gqa_and_lengths, check_fp8_format, check_fp8_hadamard, check_fp8_block_scale,
+          check_fp8_attention]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -756,6 +885,16 @@ MUTANTS = {
     "bwd_causal_dropped": [("backward", "allowed &= k_pos[None, :] <= q_pos[:, None]", "allowed &= True")],
     "bwd_top_left": [("backward", "q_pos = (n - Lq) + np.arange(Lq)", "q_pos = np.arange(Lq)")],
     "bwd_window_off_by_one": [("backward", "(dist < window)", "(dist <= window)")],
+    "fp8_ties_away": [("fp8", "mag = np.rint(a / spacing) * spacing", "mag = np.floor(a / spacing + 0.5) * spacing")],
+    "fp8_no_subnormals": [("fp8", "binade = np.maximum(E - 1, -6)", "binade = E - 1")],
+    "fp8_bias_off": [("fp8", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)")],
+    "fp8_scale_loose": [("fp8", "return int(E - 9) if amax <= 0.875 * 2.0 ** E else int(E - 8)", "return int(E - 8)")],
+    "fp8_scale_overflow": [("fp8", "return int(E - 9) if amax <= 0.875 * 2.0 ** E else int(E - 8)", "return int(E - 9)")],
+    "fp8_no_signs": [("fp8", "return (x * s) @ H", "return x @ H")],
+    "fp8_unnormalised": [("fp8", "eff = scale / D if signs is not None else scale", "eff = scale")],
+    "fp8_one_scale": [("fp8", "blk = x32[idx][j * block_rows:(j + 1) * block_rows]\n            k = block_scale_exponent(float(np.abs(blk).max()) if blk.size else 0.0)",
+                       "blk = x32[idx][j * block_rows:(j + 1) * block_rows]\n            k = block_scale_exponent(float(np.abs(x32).max()))")],
+    "fp8_code_sign_dropped": [("fp8", "codes = np.where(normal, code_norm, code_sub) + np.where(neg, 0x80, 0)", "codes = np.where(normal, code_norm, code_sub)")],
 }
 
 
