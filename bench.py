@@ -9,7 +9,9 @@ non-causal prefill B=4, Hq=Hkv=16, Lq=Lk=1024, D=64; the causal, long-context
 GQA and split-KV decode workloads, and the follow-on variants (the GQA
 workload under a causal window of 4096 keys; the decode workload served from
 a shuffled paged cache with 16-token pages; the backward of the causal 4K and
-1K prefill workloads, one fa_bwd call per step), are timed the same way and
+1K prefill workloads, one fa_bwd call per step; the causal 4K and GQA 16K
+forward with FP8 scores, one fa_fwd_fp8 call per step on Q and K quantized
+beforehand, the quantization timed separately), are timed the same way and
 reported under "workloads".  Time is taken with HIP events on the stream the kernels are
 launched on (torch's current stream), bracketed by device synchronisation.
 
@@ -35,6 +37,10 @@ if ROOT not in sys.path:
 METRIC = "attn fwd TFLOP/s & % of MI355X bf16 MFMA peak; decode HBM GB/s & % peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA, twice the bf16 rate
+# FP8-score forward: half the algorithmic FLOPs (S = QK^T) at the fp8 rate and
+# half (PV) at the bf16 rate, so its peak is the harmonic combination.
+PEAK_FP8_SCORES_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 HEADLINE = "prefill_b4_h16_l1024_d64"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -81,6 +87,26 @@ def time_workload(w, steps, warmup, dev):
         fwd()                                   # the forward's o and lse are the backward's inputs
         call = binding.PreparedBwdCall(q, k, v, o, lse, inp.meta["dout"].to(dev), causal=w.causal,
                                        window=w.window, scale=w.scale, kv_lens=kl)
+    elif w.fp8:
+        # Q and K quantized (after the random-sign Hadamard transform) before
+        # timing, as an FP8 cache would hold them; the step is one fa_fwd_fp8.
+        # The quantizer is timed separately below.
+        k, v = inp.k.to(dev), inp.v.to(dev)
+        sg = inp.meta["signs"].to(dev)
+        q8, qs = binding.quantize_fp8(q, binding.FP8_Q_BLOCK, sg)
+        k8, ks = binding.quantize_fp8(k, binding.FP8_K_BLOCK, sg)
+        call = binding.PreparedFp8Call(q8, k8, v, qs, ks, causal=w.causal, scale=w.scale / w.D, kv_lens=kl)
+
+        lib = binding.load_library()
+        st = torch.cuda.current_stream(dev).cuda_stream
+        qargs = (q.data_ptr(), q8.data_ptr(), qs.data_ptr(), w.B * w.Hq, w.Lq, w.D, binding.FP8_Q_BLOCK,
+                 sg.data_ptr(), st)
+        kargs = (k.data_ptr(), k8.data_ptr(), ks.data_ptr(), w.B * w.Hkv, w.Lk, w.D, binding.FP8_K_BLOCK,
+                 sg.data_ptr(), st)
+
+        def quantize():                     # one ctypes call each, arguments marshalled once
+            lib.fa_quantize_fp8(*qargs)
+            lib.fa_quantize_fp8(*kargs)
     elif w.page_size:
         # Only the paged copy of K and V is resident for a paged workload.
         kc, vc, table = (t.to(dev) for t in inp.meta["paged"])
@@ -107,6 +133,16 @@ def time_workload(w, steps, warmup, dev):
            "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9}
     if w.Lq == 1 and not w.backward:
         rec.update(bound="hbm", frac=rec["gbs"] / PEAK_HBM_GBS)
+    elif w.fp8:
+        rec.update(bound="mfma", frac=rec["tflops"] / PEAK_FP8_SCORES_TFLOPS, peak=PEAK_FP8_SCORES_TFLOPS)
+        quantize()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            quantize()
+        end.record()
+        torch.cuda.synchronize()
+        rec["quantize_ms"] = start.elapsed_time(end) / steps
     else:
         rec.update(bound="mfma", frac=rec["tflops"] / PEAK_BF16_TFLOPS)
     del call, q, k, v, o, lse, kl
@@ -212,7 +248,7 @@ def main():
     unit = "GB/s" if decode else "TFLOP/s"
     traffic = stored_traffic(head.name)
     roof = {"bound": rec["bound"], "achieved": round(value, 3),
-            "peak": PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS,
+            "peak": PEAK_HBM_GBS if decode else rec.get("peak", PEAK_BF16_TFLOPS),
             "unit": unit, "frac": round(rec["frac"], 4), "traffic": traffic}
     cpu = None
     if not args.no_cpu:
@@ -221,7 +257,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(rec["ms_per_step"], 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 scores, bf16 PV" if head.fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) bf16 inputs)",
         "config": {"workload": head.name, "B": head.B, "Hq": head.Hq, "Hkv": head.Hkv,
                    "Lq": head.Lq, "Lk": head.Lk, "D": head.D, "causal": head.causal,

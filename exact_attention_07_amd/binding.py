@@ -21,7 +21,11 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every entry point declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_bwd",
+            "fa_quantize_fp8", "fa_fwd_fp8",
             "fa_workspace_bytes", "fa_status_string", "fa_last_error")
+
+# Block sizes of the FP8 forward's scales (query rows, keys).
+FP8_Q_BLOCK, FP8_K_BLOCK = 256, 64
 
 
 class FaError(RuntimeError):
@@ -59,6 +63,12 @@ def load_library(path: Optional[str] = None):
     # q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, causal, window, scale, kv_lens, stream
     lib.fa_bwd.argtypes = [vp] * 9 + [i32] * 8 + [f32, vp, vp]
     lib.fa_bwd.restype = i32
+    # x, x8, scales, heads, L, D, block_rows, signs, stream
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.fa_quantize_fp8.restype = i32
+    # q8, k8, v, o, lse, q_scales, k_scales, B, Hq, Hkv, Lq, Lk, D, causal, scale, kv_lens, stream
+    lib.fa_fwd_fp8.argtypes = [vp] * 7 + [i32] * 7 + [f32, vp, vp]
+    lib.fa_fwd_fp8.restype = i32
     lib.fa_workspace_bytes.argtypes = [i32] * 6
     lib.fa_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i32]
@@ -295,3 +305,97 @@ class PreparedBwdCall:
         if status != FA_OK:
             _check(status)
         return self.grads
+
+
+def quantize_fp8(x, block_rows, signs=None, stream=None):
+    """E4M3 codes and block scales of the rows of ``x`` [B, H, L, D] (bf16)
+    through ``fa_quantize_fp8``; ``signs`` (D values +-1, fp32 device tensor)
+    applies the Hadamard transform with those sign flips first.  Returns
+    (codes uint8 [B, H, L, D], scales fp32 [B, H, ceil(L / block_rows)])."""
+    if x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("x must be a contiguous 4-D bfloat16 GPU tensor [B, H, L, D]")
+    B, H, L, D = x.shape
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != D
+                              or signs.device != x.device or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous fp32 device tensor of D entries")
+    codes = torch.empty(B, H, L, D, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(B, H, -(-L // block_rows), dtype=torch.float32, device=x.device)
+    s = torch.cuda.current_stream(x.device).cuda_stream if stream is None else stream
+    _check(load_library().fa_quantize_fp8(_ptr(x), _ptr(codes), _ptr(scales), B * H, L, D,
+                                          int(block_rows), _ptr(signs), s))
+    return codes, scales
+
+
+def _prepare_fp8(q8, k8, v, q_scales, k_scales, o, lse, kv_lens, want_lse):
+    for name, t in (("q8", q8), ("k8", k8)):
+        if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a contiguous 4-D uint8 GPU tensor of E4M3 codes")
+    if v.dtype != torch.bfloat16 or not v.is_contiguous() or v.device != q8.device:
+        raise ValueError("v must be a contiguous bf16 device tensor")
+    B, Hq, Lq, D = q8.shape
+    _, Hkv, Lk, _ = k8.shape
+    if tuple(v.shape) != tuple(k8.shape) or k8.shape[0] != B or k8.shape[3] != D:
+        raise ValueError("k8 and v must be [B, Hkv, Lk, D] with the batch and D of q8")
+    for name, t, shape in (("q_scales", q_scales, (B, Hq, -(-Lq // FP8_Q_BLOCK))),
+                           ("k_scales", k_scales, (B, Hkv, -(-Lk // FP8_K_BLOCK)))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() \
+                or t.device != q8.device:
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor {shape}")
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != B
+                                or kv_lens.device != q8.device or not kv_lens.is_contiguous()):
+        raise ValueError("kv_lens must be a contiguous int32 device tensor of B entries")
+    o = torch.empty(B, Hq, Lq, D, dtype=torch.bfloat16, device=q8.device) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device=q8.device)
+    return o, lse, (B, Hq, Hkv, Lq, Lk, D)
+
+
+def fa_fwd_fp8(q8, k8, v, q_scales, k_scales, o=None, lse=None, *, causal=False, scale=None,
+               kv_lens=None, stream=None, want_lse=True):
+    """Attention with FP8 scores through ``fa_fwd_fp8``: q8, k8 are E4M3 codes
+    with block scales (256 query rows, 64 keys) as from ``quantize_fp8``;
+    S = scale * (q8 sq)(k8 sk)^T.  Returns (o, lse)."""
+    o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare_fp8(q8, k8, v, q_scales, k_scales, o, lse, kv_lens,
+                                                   want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q8.device).cuda_stream if stream is None else stream
+    _check(load_library().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_scales),
+                                      _ptr(k_scales), B, Hq, Hkv, Lq, Lk, D, int(bool(causal)), scale,
+                                      _ptr(kv_lens), s))
+    return o, lse
+
+
+def attention_fp8(q, k, v, *, causal=False, scale=None, kv_lens=None, signs=None, stream=None):
+    """bf16 Q, K, V -> FP8 attention: Q and K block-quantized (after the
+    Hadamard transform with ``signs`` when given, whose factor D in the
+    scores is divided out of the scale), then ``fa_fwd_fp8``.  Returns
+    (o, lse)."""
+    D = q.shape[3]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    q8, qs = quantize_fp8(q, FP8_Q_BLOCK, signs, stream)
+    k8, ks = quantize_fp8(k, FP8_K_BLOCK, signs, stream)
+    eff = scale / D if signs is not None else scale
+    return fa_fwd_fp8(q8, k8, v, qs, ks, causal=causal, scale=eff, kv_lens=kv_lens, stream=stream)
+
+
+class PreparedFp8Call:
+    """fa_fwd_fp8 with its arguments checked and marshalled once (see PreparedCall)."""
+
+    def __init__(self, q8, k8, v, q_scales, k_scales, *, causal=False, scale=None, kv_lens=None,
+                 stream=None):
+        o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare_fp8(q8, k8, v, q_scales, k_scales, None, None,
+                                                       kv_lens, True)
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        s = torch.cuda.current_stream(q8.device).cuda_stream if stream is None else stream
+        self.o, self.lse = o, lse
+        self._keep = (q8, k8, v, q_scales, k_scales, kv_lens)
+        self._fn = load_library().fa_fwd_fp8
+        self._args = (_ptr(q8), _ptr(k8), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_scales), _ptr(k_scales),
+                      B, Hq, Hkv, Lq, Lk, D, int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), s)
+        self()
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+        return self.o, self.lse

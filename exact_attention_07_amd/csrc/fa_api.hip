@@ -351,6 +351,66 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     return FA_OK;
 }
 
+int fa_quantize_fp8(const void* x, void* x8, float* scales, int heads, int L, int D,
+                    int block_rows, const float* signs, void* stream) {
+    g_last_error[0] = '\0';
+    if (heads <= 0 || L <= 0 || block_rows <= 0)
+        return fail(FA_ERR_INVALID_ARG, "heads, L and block_rows must be positive: heads=%d L=%d block_rows=%d",
+                    heads, L, block_rows);
+    if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension D=%d is not supported (64 or 128)", D);
+    if (!x || !x8 || !scales) return fail(FA_ERR_INVALID_ARG, "x, x8 and scales must not be NULL");
+    if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4) || !aligned(signs, 4))
+        return fail(FA_ERR_INVALID_ARG, "x and x8 must be 16-byte aligned, scales and signs 4-byte aligned");
+    const long long nblk = (L + (long long)block_rows - 1) / block_rows;
+    if ((long long)heads * nblk > INT32_MAX || (long long)L * D > INT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "problem too large");
+    fa::QuantParams p;
+    p.x = static_cast<const __bf16*>(x);
+    p.x8 = static_cast<uint8_t*>(x8);
+    p.scales = scales;
+    p.signs = signs;
+    p.heads = heads; p.L = L; p.block_rows = block_rows; p.nblk = (int)nblk;
+    hipError_t e = fa::launch_quantize_fp8(D, p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,
+               const float* q_scales, const float* k_scales,
+               int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+               const int* kv_lens, void* stream) {
+    g_last_error[0] = '\0';
+    const Shape s{B, Hq, Hkv, Lq, Lk, D};
+    int st = validate(q8, k8, v, o, lse, s, causal, scale, kv_lens);
+    if (st != FA_OK) return st;
+    if (D != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward is built for D=128 (got D=%d)", D);
+    if (!q_scales || (Lk > 0 && !k_scales)) return fail(FA_ERR_INVALID_ARG, "q_scales and k_scales must not be NULL");
+    if (!aligned(q_scales, 4) || !aligned(k_scales, 4))
+        return fail(FA_ERR_INVALID_ARG, "q_scales and k_scales must be 4-byte aligned");
+    fa::PrefillParams p;
+    p.q = nullptr; p.k = nullptr;
+    p.v = static_cast<const __bf16*>(v);
+    p.o = static_cast<__bf16*>(o);
+    p.lse = lse; p.kv_lens = kv_lens;
+    p.q8 = static_cast<const uint8_t*>(q8);
+    p.k8 = static_cast<const uint8_t*>(k8);
+    p.q_scale = q_scales;
+    p.k_scale = k_scales;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk;
+    p.r = Hq / Hkv;
+    p.n_qblocks = (Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+    const int units = B * Hkv;
+    p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+    p.window = 0;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    const long long total = (long long)B * Hq * p.n_qblocks;
+    if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    hipError_t e = fa::launch_prefill_fp8(causal != 0, p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
 size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D) {
     const Shape s{B, Hq, Hkv, Lq, Lk, D};
     char saved[sizeof(g_last_error)];

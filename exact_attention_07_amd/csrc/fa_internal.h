@@ -3,12 +3,19 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
 // Query rows per prefill workgroup: four wavefronts of 64 rows, each
 // workgroup sharing every K/V tile among them.
 constexpr int kPrefillRows = 256;
+
+// FP8 (E4M3) operands: one power-of-two scale per kFp8QBlock query rows and
+// per kFp8KBlock keys of a head -- the prefill workgroup's query block and
+// its KV tile.
+constexpr int kFp8QBlock = kPrefillRows;
+constexpr int kFp8KBlock = 64;
 
 struct PrefillParams {
     const __bf16* q;
@@ -24,6 +31,20 @@ struct PrefillParams {
     int window;            // causal window width (keys j with 0 <= pos_i - j < window); 0 = none
     float scale;           // softmax scale
     float c;               // scale * log2(e): scores enter exp2 as s * c
+    // FP8 instantiation only: E4M3 codes of Q [B, Hq, Lq, D] and K [B, Hkv, Lk, D]
+    // with their block scales [B, Hq, ceil(Lq / 256)] and [B, Hkv, ceil(Lk / 64)].
+    const uint8_t* q8;
+    const uint8_t* k8;
+    const float* q_scale;
+    const float* k_scale;
+};
+
+struct QuantParams {
+    const __bf16* x;       // [heads, L, D]
+    uint8_t* x8;           // [heads, L, D] E4M3 codes
+    float* scales;         // [heads, nblk] powers of two
+    const float* signs;    // D values +-1 (Hadamard with sign flips), or null
+    int heads, L, block_rows, nblk;
 };
 
 struct SplitParams {
@@ -84,6 +105,9 @@ struct BwdParams {
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream);
+// The prefill with E4M3 Q and K (D = 128): p.q8, p.k8 and the scales replace p.q and p.k.
+hipError_t launch_prefill_fp8(bool causal, const PrefillParams& p, hipStream_t stream);
+hipError_t launch_quantize_fp8(int D, const QuantParams& p, hipStream_t stream);
 hipError_t launch_splitkv(int D, bool paged, const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
 // The dq kernel (which also writes delta) then the dk/dv kernel.

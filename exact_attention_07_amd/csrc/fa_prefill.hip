@@ -79,7 +79,23 @@ struct Const { static constexpr int value = N; };
 constexpr float kTau = 8.0f;
 constexpr float kTauSum = 256.0f;
 
-template <int D, bool CAUSAL, bool WINDOW>
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// FP8 instantiation: S^T = K Q^T from E4M3 codes on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales in the instruction; the
+// tile's dequantisation factor s_q s_k goes into the exponent's scale).  A
+// lane holds 32 bytes of its K row (A) or Q row (B); the instruction pairs
+// byte e of lane half hi in A with the same in B, so giving both the bytes
+// 64 ks + 32 hi + e of a row makes the product a dot product over D.  K rows
+// of 128 bytes sit in LDS in 16-byte chunks XOR-swizzled by (row / 2) % 8,
+// so 16 lanes reading one chunk column of 16 rows hit 16 distinct bank
+// groups.  V and P stay bf16 (the PV product is the bf16 one).
+template <bool FP8>
+struct ScoreOperand { typedef bf16x8 type; };
+template <>
+struct ScoreOperand<true> { typedef i32x8 type; };
+
+template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
     constexpr int NW = 8;                   // wavefronts: two groups of four
@@ -96,6 +112,11 @@ prefill_kernel(PrefillParams p) {
     static_assert(BM == kPrefillRows, "host and kernel disagree on the query block");
     static_assert(NI >= 1 && (BN * CH) % NT == 0, "a tile must split evenly over the workgroup");
     static_assert(CAUSAL || !WINDOW, "the window is causal");
+    static_assert(!FP8 || (D == 128 && !WINDOW), "the FP8 scores are built for D = 128 without a window");
+    constexpr int KSQ = FP8 ? D / 64 : KS;  // k-steps of S^T
+    constexpr int NIK = FP8 ? BN * D / (NT * 16) : NI;   // 16-byte copies per thread per K tile
+    static_assert(NIK >= 1, "a K tile must split evenly over the workgroup");
+    typedef typename ScoreOperand<FP8>::type SA;
 
     // K buffers at [0, NB TILE), V buffers at [NB TILE, 2 NB TILE).
     __shared__ __attribute__((aligned(16))) bf16 smem[2 * NB * TILE];
@@ -152,11 +173,29 @@ prefill_kernel(PrefillParams p) {
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
 
     // ---- Q tile: B operand of S^T, resident in registers -------------------
-    const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)p.Lq * D * 2);   // rows >= Lq read as zero
-    bf16x8 qf[KS];
+    SA qf[KSQ];
+    if constexpr (FP8) {
+        const rsrc_t qbuf = make_rsrc(p.q8 + qoff, (uint32_t)p.Lq * D);   // rows >= Lq read as zero
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = load16(qbuf, (uint32_t)(qrow * D + ks * 16 + hi * 8) * 2);
+        for (int ks = 0; ks < KSQ; ++ks) {
+            const uint32_t at = (uint32_t)(qrow * D + 64 * ks + 32 * hi);
+            const i32x4 lo = __builtin_bit_cast(i32x4, load16(qbuf, at));
+            const i32x4 up = __builtin_bit_cast(i32x4, load16(qbuf, at + 16));
+            qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        }
+    } else {
+        const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)p.Lq * D * 2);   // rows >= Lq read as zero
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = load16(qbuf, (uint32_t)(qrow * D + ks * 16 + hi * 8) * 2);
+    }
+    // FP8: exponent scale of tile t = c s_q s_k(t); s_k is read one tile ahead.
+    const float cq = FP8 ? p.c * p.q_scale[(size_t)(b * p.Hq + h) * p.n_qblocks + qblk] : p.c;
+    const int nks = (p.Lk + kFp8KBlock - 1) / kFp8KBlock;
+    const float* kscale = FP8 ? p.k_scale + (size_t)(b * p.Hkv + g) * nks : nullptr;
+    auto k_scale_of = [&](int t) __attribute__((always_inline)) {   // tile index relative to tb
+        return (FP8 && nks > 0) ? kscale[min(tb + t, nks - 1)] : 1.0f;   // no K rows: nothing to read
+    };
 
     // ---- direct HBM -> LDS copies -----------------------------------------
     // Copy i of wavefront w fills LDS chunk positions P = (w*NI + i)*64 + lane of
@@ -164,13 +203,21 @@ prefill_kernel(PrefillParams p) {
     // The per-lane source offsets are fixed; each tile gets its own buffer
     // descriptor (base advanced by the tile, range = the valid rows left), so
     // rows past n arrive as zeros and the per-tile work is scalar.
-    uint32_t koff[NI], voff[NI];
+    uint32_t koff[NIK], voff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int P = (w * NI + i) * 64 + l;
         const int row = P / CH;
-        koff[i] = (uint32_t)(row * D + (((P % CH) ^ k_swizzle<D>(row)) * 8)) * 2;
+        if (!FP8) koff[i] = (uint32_t)(row * D + (((P % CH) ^ k_swizzle<D>(row)) * 8)) * 2;
         voff[i] = (uint32_t)(row * D + (((P % CH) ^ v_swizzle<D>(row)) * 8)) * 2;
+    }
+    if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < NIK; ++i) {     // E4M3 rows of D bytes: D / 16 chunks
+            const int P = (w * NIK + i) * 64 + l;
+            const int row = P / (D / 16);
+            koff[i] = (uint32_t)(row * D + (((P % (D / 16)) ^ ((row >> 1) & 7)) * 16));
+        }
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)smem);
     auto copy_tile = [&](const bf16* base, int t, int buf, const uint32_t (&offs)[NI]) __attribute__((always_inline)) {
@@ -182,7 +229,19 @@ prefill_kernel(PrefillParams p) {
         for (int i = 0; i < NI; ++i)
             copy16_to_lds_async(d, offs[i], lds0 + (uint32_t)(buf * TILE + (w * NI + i) * 512) * 2);
     };
-    auto copy_k = [&](int t) { copy_tile(p.k, t, t % NB, koff); };
+    auto copy_k = [&](int t) __attribute__((always_inline)) {
+        if constexpr (FP8) {
+            const int ta = tb + t;
+            const int rows = n - ta * BN;
+            const i32x4 d = make_desc(p.k8 + kvoff + (size_t)(rows > 0 ? ta : 0) * BN * D,
+                                      (uint32_t)(rows > 0 ? rows : 0) * D);
+#pragma unroll
+            for (int i = 0; i < NIK; ++i)
+                copy16_to_lds_async(d, koff[i], lds0 + (uint32_t)((t % NB) * TILE * 2 + (w * NIK + i) * 1024));
+        } else {
+            copy_tile(p.k, t, t % NB, koff);
+        }
+    };
     auto copy_v = [&](int t) { copy_tile(p.v, t, NB + t % NB, voff); };
 
     // ---- per-lane LDS read offsets (constant over the loop) -----------------
@@ -195,6 +254,26 @@ prefill_kernel(PrefillParams p) {
     const int vxor = v_swizzle<D>(vrow);    // rows differ from vrow by multiples of 4
     const int vcol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
+    // A operand (K rows) of score step ks of key block kb, and the product.
+    auto k_operand = [&](const bf16* Ks, int kb, int ks) __attribute__((always_inline)) -> SA {
+        if constexpr (FP8) {
+            const uint8_t* row = reinterpret_cast<const uint8_t*>(Ks) + (kb * 32 + krow) * D;
+            const int x8 = (krow >> 1) & 7;
+            const int c0 = 4 * ks + 2 * hi;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(row + ((c0 ^ x8) * 16));
+            const i32x4 up = *reinterpret_cast<const i32x4*>(row + (((c0 + 1) ^ x8) * 16));
+            return i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        } else {
+            return *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + krow) * D + (((2 * ks + hi) ^ kxor) * 8));
+        }
+    };
+    auto score_mfma = [&](const SA& a, int ks, const f32x16& acc_in) __attribute__((always_inline)) -> f32x16 {
+        if constexpr (FP8)
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], acc_in, 0, 0, 0, 127, 0, 127);
+        else
+            return mfma_32x32x16(a, qf[ks], acc_in);
+    };
+
     f32x16 s[KB];                           // S^T of the tile being prepared
     auto score_tile = [&](int t) __attribute__((always_inline)) {
         const bf16* Ks = smem + (t % NB) * TILE;
@@ -202,11 +281,7 @@ prefill_kernel(PrefillParams p) {
         for (int kb = 0; kb < KB; ++kb) {
             s[kb] = zero_f32x16();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    Ks + (kb * 32 + krow) * D + (((2 * ks + hi) ^ kxor) * 8));
-                s[kb] = mfma_32x32x16(a, qf[ks], s[kb]);
-            }
+            for (int ks = 0; ks < KSQ; ++ks) s[kb] = score_mfma(k_operand(Ks, kb, ks), ks, s[kb]);
         }
     };
 
@@ -222,11 +297,14 @@ prefill_kernel(PrefillParams p) {
     // rounded values) while its score products run.
     float pe[KB][2][8];
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    float ksc_next = k_scale_of(0);         // FP8: s_k of the tile softmax_tile handles next
 
     // Vector phase for tile t (scores in s): mask where needed, p -> pe and the
     // fp32 row sum, and the rare reference move.
     auto softmax_tile = [&](int t) __attribute__((always_inline)) {
         const int k0 = (tb + t) * BN;
+        const float ct = FP8 ? cq * ksc_next : c;   // this tile's exponent scale
+        if (FP8) ksc_next = k_scale_of(t + 1);
         // Elementwise masks only where some pair of this wavefront's rows and
         // the tile is out: past n, above the diagonal, or (window) at least w
         // positions before the wavefront's last row.
@@ -257,7 +335,7 @@ prefill_kernel(PrefillParams p) {
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], c, -r));
+                        pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], ct, -r));
                         se[j & 3] += pe[kb][half][j];
                     }
         };
@@ -280,7 +358,7 @@ prefill_kernel(PrefillParams p) {
             float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
             mx = max_with_partner(mx);
             const bool shift = move && mx != kNegInf;   // a row with no valid key so far keeps -inf
-            const float r_new = shift ? mx * c + kTau : ref;   // kTau of headroom above the max
+            const float r_new = shift ? mx * ct + kTau : ref;  // kTau of headroom above the max
             const float alpha = shift ? exp2_fast(ref - r_new) : 1.0f;   // 0 from an empty row
             ref = r_new;
             ell_e *= alpha;
@@ -304,16 +382,15 @@ prefill_kernel(PrefillParams p) {
         constexpr int PH = decltype(phase)::value;      // t % NB
         const bf16* Ks = smem + ((PH + 1) % NB) * TILE;
         const bf16* Vs = smem + (NB + PH) * TILE;
-        constexpr int NQ = KB * KS;         // score products
+        constexpr int NQ = KB * KSQ;        // score products
         constexpr int NF = DB * KB * 2;     // PV products (one V fragment each)
         constexpr int NOPS = NQ + NF;
         constexpr int AHEAD = 6;
-        bf16x8 frag[NOPS];
+        SA kfrag[NQ];                       // score operands
+        bf16x8 frag[NOPS];                  // PV operands (entries NQ..)
         auto read_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
-                const int kb = i / KS, ks = i % KS;
-                frag[i] = *reinterpret_cast<const bf16x8*>(
-                    Ks + (kb * 32 + krow) * D + (((2 * ks + hi) ^ kxor) * 8));
+                kfrag[i] = k_operand(Ks, i / KSQ, i % KSQ);
             } else {
                 const int f = i - NQ;
                 const int db = f / (KB * 2), kb = (f / 2) % KB, half = f % 2;
@@ -343,8 +420,8 @@ prefill_kernel(PrefillParams p) {
         };
         auto mfma_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
-                const int kb = i / KS, ks = i % KS;
-                s[kb] = mfma_32x32x16(frag[i], qf[ks], ks == 0 ? zero_f32x16() : s[kb]);
+                const int kb = i / KSQ, ks = i % KSQ;
+                s[kb] = score_mfma(kfrag[i], ks, ks == 0 ? zero_f32x16() : s[kb]);
                 if (i % (NQ / NP) == 0) convert_p(i / (NQ / NP));
                 if (i == NQ - 1) ell_r += sr[0] + sr[1];
             } else {
@@ -389,7 +466,7 @@ prefill_kernel(PrefillParams p) {
         // phase one basic block.
         matrix_phase(phase);
         __builtin_amdgcn_s_setprio(0);
-        wait_vector_loads_until<2 * NI>();  // the copies of M(t-1) have landed
+        wait_vector_loads_until<NIK + NI>();   // the copies of M(t-1) have landed
         __syncthreads();
         // ---- vector phase V(t) ----
         if (t + 1 < ntiles) softmax_tile(t + 1);
@@ -430,6 +507,14 @@ void launch_prefill_d(bool causal, bool window, const PrefillParams& p, dim3 gri
     if (window)      hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, block, 0, stream, p);
     else if (causal) hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, block, 0, stream, p);
     else             hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, block, 0, stream, p);
+}
+
+hipError_t launch_prefill_fp8(bool causal, const PrefillParams& p, hipStream_t stream) {
+    const long long total = (long long)p.B * p.Hq * p.n_qblocks;
+    const dim3 grid((unsigned)total), block(512);
+    if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, false, true>), grid, block, 0, stream, p);
+    else        hipLaunchKernelGGL((prefill_kernel<128, false, false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream) {

@@ -56,6 +56,7 @@ class Workload:
     window: int = 0             # causal window width (0 = none)
     page_size: int = 0          # > 0: K and V are served from a paged cache
     backward: bool = False      # time the backward (fa_bwd) instead of the forward
+    fp8: bool = False           # FP8 scores: Q, K block-quantized after the random-sign Hadamard transform
 
     @property
     def seed(self) -> int:
@@ -90,6 +91,11 @@ WORKLOADS = [
              description="backward of the causal prefill forward"),
     Workload("bwd_prefill_b4_h16_l1024_d64", 4, 16, 16, 1024, 1024, 64, False, 1, backward=True,
              description="backward of the prefill forward, no mask"),
+    Workload("fp8_causal_b2_h16_l4096_d128", 2, 16, 16, 4096, 4096, 128, True, 2, fp8=True,
+             description="causal prefill forward with FP8 scores (block scales, incoherent processing)"),
+    Workload("fp8_gqa_causal_b1_hq32_hkv8_l16384_d128", 1, 32, 8, 16384, 16384, 128, True, 3,
+             q_boost_every=8, q_boost=4.0, fp8=True,
+             description="long-context causal GQA forward with FP8 scores"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -124,6 +130,9 @@ def make_inputs(w: Workload) -> Inputs:
                                    dtype=torch.float32).to(torch.bfloat16)
     if w.window:
         meta["window"] = w.window
+    if w.fp8:
+        # The random signs of the incoherent-processing transform, drawn after the base inputs.
+        meta["signs"] = (torch.randint(0, 2, (w.D,), generator=g) * 2 - 1).to(torch.float32)
     if w.page_size:
         # The paged copy of the same K and V; the contiguous tensors stay for reference.
         meta["paged"] = page_kv(k, v, kv_lens, w.page_size, seed=w.seed + 7919)
@@ -233,8 +242,14 @@ def algorithmic_flops(w, kv_lens=None) -> int:
 def compulsory_bytes(w, kv_lens=None) -> int:
     """Bytes that must cross HBM once: Q read, the K and V rows some query can
     see read once per KV head, O written (bf16) and the LSE written (fp32);
-    with a paged cache also the page-table entries of those rows (int32)."""
+    with a paged cache also the page-table entries of those rows (int32);
+    with FP8 scores Q and K are one byte per element plus their block scales."""
     ns = valid_lengths(w, kv_lens)
+    if w.fp8:
+        q = w.B * w.Hq * w.Lq * w.D + w.B * w.Hq * -(-w.Lq // 256) * 4
+        o = w.B * w.Hq * w.Lq * w.D * 2
+        kv = sum(w.Hkv * n * w.D * (1 + 2) + w.Hkv * -(-n // 64) * 4 for n in ns)
+        return q + o + w.B * w.Hq * w.Lq * 4 + kv
     qo = 2 * w.B * w.Hq * w.Lq * w.D * 2
     lse = w.B * w.Hq * w.Lq * 4
     seen = [min(n, w.window + w.Lq - 1) if w.window > 0 else n for n in ns]

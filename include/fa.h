@@ -163,6 +163,50 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int B, int Hq, int Hkv, int Lq, int Lk, int D,
            int causal, int window, float scale, const int* kv_lens, void* stream);
 
+/*
+ * FP8 block quantization with optional incoherent processing (FlashAttention
+ * from Scratch, section 10.3 "Treat FP8 as a second lesson"; FlashAttention
+ * 1-4, FlashAttention-3 point 3: one FP8 scale per tile, and Q and K
+ * multiplied by the same random orthogonal matrix -- a Hadamard transform with
+ * random sign flips -- before quantizing).  For each of `heads` independent
+ * [L, D] row sets of x and each block of `block_rows` consecutive rows:
+ *     x'    = H (signs * x) per row when signs != NULL (H: the D x D Sylvester
+ *             Hadamard matrix, entries +-1, unnormalised), else x; rounded to fp32
+ *     scale = 2^k, the smallest power of two with max|x'| 2^-k <= 448
+ *             (1 for an all-zero block)
+ *     x8    = E4M3 code of x' / scale, rounded to nearest, ties to even (OCP
+ *             FP8 E4M3: largest finite 448, subnormals to 2^-9)
+ *   x      : bf16, device, contiguous [heads, L, D], 16-byte aligned
+ *   x8     : uint8 E4M3 codes, device, [heads, L, D], 16-byte aligned, written
+ *   scales : fp32, device, [heads, ceil(L / block_rows)], written
+ *   signs  : fp32, device, D values each +1 or -1, or NULL for no transform
+ * Since H H^T = D I, scores from transformed Q and K are D times the
+ * original: divide the softmax scale by D (fa_fwd_fp8 takes it as given).
+ * The forward expects Q blocks of 256 rows and K blocks of 64 rows.
+ * Errors: FA_ERR_INVALID_ARG (non-positive sizes, NULL or misaligned
+ * buffers, a problem too large), FA_ERR_UNSUPPORTED (D not 64 or 128),
+ * FA_ERR_HIP.
+ */
+int fa_quantize_fp8(const void* x, void* x8, float* scales, int heads, int L, int D,
+                    int block_rows, const float* signs, void* stream);
+
+/*
+ * Attention forward with FP8 scores: fa_fwd's operation with
+ *     S_ij = scale * (q8_i * sq) . (k8_j * sk)
+ * where q8 and k8 hold E4M3 codes from fa_quantize_fp8, sq the scale of q8's
+ * 256-row block and sk the scale of k8's 64-row block.  The score product runs
+ * on the gfx950 FP8 matrix instruction with fp32 accumulation; the
+ * probabilities and V stay bf16 (the PV product is fa_fwd's).
+ *   q8 : uint8 [B, Hq, Lq, D] codes, with q_scales fp32 [B, Hq, ceil(Lq / 256)]
+ *   k8 : uint8 [B, Hkv, Lk, D] codes, with k_scales fp32 [B, Hkv, ceil(Lk / 64)]
+ *   v, o, lse, kv_lens, causal, stream: as for fa_fwd (no window)
+ * D must be 128 (FA_ERR_UNSUPPORTED otherwise); other errors as for fa_fwd.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,
+               const float* q_scales, const float* k_scales,
+               int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+               const int* kv_lens, void* stream);
+
 /* Bytes of split-KV workspace fa_fwd would use for this shape (0 when it
  * takes the prefill path, or for invalid sizes). */
 size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);

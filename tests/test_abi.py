@@ -189,3 +189,58 @@ def test_backward_validation(lib, kw, status):
     got = call_bwd(lib, **kw)
     assert got == status, (kw, got, lib.fa_last_error())
     assert lib.fa_last_error().decode() != ""
+
+
+def call_quant(lib, x=P, x8=P, scales=P, heads=2, L=100, D=128, block_rows=64, signs=None):
+    return lib.fa_quantize_fp8(x, x8, scales, heads, L, D, block_rows, signs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), binding.FA_ERR_INVALID_ARG),
+    (dict(x8=None), binding.FA_ERR_INVALID_ARG),
+    (dict(scales=None), binding.FA_ERR_INVALID_ARG),
+    (dict(x8=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(signs=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(block_rows=0), binding.FA_ERR_INVALID_ARG),
+    (dict(L=0), binding.FA_ERR_INVALID_ARG),
+    (dict(heads=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(D=96), binding.FA_ERR_UNSUPPORTED),
+])
+def test_quantize_fp8_validation(lib, kw, status):
+    got = call_quant(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
+
+
+def call_fp8(lib, q8=P, k8=P, v=P, o=P, lse=P, qs=P, ks=P, B=1, Hq=2, Hkv=1, Lq=4, Lk=8, D=128,
+             causal=0, scale=0.125, kv_lens=None):
+    return lib.fa_fwd_fp8(q8, k8, v, o, lse, qs, ks, B, Hq, Hkv, Lq, Lk, D, causal,
+                          ctypes.c_float(scale), kv_lens, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), binding.FA_ERR_UNSUPPORTED),
+    (dict(D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(qs=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ks=None), binding.FA_ERR_INVALID_ARG),
+    (dict(qs=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(q8=None), binding.FA_ERR_INVALID_ARG),
+    (dict(k8=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+])
+def test_fwd_fp8_validation(lib, kw, status):
+    got = call_fp8(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_fp8_binding_requires_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.quantize_fp8(x, 64)
+    with pytest.raises(ValueError):
+        binding._prepare_fp8(x.to(torch.uint8), x.to(torch.uint8), x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1),
+                             None, None, None, True)

@@ -1,0 +1,171 @@
+"""GPU tests of the FP8 path: fa_quantize_fp8 and fa_fwd_fp8 against the
+fp64 oracle (oracle/fp8.py).
+
+* Quantization is integer work decided on exact values (the transform is
+  exact in fp64, the scales are powers of two), so codes and scales must
+  match the oracle bit for bit.
+* The forward must match the oracle's attention of the same quantized Q and
+  K (the dense definition on the dequantized values, V as given) within the
+  forward's bar (tests/parity.py): the FP8 rounding is in both sides; what is
+  left is the kernel's fp32 accumulation and bf16 probabilities, as for
+  fa_fwd.
+* Accuracy against the unquantized attention is reported, and the pages'
+  experiment is repeated on the GPU: with outlier channels shared by Q and
+  K, incoherent processing must cut the error well below block scales alone.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_07_amd import binding, workloads as W
+from tests.parity import compare, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    if not os.path.exists(binding.LIB_PATH):
+        from exact_attention_07_amd import build
+        build.build()
+    binding.load_library()
+    return torch.device("cuda:0")
+
+
+def signs_of(seed, D):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randint(0, 2, (D,), generator=g) * 2 - 1).to(torch.float32)
+
+
+def rows(seed, shape, outliers=0, mult=10.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g)
+    if outliers:
+        ch = torch.randperm(shape[-1], generator=g)[:outliers]
+        x[..., ch] *= mult
+    return x.to(torch.bfloat16)
+
+
+QUANT_CASES = [
+    # B, H, L, D, block_rows, transform, outlier channels
+    (1, 2, 300, 128, 64, False, 0),
+    (1, 2, 300, 128, 64, True, 0),
+    (2, 3, 513, 128, 256, True, 2),
+    (1, 1, 77, 64, 64, True, 0),
+    (2, 2, 130, 64, 256, False, 3),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_quantizer_matches_oracle(dev, case):
+    B, H, L, D, R, tr, nout = case
+    x = rows(40 + L + D, (B, H, L, D), nout)
+    if L > 100:                           # an all-zero block and a block of tiny values
+        x[0, 0, :min(R, L)] = 0
+        x[-1, -1, -min(R, L):] = x[-1, -1, -min(R, L):] * 2.0 ** -30
+    sg = signs_of(7 + D, D) if tr else None
+    codes, scales = binding.quantize_fp8(x.to(dev), R, None if sg is None else sg.to(dev))
+    torch.cuda.synchronize()
+    rc, rs, _ = oracle.fp8.quantize_rows(x, R, None if sg is None else sg.numpy())
+    assert np.array_equal(scales.cpu().numpy().astype(np.float64), rs), "block scales differ"
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
+
+
+FWD_CASES = [
+    # B, Hq, Hkv, Lq, Lk, causal, kv_lens, transform
+    (1, 2, 2, 64, 64, False, None, False),
+    (2, 4, 2, 300, 333, False, None, True),
+    (2, 4, 2, 300, 333, True, None, True),
+    (2, 4, 2, 257, 300, True, "ragged", False),
+    (3, 8, 2, 129, 190, False, "ragged", True),
+    (2, 4, 4, 1, 500, False, "ragged", True),       # one query per head
+    (1, 2, 2, 100, 60, True, None, True),           # more queries than keys: empty rows
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"_{c[6] is not None}_{c[7]}")
+def test_fp8_forward_matches_oracle(dev, case):
+    B, Hq, Hkv, Lq, Lk, causal, lens, tr = case
+    D = 128
+    c = W.random_case(1200 + Lq + Lk, B, Hq, Hkv, Lq, Lk, D, causal, lens)
+    sg = signs_of(11, D) if tr else None
+    kl = None if c.kv_lens is None else c.kv_lens.to(dev)
+    o, lse = binding.attention_fp8(c.q.to(dev), c.k.to(dev), c.v.to(dev), causal=causal, scale=c.scale,
+                                   kv_lens=kl, signs=None if sg is None else sg.to(dev))
+    torch.cuda.synchronize()
+    ro, rl, *_ = oracle.fp8.fp8_attention_forward(c.q, c.k, c.v, c.scale, causal, c.kv_lens,
+                                                  None if sg is None else sg.numpy())
+    m = compare(o, lse, ro, rl)
+    print(f"[parity] fp8 {case}: {m}", flush=True)
+
+
+def test_fp8_zero_length_and_nan_padding(dev):
+    # Zero-length sequences give O = 0 and LSE = -inf; NaN in V rows past a
+    # sequence's length is never read.  (K is quantized whole, padding rows
+    # included, on both sides.)
+    B, H, L, D = 3, 2, 96, 128
+    c = W.random_case(1300, B, H, H, L, L, D, True, [96, 0, 41])
+    v = c.v.clone()
+    v[2, :, 41:] = float("nan")
+    sg = signs_of(13, D)
+    o, lse = binding.attention_fp8(c.q.to(dev), c.k.to(dev), v.to(dev), causal=True, scale=c.scale,
+                                   kv_lens=c.kv_lens.to(dev), signs=sg.to(dev))
+    torch.cuda.synchronize()
+    ro, rl, *_ = oracle.fp8.fp8_attention_forward(c.q, c.k, c.v, c.scale, True, c.kv_lens, sg.numpy())
+    assert torch.all(o[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    compare(o, lse, ro, rl)
+
+
+def test_fp8_accuracy_and_incoherent_processing(dev):
+    # Against the unquantized attention of the same bf16 inputs; with outlier
+    # channels shared by Q and K, the transform must cut the error at least
+    # in half (FA3 reports 2.6x against per-tensor scales on its inputs).
+    B, H, L, D = 1, 4, 1024, 128
+    g = torch.Generator().manual_seed(1401)
+    q, k, v = (torch.randn(B, H, L, D, generator=g) for _ in range(3))
+    ch = torch.randperm(D, generator=g)[:2]
+    q[..., ch] *= 10.0
+    k[..., ch] *= 10.0
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(D) / 10.0
+    ref, _ = oracle.attention_forward(q, k, v, scale, True)
+    sg = signs_of(15, D)
+    out = {}
+    for name, s in (("block", None), ("block+incoherent", sg)):
+        o, _ = binding.attention_fp8(q.to(dev), k.to(dev), v.to(dev), causal=True, scale=scale,
+                                     signs=None if s is None else s.to(dev))
+        torch.cuda.synchronize()
+        out[name] = float(np.sqrt(np.mean((o.float().cpu().numpy() - ref) ** 2)))
+    print(f"[accuracy] rmse vs unquantized attention: {out}", flush=True)
+    assert out["block+incoherent"] * 2.0 < out["block"], out
+    assert out["block+incoherent"] < 2e-2, out
+
+
+def test_fp8_full_size_sampled_rows(dev):
+    # The FP8 workload at full size in the benchmark's launch configuration:
+    # quantize with the transform, run the forward, and check sampled rows of
+    # a few heads against the oracle on the same quantized values.
+    w = W.BY_NAME["fp8_causal_b2_h16_l4096_d128"]
+    inp = W.make_inputs(w)
+    sg = inp.meta["signs"]
+    q8, qs = binding.quantize_fp8(inp.q.to(dev), binding.FP8_Q_BLOCK, sg.to(dev))
+    k8, ks = binding.quantize_fp8(inp.k.to(dev), binding.FP8_K_BLOCK, sg.to(dev))
+    eff = w.scale / w.D
+    o, lse = binding.fa_fwd_fp8(q8, k8, inp.v.to(dev), qs, ks, causal=True, scale=eff)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    for (b, h) in ((0, 0), (1, 9)):
+        rc, rsq, qv = oracle.fp8.quantize_rows(inp.q[b:b + 1, h:h + 1], binding.FP8_Q_BLOCK, sg.numpy())
+        kc, rsk, kv = oracle.fp8.quantize_rows(inp.k[b:b + 1, h:h + 1], binding.FP8_K_BLOCK, sg.numpy())
+        assert np.array_equal(q8[b, h].cpu().numpy(), rc[0, 0]) and np.array_equal(k8[b, h].cpu().numpy(), kc[0, 0])
+        rr = sample_rows(w.Lq, 1500 + b * 16 + h)
+        ro, rl = oracle.attention_rows(qv, kv, inp.v[b:b + 1, h:h + 1], eff, True, None, 0, 0, rows=rr)
+        compare(o[b, h][rr], lse[b, h][rr], ro, rl)
