@@ -60,9 +60,22 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 16-byte-chunk XOR swizzle of the backward's LDS tiles, which are read two
+// ways: one row per lane (16 lanes: 16 consecutive rows, one chunk column)
+// and by the transposing read (32 lanes: 4 consecutive rows, aligned, times 4
+// consecutive chunks, aligned).  The first needs the swizzle to be a
+// bijection on the row's low bits (bits 1..3 at D = 64, where two rows share
+// the 64 banks); the second needs the 4 rows moved to 4 (D = 128) or 2
+// (D = 64) different aligned chunk groups, i.e. swizzle bits 2 (and 3) taken
+// from the row's low bits.  Both reads are then free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int bwd_swizzle(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
 // Direct HBM -> LDS copies of a 32-row tile of a [rows, D] bf16 tensor by the
-// workgroup's NT threads into a tile buffer laid out row-major with the K
-// swizzle.  Copy i of wavefront w fills 16-byte chunk position
+// workgroup's NT threads into a tile buffer laid out row-major with
+// bwd_swizzle.  Copy i of wavefront w fills 16-byte chunk position
 // P = (w * NI + i) * 64 + lane of the buffer, so each thread reads chunk
 // (P % CH) ^ swizzle(row) of row P / CH: the fixed per-lane source offsets
 // carry the swizzle and every copy instruction writes 1 KiB of consecutive
@@ -78,7 +91,7 @@ struct TileCopy {
         for (int i = 0; i < NI; ++i) {
             const int P = (w * NI + i) * 64 + l;
             const int row = P / CH;
-            off[i] = (uint32_t)(row * D + (((P % CH) ^ k_swizzle<D>(row)) * 8)) * 2;
+            off[i] = (uint32_t)(row * D + (((P % CH) ^ bwd_swizzle<D>(row)) * 8)) * 2;
         }
     }
     __device__ __forceinline__ void issue(const bf16* src, int valid, uint32_t lds_buf, int w) const {
@@ -101,13 +114,13 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
 
-// A-operand fragment: row `row` of a K-swizzled tile, 16-byte chunk `chunk`.
+// A-operand fragment: row `row` of a swizzled tile, 16-byte chunk `chunk`.
 template <int D>
 __device__ __forceinline__ bf16x8 read_row_chunk(const bf16* tile, int row, int chunk) {
-    return *reinterpret_cast<const bf16x8*>(tile + row * D + ((chunk ^ k_swizzle<D>(row)) * 8));
+    return *reinterpret_cast<const bf16x8*>(tile + row * D + ((chunk ^ bwd_swizzle<D>(row)) * 8));
 }
 
-// Transposed fragment of a K-swizzled tile: lane l receives column
+// Transposed fragment of a swizzled tile: lane l receives column
 // col0 + (l % 32) of rows row0 + 8*(l/32) + e, e = 0..7 (the operand layout of
 // an MFMA whose k index runs down the tile's rows).  Each lane's two 8-byte
 // reads are addressed through the swizzle of their own rows.
@@ -116,8 +129,8 @@ __device__ __forceinline__ bf16x8 read_transposed(const bf16* tile, int row0, in
     const int hi = l >> 5;
     const int r = row0 + 8 * hi + ((l & 15) >> 2);
     const int col = col0 + 16 * ((l >> 4) & 1) + 4 * (l & 3);
-    const bf16* a = tile + r * D + (((col >> 3) ^ k_swizzle<D>(r)) * 8) + (col & 7);
-    const bf16* b = tile + (r + 4) * D + (((col >> 3) ^ k_swizzle<D>(r + 4)) * 8) + (col & 7);
+    const bf16* a = tile + r * D + (((col >> 3) ^ bwd_swizzle<D>(r)) * 8) + (col & 7);
+    const bf16* b = tile + (r + 4) * D + (((col >> 3) ^ bwd_swizzle<D>(r + 4)) * 8) + (col & 7);
     const bf16x4 lo = lds_read_transposed(a);
     const bf16x4 up = lds_read_transposed(b);
     bf16x8 f;
@@ -363,7 +376,7 @@ bwd_dkdv_kernel(BwdParams p) {
         for (int ks = 0; ks < KS; ++ks) {
             const uint32_t at = (uint32_t)(key * D + ks * 16 + hi * 8) * 2;
             const int row = l & 31, chunk = 2 * ks + hi;
-            const int slot = row * D + ((chunk ^ k_swizzle<D>(row)) * 8);
+            const int slot = row * D + ((chunk ^ bwd_swizzle<D>(row)) * 8);
             if (load_k) *reinterpret_cast<bf16x8*>(Kw + slot) = load16(kbuf, at);
             if (load_v) *reinterpret_cast<bf16x8*>(Vw + slot) = load16(vbuf, at);
         }
