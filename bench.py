@@ -230,7 +230,8 @@ def main():
     head = W.BY_NAME[args.workload]
     print(f"[bench] timing {head.name}: warmup {args.warmup}, steps {args.steps}", flush=True)
     rec, inp = time_workload(head, args.steps, args.warmup, dev)
-    print(f"[bench] {head.name}: {rec['ms_per_step'] * 1e3:.1f} us/step", flush=True)
+    print(f"[bench] {head.name}: {rec['ms_per_step'] * 1e3:.1f} us/step"
+          + (f", quantizing Q and K {rec['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in rec else ""), flush=True)
 
     extra = {}
     if not args.no_extra:
@@ -241,7 +242,8 @@ def main():
             r, _ = time_workload(w, steps, max(2, min(args.warmup, 5)), dev)
             extra[w.name] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
             print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.1f} us/step, "
-                  f"{r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s", flush=True)
+                  f"{r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s"
+                  + (f", quantizing Q and K {r['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in r else ""), flush=True)
 
     decode = head.Lq == 1
     value = rec["gbs"] if decode else rec["tflops"]

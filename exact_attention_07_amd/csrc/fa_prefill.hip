@@ -447,11 +447,14 @@ prefill_kernel(PrefillParams p) {
     copy_v(0);
     copy_k(2);
     copy_v(1);
-    wait_all_vector_loads();                // Q and every prologue copy
+    // Q and K(0) only: the other four tiles stream in while S(0) and P(0) are
+    // computed (vmcnt counts in issue order).
+    wait_vector_loads_until<2 * NIK + 2 * NI>();
     __syncthreads();
     score_tile(0);
     softmax_tile(0);
-    __syncthreads();                        // K(0) read by every wavefront before M(0) refills its buffer
+    wait_vector_loads_until<NIK + NI>();    // K(1) and V(0), the first matrix phase's operands
+    __syncthreads();                        // ... visible; K(0) read by every wavefront before M(0) refills its buffer
     if (grp == 1) __syncthreads();          // the second group runs one phase behind
 
     // One tile: matrix phase M(t), barrier, vector phase V(t), barrier.
