@@ -23,6 +23,14 @@ O = softmax(S + M) V with S = scale * Q K^T and M_ij = 0 for an allowed pair,
     only at the query's position or at most w - 1 positions before it (the
     page's formula is lost in extraction; this reading makes w the number of
     keys a row sees once it is w or more positions into the sequence);
+  * §12 "Programmable attention": a score may be modified before the softmax,
+    S'_ij = f(S_ij, i, j); FlashAttention 1-4 (noviorlu.github.io),
+    FlashAttention-4 point 4, names ALiBi and soft-capping as such
+    modifiers.  Neither formula is on the pages; the readings taken are
+    soft-capping S' = cap * tanh(S / cap) of the scaled score and ALiBi
+    S' = S - slope_h * |pos_i - pos_j| with one slope per query head (on
+    causal pairs |pos_i - pos_j| = pos_i - pos_j); a modifier acts before the
+    masks, so a masked pair stays -inf;
   * FlashAttention Cheat Sheet (mxino.github.io), §1 "The whole operation":
     Q [B, Hq, Lq, D], K and V [B, Hkv, Lk, D].
 
@@ -42,14 +50,16 @@ def as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None, window=0):
+def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None, window=0,
+               alibi_slope=0.0, softcap=0.0):
     """Materialised attention for one (batch, head): returns (O, LSE) in fp64.
 
     q: [Lq, D]; k: [Lk, D]; v: [Lk, Dv].  q_pos / k_pos are the absolute
     token positions of the rows (default 0..L-1); with ``causal`` a pair is
     allowed iff k_pos[j] <= q_pos[i]; with ``window`` = w > 0 a pair is
     allowed iff 0 <= q_pos[i] - k_pos[j] < w (the causal window, which is
-    causal by itself).
+    causal by itself).  ``softcap`` > 0 caps the scaled scores at +-softcap
+    (cap * tanh(S / cap)); ``alibi_slope`` subtracts slope * |q_pos - k_pos|.
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     Lq, Lk, Dv = q.shape[0], k.shape[0], v.shape[1]
@@ -60,6 +70,11 @@ def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None, window=0):
 
     # Write the whole score matrix.
     S = scale * (q @ k.T)
+    # Score modifiers, before any mask.
+    if softcap > 0:
+        S = softcap * np.tanh(S / softcap)
+    if alibi_slope != 0.0:
+        S = S - alibi_slope * np.abs(q_pos[:, None] - k_pos[None, :]).astype(np.float64)
     if causal:
         S = np.where(k_pos[None, :] > q_pos[:, None], -np.inf, S)
     if window > 0:
@@ -88,7 +103,8 @@ def _kv_len(kv_lens, b, Lk):
     return int(min(max(int(as_f64(kv_lens)[b]), 0), Lk))
 
 
-def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None, window=0):
+def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None, window=0,
+                   alibi_slopes=None, softcap=0.0):
     """(O, LSE) of selected query rows of one (b, h) of a batched problem.
 
     Rows are evaluated by the same definition as ``attention_forward``; this
@@ -104,14 +120,18 @@ def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None, window=0):
     k_bg = as_f64(k[b, g, :n])
     v_bg = as_f64(v[b, g, :n])
     q_pos = (n - Lq) + rows          # bottom-right: the queries end the cache
-    return dense_head(q_bh, k_bg, v_bg, scale, causal, q_pos, np.arange(n), window)
+    slope = 0.0 if alibi_slopes is None else float(as_f64(alibi_slopes)[h])
+    return dense_head(q_bh, k_bg, v_bg, scale, causal, q_pos, np.arange(n), window, slope, softcap)
 
 
-def attention_forward(q, k, v, scale, causal=False, kv_lens=None, window=0):
+def attention_forward(q, k, v, scale, causal=False, kv_lens=None, window=0, alibi_slopes=None,
+                      softcap=0.0):
     """Batched attention over [B, H, L, D] inputs: returns O [B, Hq, Lq, Dv]
     and LSE [B, Hq, Lq], both fp64.  ``kv_lens[b]`` (clamped to [0, Lk]) is the
     number of valid keys of sequence b; None means all Lk are valid.
-    ``window`` > 0 applies the causal window of that width."""
+    ``window`` > 0 applies the causal window of that width; ``alibi_slopes``
+    ([Hq], one per query head) and ``softcap`` are the score modifiers of
+    ``dense_head``."""
     B, Hq, Lq = q.shape[0], q.shape[1], q.shape[2]
     Hkv, Dv = k.shape[1], v.shape[3]
     assert Hq % Hkv == 0, "query heads must be a multiple of KV heads"
@@ -120,5 +140,6 @@ def attention_forward(q, k, v, scale, causal=False, kv_lens=None, window=0):
     for b in range(B):
         for h in range(Hq):
             O[b, h], lse[b, h] = attention_rows(q, k, v, scale, causal, kv_lens, b, h,
-                                                window=window)
+                                                window=window, alibi_slopes=alibi_slopes,
+                                                softcap=softcap)
     return O, lse

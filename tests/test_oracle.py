@@ -704,6 +704,66 @@ def _bf16(x):
     return torch.tensor(np.asarray(x), dtype=torch.float32).to(torch.bfloat16).double().numpy()
 
 
+def check_score_modifiers(orc):
+    # Zero slope / no cap is plain attention, bit for bit.
+    rng = np.random.default_rng(41)
+    q, k, v = rng.standard_normal((6, 8)), rng.standard_normal((11, 8)), rng.standard_normal((11, 3))
+    qp = np.arange(5, 11)
+    O0, l0 = orc.dense_head(q, k, v, 0.3, True, qp)
+    O1, l1 = orc.dense_head(q, k, v, 0.3, True, qp, alibi_slope=0.0, softcap=0.0)
+    assert np.array_equal(O0, O1) and np.array_equal(l0, l1)
+    # ALiBi closed form: identical keys give equal raw scores, so the weights
+    # are exp(-slope * distance) alone.
+    slope, pos = 0.37, 9
+    kk = np.tile(rng.standard_normal((1, 4)), (pos + 1, 1))
+    qq = rng.standard_normal((1, 4))
+    s0 = 0.5 * float(qq[0] @ kk[0])
+    w = [math.exp(-slope * (pos - j)) for j in range(pos + 1)]
+    vv = rng.standard_normal((pos + 1, 2))
+    O, lse = orc.dense_head(qq, kk, vv, 0.5, True, [pos], alibi_slope=slope)
+    exp_o = [sum(w[j] * vv[j, c] for j in range(pos + 1)) / math.fsum(w) for c in range(2)]
+    assert np.allclose(O[0], exp_o, rtol=0, atol=1e-13)
+    assert abs(lse[0] - (s0 + math.log(math.fsum(w)))) < 1e-13
+    # ALiBi against torch's SDPA with an additive bias (GQA, kv_lens, causal):
+    # query head h uses slopes[h].
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 5, 9, 6
+    g0 = torch.Generator().manual_seed(43)
+    qt = torch.randn(B, Hq, Lq, D, generator=g0, dtype=torch.float64)
+    kt = torch.randn(B, Hkv, Lk, D, generator=g0, dtype=torch.float64)
+    vt = torch.randn(B, Hkv, Lk, D, generator=g0, dtype=torch.float64)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625])
+    lens = [9, 6]
+    O, _ = orc.attention_forward(qt, kt, vt, 0.4, True, np.array(lens), alibi_slopes=slopes)
+    for b in range(B):
+        n = lens[b]
+        qpos = torch.arange(Lq, dtype=torch.float64) + (n - Lq)
+        kpos = torch.arange(n, dtype=torch.float64)
+        dist = qpos[:, None] - kpos[None, :]
+        for h in range(Hq):
+            bias = -slopes[h] * dist.abs()
+            bias = bias.masked_fill(dist < 0, float("-inf"))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qt[b, h][None], kt[b, h // 2, :n][None], vt[b, h // 2, :n][None], attn_mask=bias, scale=0.4)[0]
+            assert np.allclose(O[b, h], ref.numpy(), rtol=0, atol=1e-12)
+    # Soft-capping against pure-Python brute force (scalar tanh and exp), on
+    # large scores so the cap bites, and its limit: a huge cap is plain attention.
+    q2, k2, v2 = 3 * rng.standard_normal((3, 4)), 3 * rng.standard_normal((7, 4)), rng.standard_normal((7, 2))
+    cap = 2.5
+    O, lse = orc.dense_head(q2, k2, v2, 0.7, True, [4, 5, 6], softcap=cap)
+    for i, p_i in enumerate([4, 5, 6]):
+        sc = [cap * math.tanh(0.7 * sum(q2[i, d] * k2[j, d] for d in range(4)) / cap) for j in range(p_i + 1)]
+        m = max(sc)
+        e = [math.exp(x - m) for x in sc]
+        z = math.fsum(e)
+        assert abs(lse[i] - (m + math.log(z))) < 1e-12
+        for c in range(2):
+            assert abs(O[i, c] - math.fsum(e[j] * v2[j, c] for j in range(p_i + 1)) / z) < 1e-12
+        assert lse[i] <= cap + math.log(p_i + 1) + 1e-12
+    Oh, lh = orc.dense_head(q2, k2, v2, 0.7, True, [4, 5, 6], softcap=1e9)
+    Op, lp = orc.dense_head(q2, k2, v2, 0.7, True, [4, 5, 6])
+    assert np.allclose(Oh, Op, rtol=0, atol=1e-12) and np.allclose(lh, lp, rtol=0, atol=1e-12)
+
+
 def check_fp8_format(orc):
     # OCP E4M3 facts (FP8 formats for deep learning, OCP 8-bit floating point
     # specification): 0x7E = 448 is the largest finite value, 0x7F / 0xFF are
@@ -829,7 +889,7 @@ CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, che
           check_fully_masked_rows, check_window_closed_forms, check_window_brute_force,
           check_paged_matches_contiguous, check_paged_permutation, check_paged_invalid_entries,
           check_backward_page_experiment, check_backward_vs_autograd, check_backward_finite_differences,
-          check_backward_gqa_and_lengths, check_fp8_format, check_fp8_hadamard, check_fp8_block_scale,
+          check_backward_gqa_and_lengths, check_score_modifiers, check_fp8_format, check_fp8_hadamard, check_fp8_block_scale,
           check_fp8_attention]
 
 
@@ -868,7 +928,7 @@ MUTANTS = {
                               "return wb[:, None] * oa + wa[:, None] * ob, L")],
     "window_off_by_one": [("attention", "(dist >= window)", "(dist > window)")],
     "window_not_causal": [("attention", "(dist < 0) | (dist >= window)", "(dist >= window)")],
-    "window_not_passed": [("attention", "np.arange(n), window)", "np.arange(n), 0)")],
+    "window_not_passed": [("attention", "np.arange(n), window, slope, softcap)", "np.arange(n), 0, slope, softcap)")],
     "page_offset_swapped": [("paged", "cache[page, :, t % page_size, :]", "cache[page, :, t // page_size, :]")],
     "page_index_mod": [("paged", "page = table[b, t // page_size]", "page = table[b, t % page_size]")],
     "paged_positions_compacted": [("paged", "positions.append(t)", "positions.append(len(positions))")],
@@ -885,6 +945,11 @@ MUTANTS = {
     "bwd_causal_dropped": [("backward", "allowed &= k_pos[None, :] <= q_pos[:, None]", "allowed &= True")],
     "bwd_top_left": [("backward", "q_pos = (n - Lq) + np.arange(Lq)", "q_pos = np.arange(Lq)")],
     "bwd_window_off_by_one": [("backward", "(dist < window)", "(dist <= window)")],
+    "alibi_sign": [("attention", "S = S - alibi_slope * np.abs", "S = S + alibi_slope * np.abs")],
+    "alibi_signed_distance": [("attention", "np.abs(q_pos[:, None] - k_pos[None, :])", "(k_pos[None, :] - q_pos[:, None])")],
+    "alibi_head_map": [("attention", "float(as_f64(alibi_slopes)[h])", "float(as_f64(alibi_slopes)[h // r])")],
+    "softcap_unscaled": [("attention", "S = softcap * np.tanh(S / softcap)", "S = np.tanh(S / softcap)")],
+    "softcap_dropped": [("attention", "S = softcap * np.tanh(S / softcap)", "S = S")],
     "fp8_ties_away": [("fp8", "mag = np.rint(a / spacing) * spacing", "mag = np.floor(a / spacing + 0.5) * spacing")],
     "fp8_no_subnormals": [("fp8", "binade = np.maximum(E - 1, -6)", "binade = E - 1")],
     "fp8_bias_off": [("fp8", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)")],
