@@ -11,7 +11,9 @@ workload under a causal window of 4096 keys; the decode workload served from
 a shuffled paged cache with 16-token pages; the backward of the causal 4K and
 1K prefill workloads, one fa_bwd call per step; the causal 4K and GQA 16K
 forward with FP8 scores, one fa_fwd_fp8 call per step on Q and K quantized
-beforehand, the quantization timed separately), are timed the same way and
+beforehand, the quantization timed separately; the causal 4K forward with
+ALiBi biases and the 1K prefill with soft-capped scores, one fa_fwd_mod call
+per step), are timed the same way and
 reported under "workloads".  Time is taken with HIP events on the stream the kernels are
 launched on (torch's current stream), bracketed by device synchronisation.
 
@@ -87,6 +89,11 @@ def time_workload(w, steps, warmup, dev):
         fwd()                                   # the forward's o and lse are the backward's inputs
         call = binding.PreparedBwdCall(q, k, v, o, lse, inp.meta["dout"].to(dev), causal=w.causal,
                                        window=w.window, scale=w.scale, kv_lens=kl)
+    elif w.alibi or w.softcap:
+        k, v = inp.k.to(dev), inp.v.to(dev)
+        sl = inp.meta["alibi_slopes"].to(dev) if w.alibi else None
+        call = binding.PreparedModCall(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=kl,
+                                       alibi_slopes=sl, softcap=w.softcap)
     elif w.fp8:
         # Q and K quantized (after the random-sign Hadamard transform) before
         # timing, as an FP8 cache would hold them; the step is one fa_fwd_fp8.

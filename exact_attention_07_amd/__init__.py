@@ -6,7 +6,7 @@ the first call into the library loads it and raises if it has not been built.
 """
 _EXPORTS = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_bwd", "fa_workspace_bytes",
             "fa_status_string", "load_library", "FaError", "PreparedCall", "PreparedPagedCall",
-            "PreparedBwdCall", "quantize_fp8", "fa_fwd_fp8", "attention_fp8", "PreparedFp8Call")
+            "PreparedBwdCall", "fa_fwd_mod", "PreparedModCall", "quantize_fp8", "fa_fwd_fp8", "attention_fp8", "PreparedFp8Call")
 
 
 def __getattr__(name):

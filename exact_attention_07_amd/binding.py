@@ -21,7 +21,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every entry point declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_bwd",
-            "fa_quantize_fp8", "fa_fwd_fp8",
+            "fa_fwd_mod", "fa_quantize_fp8", "fa_fwd_fp8",
             "fa_workspace_bytes", "fa_status_string", "fa_last_error")
 
 # Block sizes of the FP8 forward's scales (query rows, keys).
@@ -63,6 +63,9 @@ def load_library(path: Optional[str] = None):
     # q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, causal, window, scale, kv_lens, stream
     lib.fa_bwd.argtypes = [vp] * 9 + [i32] * 8 + [f32, vp, vp]
     lib.fa_bwd.restype = i32
+    # q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, causal, scale, kv_lens, alibi_slopes, softcap, stream
+    lib.fa_fwd_mod.argtypes = fwd_args[:14] + [vp, f32, vp]
+    lib.fa_fwd_mod.restype = i32
     # x, x8, scales, heads, L, D, block_rows, signs, stream
     lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
     lib.fa_quantize_fp8.restype = i32
@@ -393,6 +396,52 @@ class PreparedFp8Call:
         self._args = (_ptr(q8), _ptr(k8), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_scales), _ptr(k_scales),
                       B, Hq, Hkv, Lq, Lk, D, int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), s)
         self()
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+        return self.o, self.lse
+
+
+def _mod_args(q, alibi_slopes, softcap):
+    Hq = q.shape[1]
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq
+                                     or alibi_slopes.device != q.device or not alibi_slopes.is_contiguous()):
+        raise ValueError("alibi_slopes must be a contiguous fp32 device tensor of Hq entries")
+    return _ptr(alibi_slopes), float(softcap)
+
+
+def fa_fwd_mod(q, k, v, o=None, lse=None, *, causal=False, scale=None, kv_lens=None, alibi_slopes=None,
+               softcap=0.0, stream=None, want_lse=True):
+    """Attention with a score modifier through ``fa_fwd_mod``: ALiBi
+    (``alibi_slopes``, [Hq] fp32) or soft-capping (``softcap`` > 0).
+    Returns (o, lse)."""
+    o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    sp, cap = _mod_args(q, alibi_slopes, softcap)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    _check(load_library().fa_fwd_mod(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk, D,
+                                      int(bool(causal)), scale, _ptr(kv_lens), sp, cap, s))
+    return o, lse
+
+
+class PreparedModCall:
+    """fa_fwd_mod with its arguments checked and marshalled once (see PreparedCall)."""
+
+    def __init__(self, q, k, v, o=None, lse=None, *, causal=False, scale=None, kv_lens=None,
+                 alibi_slopes=None, softcap=0.0, stream=None):
+        o, lse = fa_fwd_mod(q, k, v, o, lse, causal=causal, scale=scale, kv_lens=kv_lens,
+                            alibi_slopes=alibi_slopes, softcap=softcap, stream=stream)
+        B, Hq, Lq, D = q.shape
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        sp, cap = _mod_args(q, alibi_slopes, softcap)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        self.o, self.lse = o, lse
+        self._keep = (q, k, v, o, lse, kv_lens, alibi_slopes)
+        self._fn = load_library().fa_fwd_mod
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, k.shape[1], Lq, k.shape[2], D,
+                      int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), sp, ctypes.c_float(cap), s)
 
     def __call__(self):
         status = self._fn(*self._args)

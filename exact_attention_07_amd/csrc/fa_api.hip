@@ -351,6 +351,45 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     return FA_OK;
 }
 
+int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+               const int* kv_lens, const float* alibi_slopes, float softcap, void* stream) {
+    g_last_error[0] = '\0';
+    const Shape s{B, Hq, Hkv, Lq, Lk, D};
+    int st = validate(q, k, v, o, lse, s, causal, scale, kv_lens);
+    if (st != FA_OK) return st;
+    if (!(softcap >= 0.0f) || !std::isfinite(softcap))
+        return fail(FA_ERR_INVALID_ARG, "softcap must be finite and >= 0");
+    if (alibi_slopes && softcap > 0.0f)
+        return fail(FA_ERR_INVALID_ARG, "give ALiBi slopes or a soft-cap, not both");
+    if (!aligned(alibi_slopes, 4)) return fail(FA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
+    if (!alibi_slopes && softcap == 0.0f)       // no modifier: the plain forward
+        return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, causal, scale, kv_lens, stream);
+    fa::PrefillParams p;
+    p.q = static_cast<const __bf16*>(q);
+    p.k = static_cast<const __bf16*>(k);
+    p.v = static_cast<const __bf16*>(v);
+    p.o = static_cast<__bf16*>(o);
+    p.lse = lse; p.kv_lens = kv_lens;
+    p.q8 = nullptr; p.k8 = nullptr; p.q_scale = nullptr; p.k_scale = nullptr;
+    p.alibi_slopes = alibi_slopes;
+    p.softcap = softcap;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk;
+    p.r = Hq / Hkv;
+    p.n_qblocks = (Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+    const int units = B * Hkv;
+    p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+    p.window = 0;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    const long long total = (long long)B * Hq * p.n_qblocks;
+    if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    hipError_t e = fa::launch_prefill_mod(D, causal != 0, alibi_slopes ? 1 : 2, p,
+                                          reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
 int fa_quantize_fp8(const void* x, void* x8, float* scales, int heads, int L, int D,
                     int block_rows, const float* signs, void* stream) {
     g_last_error[0] = '\0';

@@ -33,10 +33,14 @@ struct PrefillParams {
     float c;               // scale * log2(e): scores enter exp2 as s * c
     // FP8 instantiation only: E4M3 codes of Q [B, Hq, Lq, D] and K [B, Hkv, Lk, D]
     // with their block scales [B, Hq, ceil(Lq / 256)] and [B, Hkv, ceil(Lk / 64)].
-    const uint8_t* q8;
-    const uint8_t* k8;
-    const float* q_scale;
-    const float* k_scale;
+    const uint8_t* q8 = nullptr;
+    const uint8_t* k8 = nullptr;
+    const float* q_scale = nullptr;
+    const float* k_scale = nullptr;
+    // Score modifiers (the modifier instantiations only): ALiBi slopes [Hq]
+    // and the soft-cap of the scaled scores.
+    const float* alibi_slopes = nullptr;
+    float softcap = 0.0f;
 };
 
 struct QuantParams {
@@ -108,6 +112,8 @@ hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_
 // The prefill with E4M3 Q and K (D = 128): p.q8, p.k8 and the scales replace p.q and p.k.
 hipError_t launch_prefill_fp8(bool causal, const PrefillParams& p, hipStream_t stream);
 hipError_t launch_quantize_fp8(int D, const QuantParams& p, hipStream_t stream);
+// The prefill with a score modifier: mod 1 = ALiBi (p.alibi_slopes), 2 = soft-cap (p.softcap).
+hipError_t launch_prefill_mod(int D, bool causal, int mod, const PrefillParams& p, hipStream_t stream);
 hipError_t launch_splitkv(int D, bool paged, const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
 // The dq kernel (which also writes delta) then the dk/dv kernel.

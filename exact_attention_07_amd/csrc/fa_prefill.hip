@@ -95,7 +95,17 @@ struct ScoreOperand { typedef bf16x8 type; };
 template <>
 struct ScoreOperand<true> { typedef i32x8 type; };
 
-template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false>
+// Score modifiers (FlashAttention from Scratch, section 12: S' = f(S, i, j)
+// before the softmax), applied to the tile's raw scores before the masks, in
+// the units the exponent uses (x = s c - r):
+//   MOD 1, ALiBi:     s -= (slope_h / scale) |pos_i - pos_j|
+//   MOD 2, soft-cap:  s  = (cap / scale) tanh(s scale / cap)
+//                        = (cap / scale) (1 - 2 / (1 + 2^(s 2 scale log2(e) / cap)))
+// (an exponential and a reciprocal per score; 2^(large) = inf gives 1, and
+// 2^(-large) = 0 gives -1).
+constexpr int kModNone = 0, kModAlibi = 1, kModSoftcap = 2;
+
+template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false, int MOD = kModNone>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
     constexpr int NW = 8;                   // wavefronts: two groups of four
@@ -113,6 +123,7 @@ prefill_kernel(PrefillParams p) {
     static_assert(NI >= 1 && (BN * CH) % NT == 0, "a tile must split evenly over the workgroup");
     static_assert(CAUSAL || !WINDOW, "the window is causal");
     static_assert(!FP8 || (D == 128 && !WINDOW), "the FP8 scores are built for D = 128 without a window");
+    static_assert(MOD == kModNone || (!FP8 && !WINDOW), "score modifiers are built for the bf16 kernel without a window");
     constexpr int KSQ = FP8 ? D / 64 : KS;  // k-steps of S^T
     constexpr int NIK = FP8 ? BN * D / (NT * 16) : NI;   // 16-byte copies per thread per K tile
     static_assert(NIK >= 1, "a K tile must split evenly over the workgroup");
@@ -298,6 +309,10 @@ prefill_kernel(PrefillParams p) {
     float pe[KB][2][8];
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     float ksc_next = k_scale_of(0);         // FP8: s_k of the tile softmax_tile handles next
+    // Modifier constants in raw-score units.
+    const float mod_a = MOD == kModAlibi ? p.alibi_slopes[h] / p.scale
+                      : MOD == kModSoftcap ? p.softcap / p.scale : 0.0f;   // slope, or cap
+    const float mod_b = MOD == kModSoftcap ? 2.0f * p.scale * 1.4426950408889634f / p.softcap : 0.0f;
 
     // Vector phase for tile t (scores in s): mask where needed, p -> pe and the
     // fp32 row sum, and the rare reference move.
@@ -305,6 +320,23 @@ prefill_kernel(PrefillParams p) {
         const int k0 = (tb + t) * BN;
         const float ct = FP8 ? cq * ksc_next : c;   // this tile's exponent scale
         if (FP8) ksc_next = k_scale_of(t + 1);
+        if constexpr (MOD == kModAlibi) {
+            // |pos_i - pos_j| = |(qpos - k0 - 8 hi) - (32 kb + 16 (v / 8) + v % 8)|
+            const float base = (float)(qrow + off - k0 - 8 * hi);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    s[kb][v] = __builtin_fmaf(-mod_a, fabsf(base - (float)(kb * 32 + 16 * (v >> 3) + (v & 7))), s[kb][v]);
+        } else if constexpr (MOD == kModSoftcap) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float e = exp2_fast(s[kb][v] * mod_b);
+                    s[kb][v] = __builtin_fmaf(-2.0f * mod_a, __builtin_amdgcn_rcpf(1.0f + e), mod_a);
+                }
+        }
         // Elementwise masks only where some pair of this wavefront's rows and
         // the tile is out: past n, above the diagonal, or (window) at least w
         // positions before the wavefront's last row.
@@ -517,6 +549,25 @@ hipError_t launch_prefill_fp8(bool causal, const PrefillParams& p, hipStream_t s
     const dim3 grid((unsigned)total), block(512);
     if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, false, true>), grid, block, 0, stream, p);
     else        hipLaunchKernelGGL((prefill_kernel<128, false, false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int MOD>
+void launch_prefill_mod_d(bool causal, const PrefillParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+    if (causal) hipLaunchKernelGGL((prefill_kernel<D, true, false, false, MOD>), grid, block, 0, stream, p);
+    else        hipLaunchKernelGGL((prefill_kernel<D, false, false, false, MOD>), grid, block, 0, stream, p);
+}
+
+hipError_t launch_prefill_mod(int D, bool causal, int mod, const PrefillParams& p, hipStream_t stream) {
+    const long long total = (long long)p.B * p.Hq * p.n_qblocks;
+    const dim3 grid((unsigned)total), block(512);
+    if (D == 64) {
+        if (mod == kModAlibi) launch_prefill_mod_d<64, kModAlibi>(causal, p, grid, block, stream);
+        else                  launch_prefill_mod_d<64, kModSoftcap>(causal, p, grid, block, stream);
+    } else {
+        if (mod == kModAlibi) launch_prefill_mod_d<128, kModAlibi>(causal, p, grid, block, stream);
+        else                  launch_prefill_mod_d<128, kModSoftcap>(causal, p, grid, block, stream);
+    }
     return hipGetLastError();
 }
 

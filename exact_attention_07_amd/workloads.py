@@ -57,6 +57,8 @@ class Workload:
     page_size: int = 0          # > 0: K and V are served from a paged cache
     backward: bool = False      # time the backward (fa_bwd) instead of the forward
     fp8: bool = False           # FP8 scores: Q, K block-quantized after the random-sign Hadamard transform
+    alibi: bool = False         # ALiBi score modifier, slopes 2^(-8 (h + 1) / Hq)
+    softcap: float = 0.0        # soft-cap score modifier (0 = none)
 
     @property
     def seed(self) -> int:
@@ -91,6 +93,10 @@ WORKLOADS = [
              description="backward of the causal prefill forward"),
     Workload("bwd_prefill_b4_h16_l1024_d64", 4, 16, 16, 1024, 1024, 64, False, 1, backward=True,
              description="backward of the prefill forward, no mask"),
+    Workload("alibi_causal_b2_h16_l4096_d128", 2, 16, 16, 4096, 4096, 128, True, 2, alibi=True,
+             description="causal prefill forward with ALiBi score biases"),
+    Workload("softcap_prefill_b4_h16_l1024_d64", 4, 16, 16, 1024, 1024, 64, False, 1, softcap=20.0,
+             description="prefill forward with soft-capped scores (cap 20)"),
     Workload("fp8_causal_b2_h16_l4096_d128", 2, 16, 16, 4096, 4096, 128, True, 2, fp8=True,
              description="causal prefill forward with FP8 scores (block scales, incoherent processing)"),
     Workload("fp8_gqa_causal_b1_hq32_hkv8_l16384_d128", 1, 32, 8, 16384, 16384, 128, True, 3,
@@ -130,6 +136,13 @@ def make_inputs(w: Workload) -> Inputs:
                                    dtype=torch.float32).to(torch.bfloat16)
     if w.window:
         meta["window"] = w.window
+    if w.alibi:
+        # The geometric slopes of the ALiBi construction (not on the pages; a
+        # synthetic choice), one per query head.
+        meta["alibi_slopes"] = torch.tensor([2.0 ** (-8.0 * (h + 1) / w.Hq) for h in range(w.Hq)],
+                                            dtype=torch.float32)
+    if w.softcap:
+        meta["softcap"] = w.softcap
     if w.fp8:
         # The random signs of the incoherent-processing transform, drawn after the base inputs.
         meta["signs"] = (torch.randint(0, 2, (w.D,), generator=g) * 2 - 1).to(torch.float32)

@@ -164,6 +164,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int causal, int window, float scale, const int* kv_lens, void* stream);
 
 /*
+ * Attention forward with a score modifier (FlashAttention from Scratch,
+ * section 12 "Programmable attention": S'_ij = f(S_ij, i, j) before the
+ * softmax; FlashAttention 1-4, FlashAttention-4 point 4 names ALiBi and
+ * soft-capping).  fa_fwd's operation with S = scale * q.k replaced by
+ *     ALiBi     (alibi_slopes != NULL): S - alibi_slopes[h] * |pos_i - pos_j|
+ *     soft-cap  (softcap > 0):          softcap * tanh(S / softcap)
+ * with the absolute positions of fa_fwd's causal alignment (query i at
+ * n_b - Lq + i, key j at j); the masks act after the modifier.  At most one
+ * modifier per call; with neither this is fa_fwd.
+ *   alibi_slopes: fp32, device, [Hq] (one per query head), 4-byte aligned
+ *   softcap: finite, >= 0 (0 = none)
+ * Other arguments, layouts and errors as for fa_fwd (no window; every Lq
+ * runs the prefill kernel).  FA_ERR_INVALID_ARG also for both modifiers at
+ * once or a negative or non-finite softcap.
+ */
+int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+               const int* kv_lens, const float* alibi_slopes, float softcap, void* stream);
+
+/*
  * FP8 block quantization with optional incoherent processing (FlashAttention
  * from Scratch, section 10.3 "Treat FP8 as a second lesson"; FlashAttention
  * 1-4, FlashAttention-3 point 3: one FP8 scale per tile, and Q and K

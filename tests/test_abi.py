@@ -244,3 +244,25 @@ def test_fp8_binding_requires_gpu_tensors():
     with pytest.raises(ValueError):
         binding._prepare_fp8(x.to(torch.uint8), x.to(torch.uint8), x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1),
                              None, None, None, True)
+
+
+def call_mod(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Lq=4, Lk=8, D=64, causal=0,
+             scale=0.125, kv_lens=None, slopes=None, softcap=0.0):
+    return lib.fa_fwd_mod(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, causal, ctypes.c_float(scale),
+                          kv_lens, slopes, ctypes.c_float(softcap), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(slopes=P, softcap=2.0), binding.FA_ERR_INVALID_ARG),     # both modifiers
+    (dict(softcap=-1.0), binding.FA_ERR_INVALID_ARG),
+    (dict(softcap=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(softcap=float("inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(slopes=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(slopes=P, D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(softcap=1.0, q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(softcap=1.0, scale=0.0), binding.FA_ERR_INVALID_ARG),
+])
+def test_fwd_mod_validation(lib, kw, status):
+    got = call_mod(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
