@@ -338,6 +338,9 @@ bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) bf16 gt[2 * TILE];
     __shared__ __attribute__((aligned(16))) float stat[2 * 64];   // per stage: L2 [0, 32), delta [32, 64)
     __shared__ __attribute__((aligned(16))) bf16 kvres[4 * 2 * TILE];  // K and V of the four key blocks
+    // Split roles: P of each key block, passed from its dV wavefront to its
+    // dK wavefront (entry-major: chunk c of lane l at ((kblk 4 + c) 64 + l) 4).
+    __shared__ __attribute__((aligned(16))) float pshare[SPLIT ? 4 * 16 * 64 : 4];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -427,7 +430,10 @@ bwd_dkdv_kernel(BwdParams p) {
         if (w == 0) stat[(f & 1) * 64 + l] = st_next;
         __syncthreads();                        // tile f visible; every wavefront is done with tile f - 1
         if (f + 1 < total) issue(f + 1);        // into the stage of tile f - 1
-        if (k0 >= n) continue;                  // this wavefront's keys are all past n
+        if (k0 >= n) {                          // this wavefront's keys are all past n
+            if (SPLIT) __syncthreads();         // ... but the P hand-over barrier is the workgroup's
+            continue;
+        }
         const int hh = f / nqt;
         const int q0 = q_first + (f - hh * nqt) * 32;
         const bf16* Qs = qt + (f & 1) * TILE;
@@ -437,18 +443,22 @@ bwd_dkdv_kernel(BwdParams p) {
         // Elementwise masks only on tiles where some pair is out (wave-uniform).
         const bool need = (q0 + 32 > p.Lq) || (k0 + 32 > n) || (p.causal && k0 + 31 > q0 + off) ||
                           (p.window > 0 && q0 + 31 + off - k0 >= p.window);
-        // One tile for one role: S (and dP for dK), the elementwise step, then
-        // the dV and/or dK products.  WITH_DK: also dP, dS and dK += dS^T Q;
-        // WITH_DV: dV += P^T G.  Each role is its own straight-line code.
-        auto tile = [&](auto with_dk, auto with_dv) __attribute__((always_inline)) {
-            constexpr bool WDK = decltype(with_dk)::value != 0;
-            constexpr bool WDV = decltype(with_dv)::value != 0;
-            // S (even steps) and dP (odd steps when WDK), two fragments each.
-            constexpr int NOP = WDK ? 2 * KS : KS;
+        // One tile for one role, each its own straight-line code.
+        //   ROLE 0 (D = 64, both): S and dP, P, dV += P^T G, dS, dK += dS^T Q.
+        //   ROLE 1 (dV, w < 4):    S, P (to LDS), barrier, dV += P^T G.
+        //   ROLE 2 (dK, w >= 4):   dP, barrier, P (from LDS), dS, dK += dS^T Q.
+        // The split roles form S once per key block and run two products each.
+        auto tile = [&](auto role_tag) __attribute__((always_inline)) {
+            constexpr int ROLE = decltype(role_tag)::value;
+            constexpr bool DO_S = ROLE != 2, DO_DP = ROLE != 1;
+            constexpr bool WDV = ROLE != 2, WDK = ROLE != 1;
+            // S and dP steps (interleaved when both), one fragment pair each.
+            constexpr int NOP = (DO_S ? KS : 0) + (DO_DP ? KS : 0);
             bf16x8 fa[NOP], fb[NOP];
+            auto is_dp_step = [&](int i) { return DO_S && DO_DP ? (i & 1) != 0 : DO_DP; };
             auto rd = [&](int i) __attribute__((always_inline)) {
-                const bool is_dp = WDK && (i & 1);
-                const int ks = WDK ? i / 2 : i;
+                const bool is_dp = is_dp_step(i);
+                const int ks = DO_S && DO_DP ? i / 2 : i;
                 fa[i] = read_row_chunk<D>(is_dp ? Gs : Qs, qrow, 2 * ks + hi);
                 fb[i] = read_row_chunk<D>(is_dp ? Vw : Kw, l & 31, 2 * ks + hi);
             };
@@ -458,8 +468,8 @@ bwd_dkdv_kernel(BwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < NOP; ++i) {
-                if (WDK && (i & 1)) dp = mfma_32x32x16(fa[i], fb[i], dp);
-                else                s = mfma_32x32x16(fa[i], fb[i], s);
+                if (is_dp_step(i)) dp = mfma_32x32x16(fa[i], fb[i], dp);
+                else               s = mfma_32x32x16(fa[i], fb[i], s);
                 if (i + kAhead < NOP) rd(i + kAhead);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -475,31 +485,48 @@ bwd_dkdv_kernel(BwdParams p) {
             // Entry v of this lane holds query q0 + 16*(v/8) + 8*hi + (v%8):
             // its L2 and delta are St[8 hi + (v%8) (+16 for v >= 8)] and
             // St[32 + ...].
-            float x[16];
+            float pr[16];
+            if (DO_S) {
+                float x[16];
 #pragma unroll
-            for (int half = 0; half < 2; ++half)
+                for (int half = 0; half < 2; ++half)
 #pragma unroll
-                for (int qd = 0; qd < 2; ++qd) {
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
+                    for (int qd = 0; qd < 2; ++qd) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int v = 8 * half + 4 * qd + e;
-                        x[v] = __builtin_fmaf(s[v], c2, -a[e]);
+                        for (int e = 0; e < 4; ++e) {
+                            const int v = 8 * half + 4 * qd + e;
+                            x[v] = __builtin_fmaf(s[v], c2, -a[e]);
+                        }
+                    }
+                if (need) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
+                        const int qpos = i + off;
+                        const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
+                                        ((p.window == 0) | (qpos - key < p.window));
+                        x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
                     }
                 }
-            if (need) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                    const int qpos = i + off;
-                    const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
-                                    ((p.window == 0) | (qpos - key < p.window));
-                    x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+                for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(x[v]);
+            }
+            f32x4* pbuf = reinterpret_cast<f32x4*>(pshare) + kblk * 4 * 64 + l;
+            if (ROLE == 1) {                    // hand P to the dK wavefront of this key block
+#pragma unroll
+                for (int c = 0; c < 4; ++c) pbuf[c * 64] = f32x4{pr[4 * c], pr[4 * c + 1], pr[4 * c + 2], pr[4 * c + 3]};
+                __syncthreads();
+            }
+            if (ROLE == 2) {
+                __syncthreads();
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const f32x4 pv = pbuf[c * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pr[4 * c + e] = pv[e];
                 }
             }
-            float pr[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(x[v]);
             if (WDV) {
                 const bf16x8 pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
                 const bf16x8 pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
@@ -532,9 +559,9 @@ bwd_dkdv_kernel(BwdParams p) {
                 }
             }
         };
-        if (!SPLIT) tile(Tag<1>{}, Tag<1>{});
-        else if (w >= 4) tile(Tag<1>{}, Tag<0>{});
-        else tile(Tag<0>{}, Tag<1>{});
+        if (!SPLIT) tile(Tag<0>{});
+        else if (w >= 4) tile(Tag<2>{});
+        else tile(Tag<1>{});
     }
 
     // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
