@@ -149,11 +149,12 @@ def test_fp8_accuracy_and_incoherent_processing(dev):
     assert out["block+incoherent"] < 2e-2, out
 
 
-def test_fp8_full_size_sampled_rows(dev):
-    # The FP8 workload at full size in the benchmark's launch configuration:
+@pytest.mark.parametrize("name", ["fp8_causal_b2_h16_l4096_d128", "fp8_gqa_causal_b1_hq32_hkv8_l16384_d128"])
+def test_fp8_full_size_sampled_rows(dev, name):
+    # The FP8 workloads at full size in the benchmark's launch configuration:
     # quantize with the transform, run the forward, and check sampled rows of
     # a few heads against the oracle on the same quantized values.
-    w = W.BY_NAME["fp8_causal_b2_h16_l4096_d128"]
+    w = W.BY_NAME[name]
     inp = W.make_inputs(w)
     sg = inp.meta["signs"]
     q8, qs = binding.quantize_fp8(inp.q.to(dev), binding.FP8_Q_BLOCK, sg.to(dev))
@@ -162,10 +163,12 @@ def test_fp8_full_size_sampled_rows(dev):
     o, lse = binding.fa_fwd_fp8(q8, k8, inp.v.to(dev), qs, ks, causal=True, scale=eff)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
-    for (b, h) in ((0, 0), (1, 9)):
+    r = w.Hq // w.Hkv
+    for (b, h) in ((0, 0), (w.B - 1, 9)):
+        g = h // r
         rc, rsq, qv = oracle.fp8.quantize_rows(inp.q[b:b + 1, h:h + 1], binding.FP8_Q_BLOCK, sg.numpy())
-        kc, rsk, kv = oracle.fp8.quantize_rows(inp.k[b:b + 1, h:h + 1], binding.FP8_K_BLOCK, sg.numpy())
-        assert np.array_equal(q8[b, h].cpu().numpy(), rc[0, 0]) and np.array_equal(k8[b, h].cpu().numpy(), kc[0, 0])
+        kc, rsk, kv = oracle.fp8.quantize_rows(inp.k[b:b + 1, g:g + 1], binding.FP8_K_BLOCK, sg.numpy())
+        assert np.array_equal(q8[b, h].cpu().numpy(), rc[0, 0]) and np.array_equal(k8[b, g].cpu().numpy(), kc[0, 0])
         rr = sample_rows(w.Lq, 1500 + b * 16 + h)
-        ro, rl = oracle.attention_rows(qv, kv, inp.v[b:b + 1, h:h + 1], eff, True, None, 0, 0, rows=rr)
+        ro, rl = oracle.attention_rows(qv, kv, inp.v[b:b + 1, g:g + 1], eff, True, None, 0, 0, rows=rr)
         compare(o[b, h][rr], lse[b, h][rr], ro, rl)
