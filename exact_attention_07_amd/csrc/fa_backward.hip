@@ -35,17 +35,19 @@
 // The wavefront also forms delta_i = G_i . O_i for its queries (one dot
 // product per lane pair) and stores it for the second kernel.
 //
-// dk/dv kernel: one workgroup per (batch, KV head, 128 keys), each wavefront
-// working on 32 of them.  K and V of the workgroup's keys stay in LDS and
-// enter S and dP as B operands; the workgroup visits every query tile of every query head that
-// reads this KV head (section 9.2's grouping, so the GQA sum happens in
-// registers) and skips tiles no query of which can see its keys (causal,
-// window).  Per shared 32-query tile (Q, G, and the rows' LSE and delta):
-// S = Q K^T and dP = G V^T with the query rows fed through the bit-2/3
-// swap, which makes the P and dS accumulators, rounded to bf16, exactly the A
-// operands of dV += P^T G and dK += dS^T Q; G and Q enter those as B operands
-// through the transposing LDS read.  Keys past a sequence's valid length get
-// zero gradient.
+// dk/dv kernels: one workgroup per (batch, KV head, 128 keys), each
+// wavefront working on 32 of them.  The workgroup visits every query tile of
+// every query head that reads this KV head (section 9.2's grouping, so the
+// GQA sum happens in registers) and skips tiles no query of which can see its
+// keys (causal, window).  Per shared 32-query tile (Q, G, and the rows' LSE
+// and delta): S = Q K^T and dP = G V^T with the query rows fed through the
+// bit-2/3 swap, which makes the P and dS accumulators, rounded to bf16,
+// exactly the A operands of dV += P^T G and dK += dS^T Q; G and Q enter those
+// as B operands through the transposing LDS read.  Keys past a sequence's
+// valid length get zero gradient.  D = 64 (bwd_dkdv_kernel): four
+// wavefronts, each with both accumulators, K and V in LDS.  D = 128
+// (bwd_dkdv_split_kernel): eight wavefronts in a dV and a dK role, pipelined
+// one tile apart (see there).
 //
 // Exponentials are base 2 with the scale folded in: p = 2^(s c2 - L2) with
 // c2 = c log2(e) and L2 = LSE log2(e); a row with LSE = -inf (no allowed key)
@@ -101,8 +103,6 @@ struct TileCopy {
     }
 };
 
-template <int N>
-struct Tag { static constexpr int value = N; };
 
 // Products per pipeline step are issued AHEAD steps after their operands'
 // LDS reads, with a scheduling fence after every step so the compiler keeps
@@ -313,42 +313,26 @@ bwd_dq_kernel(BwdParams p) {
 
 // D = 64: four wavefronts, each accumulating both dK and dV of its 32 keys
 // (two wavefronts per SIMD fit with every accumulator in ordinary VGPRs).
-// D = 128: dK and dV of 32 keys alone would take 128 registers, so the work
-// is split by role: eight wavefronts, wavefront w owning key block w % 4 --
-// w < 4 accumulates dV (products S and P^T G), w >= 4 accumulates dK
-// (products S, dP and dS^T Q), both from the same shared tiles.  Waves w and
-// w + 4 share a SIMD; S is formed twice per key block (40 products per tile
-// instead of 32) in exchange for no register spilling and two wavefronts per
-// SIMD.
+// D = 128, where dK and dV of 32 keys alone would take 128 registers, runs
+// bwd_dkdv_split_kernel below.
 template <int D>
-struct DkdvShape {
-    static constexpr bool SPLIT = D == 128;
-    static constexpr int NT = SPLIT ? 512 : 256;
-};
-
-template <int D>
-__global__ void __launch_bounds__(DkdvShape<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdParams p) {
+    static_assert(D == 64, "D = 128 runs bwd_dkdv_split_kernel");
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE = 32 * D;
-    constexpr bool SPLIT = DkdvShape<D>::SPLIT;
-    constexpr int NT = DkdvShape<D>::NT;
+    constexpr int NT = 256;
     __shared__ __attribute__((aligned(16))) bf16 qt[2 * TILE];
     __shared__ __attribute__((aligned(16))) bf16 gt[2 * TILE];
     __shared__ __attribute__((aligned(16))) float stat[2 * 64];   // per stage: L2 [0, 32), delta [32, 64)
     __shared__ __attribute__((aligned(16))) bf16 kvres[4 * 2 * TILE];  // K and V of the four key blocks
-    // Split roles: P of each key block, passed from its dV wavefront to its
-    // dK wavefront (entry-major: chunk c of lane l at ((kblk 4 + c) 64 + l) 4).
-    __shared__ __attribute__((aligned(16))) float pshare[SPLIT ? 4 * 16 * 64 : 4];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
     const int hi = l >> 5;
     const int kblk = w & 3;                     // this wavefront's 32-key block
-    const bool do_dv = !SPLIT || w < 4;
-    const bool do_dk = !SPLIT || w >= 4;
     const int nbg = p.B * p.Hkv;
     const int kb = blockIdx.x / nbg;            // first key blocks first
     const int bg = blockIdx.x - kb * nbg;       // b * Hkv + g; on XCD bg % 8 when nbg % 8 == 0
@@ -361,18 +345,17 @@ bwd_dkdv_kernel(BwdParams p) {
     const int key = k0 + (l & 31);              // this lane's key (accumulator column of S, dP)
     const size_t kvoff = (size_t)bg * p.Lk * D;
 
-    f32x16 acc[DB], acc2[SPLIT ? 1 : DB];       // dV (or dK for w >= 4 when split); dK when not split
+    f32x16 acc[DB], acc2[DB];                   // dV, dK
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
 #pragma unroll
-    for (int db = 0; db < (SPLIT ? 1 : DB); ++db) acc2[db] = zero_f32x16();
+    for (int db = 0; db < DB; ++db) acc2[db] = zero_f32x16();
 
     // K and V of each key block (keys past n read as zero) in LDS, read as B
     // operands: lane l takes row l % 32, chunk 2 ks + hi.
     bf16* Kw = kvres + kblk * 2 * TILE;
     bf16* Vw = Kw + TILE;
     {
-        const bool load_k = !SPLIT || w < 4, load_v = !SPLIT || w >= 4;
         const rsrc_t kbuf = make_rsrc(p.k + kvoff, (uint32_t)n * D * 2);
         const rsrc_t vbuf = make_rsrc(p.v + kvoff, (uint32_t)n * D * 2);
 #pragma unroll
@@ -380,8 +363,8 @@ bwd_dkdv_kernel(BwdParams p) {
             const uint32_t at = (uint32_t)(key * D + ks * 16 + hi * 8) * 2;
             const int row = l & 31, chunk = 2 * ks + hi;
             const int slot = row * D + ((chunk ^ bwd_swizzle<D>(row)) * 8);
-            if (load_k) *reinterpret_cast<bf16x8*>(Kw + slot) = load16(kbuf, at);
-            if (load_v) *reinterpret_cast<bf16x8*>(Vw + slot) = load16(vbuf, at);
+            *reinterpret_cast<bf16x8*>(Kw + slot) = load16(kbuf, at);
+            *reinterpret_cast<bf16x8*>(Vw + slot) = load16(vbuf, at);
         }
     }
 
@@ -430,10 +413,7 @@ bwd_dkdv_kernel(BwdParams p) {
         if (w == 0) stat[(f & 1) * 64 + l] = st_next;
         __syncthreads();                        // tile f visible; every wavefront is done with tile f - 1
         if (f + 1 < total) issue(f + 1);        // into the stage of tile f - 1
-        if (k0 >= n) {                          // this wavefront's keys are all past n
-            if (SPLIT) __syncthreads();         // ... but the P hand-over barrier is the workgroup's
-            continue;
-        }
+        if (k0 >= n) continue;                  // this wavefront's keys are all past n
         const int hh = f / nqt;
         const int q0 = q_first + (f - hh * nqt) * 32;
         const bf16* Qs = qt + (f & 1) * TILE;
@@ -443,22 +423,13 @@ bwd_dkdv_kernel(BwdParams p) {
         // Elementwise masks only on tiles where some pair is out (wave-uniform).
         const bool need = (q0 + 32 > p.Lq) || (k0 + 32 > n) || (p.causal && k0 + 31 > q0 + off) ||
                           (p.window > 0 && q0 + 31 + off - k0 >= p.window);
-        // One tile for one role, each its own straight-line code.
-        //   ROLE 0 (D = 64, both): S and dP, P, dV += P^T G, dS, dK += dS^T Q.
-        //   ROLE 1 (dV, w < 4):    S, P (to LDS), barrier, dV += P^T G.
-        //   ROLE 2 (dK, w >= 4):   dP, barrier, P (from LDS), dS, dK += dS^T Q.
-        // The split roles form S once per key block and run two products each.
-        auto tile = [&](auto role_tag) __attribute__((always_inline)) {
-            constexpr int ROLE = decltype(role_tag)::value;
-            constexpr bool DO_S = ROLE != 2, DO_DP = ROLE != 1;
-            constexpr bool WDV = ROLE != 2, WDK = ROLE != 1;
-            // S and dP steps (interleaved when both), one fragment pair each.
-            constexpr int NOP = (DO_S ? KS : 0) + (DO_DP ? KS : 0);
+        // One tile: S and dP (interleaved), P, dV += P^T G, dS, dK += dS^T Q.
+        {
+            constexpr int NOP = 2 * KS;         // S on even steps, dP on odd ones
             bf16x8 fa[NOP], fb[NOP];
-            auto is_dp_step = [&](int i) { return DO_S && DO_DP ? (i & 1) != 0 : DO_DP; };
             auto rd = [&](int i) __attribute__((always_inline)) {
-                const bool is_dp = is_dp_step(i);
-                const int ks = DO_S && DO_DP ? i / 2 : i;
+                const bool is_dp = (i & 1) != 0;
+                const int ks = i / 2;
                 fa[i] = read_row_chunk<D>(is_dp ? Gs : Qs, qrow, 2 * ks + hi);
                 fb[i] = read_row_chunk<D>(is_dp ? Vw : Kw, l & 31, 2 * ks + hi);
             };
@@ -468,106 +439,79 @@ bwd_dkdv_kernel(BwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < NOP; ++i) {
-                if (is_dp_step(i)) dp = mfma_32x32x16(fa[i], fb[i], dp);
-                else               s = mfma_32x32x16(fa[i], fb[i], s);
+                if (i & 1) dp = mfma_32x32x16(fa[i], fb[i], dp);
+                else       s = mfma_32x32x16(fa[i], fb[i], s);
                 if (i + kAhead < NOP) rd(i + kAhead);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // Transposed G (dV) and Q (dK) fragments, read now so that the
             // elementwise step covers their latency.
-            bf16x8 gT[WDV ? 2 * DB : 1], qT[WDK ? 2 * DB : 1];
+            bf16x8 gT[2 * DB], qT[2 * DB];
 #pragma unroll
             for (int f = 0; f < 2 * DB; ++f) {
-                if (WDV) gT[f] = read_transposed<D>(Gs, 16 * (f & 1), 32 * (f >> 1), l);
-                if (WDK) qT[f] = read_transposed<D>(Qs, 16 * (f & 1), 32 * (f >> 1), l);
+                gT[f] = read_transposed<D>(Gs, 16 * (f & 1), 32 * (f >> 1), l);
+                qT[f] = read_transposed<D>(Qs, 16 * (f & 1), 32 * (f >> 1), l);
             }
             __builtin_amdgcn_sched_barrier(0);
             // Entry v of this lane holds query q0 + 16*(v/8) + 8*hi + (v%8):
             // its L2 and delta are St[8 hi + (v%8) (+16 for v >= 8)] and
             // St[32 + ...].
+            float x[16];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int qd = 0; qd < 2; ++qd) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 8 * half + 4 * qd + e;
+                        x[v] = __builtin_fmaf(s[v], c2, -a[e]);
+                    }
+                }
+            if (need) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
+                    const int qpos = i + off;
+                    const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
+                                    ((p.window == 0) | (qpos - key < p.window));
+                    x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+                }
+            }
             float pr[16];
-            if (DO_S) {
-                float x[16];
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
+            for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(x[v]);
+            const bf16x8 pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+            const bf16x8 pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
 #pragma unroll
-                    for (int qd = 0; qd < 2; ++qd) {
-                        const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
+            for (int db = 0; db < DB; ++db) {
+                acc[db] = mfma_32x32x16(pb0, gT[2 * db], acc[db]);
+                acc[db] = mfma_32x32x16(pb1, gT[2 * db + 1], acc[db]);
+            }
+            float ds[16];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int v = 8 * half + 4 * qd + e;
-                            x[v] = __builtin_fmaf(s[v], c2, -a[e]);
-                        }
-                    }
-                if (need) {
+            for (int half = 0; half < 2; ++half)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                        const int qpos = i + off;
-                        const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
-                                        ((p.window == 0) | (qpos - key < p.window));
-                        x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+                for (int qd = 0; qd < 2; ++qd) {
+                    const f32x4 d = *reinterpret_cast<const f32x4*>(St + 32 + 16 * half + 8 * hi + 4 * qd);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 8 * half + 4 * qd + e;
+                        ds[v] = pr[v] * (dp[v] - d[e]);
                     }
                 }
+            const bf16x8 db0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            const bf16x8 db1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(x[v]);
+            for (int db = 0; db < DB; ++db) {
+                acc2[db] = mfma_32x32x16(db0, qT[2 * db], acc2[db]);
+                acc2[db] = mfma_32x32x16(db1, qT[2 * db + 1], acc2[db]);
             }
-            f32x4* pbuf = reinterpret_cast<f32x4*>(pshare) + kblk * 4 * 64 + l;
-            if (ROLE == 1) {                    // hand P to the dK wavefront of this key block
-#pragma unroll
-                for (int c = 0; c < 4; ++c) pbuf[c * 64] = f32x4{pr[4 * c], pr[4 * c + 1], pr[4 * c + 2], pr[4 * c + 3]};
-                __syncthreads();
-            }
-            if (ROLE == 2) {
-                __syncthreads();
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const f32x4 pv = pbuf[c * 64];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pr[4 * c + e] = pv[e];
-                }
-            }
-            if (WDV) {
-                const bf16x8 pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
-                const bf16x8 pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    acc[db] = mfma_32x32x16(pb0, gT[2 * db], acc[db]);
-                    acc[db] = mfma_32x32x16(pb1, gT[2 * db + 1], acc[db]);
-                }
-            }
-            if (WDK) {
-                float ds[16];
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int qd = 0; qd < 2; ++qd) {
-                        const f32x4 d = *reinterpret_cast<const f32x4*>(St + 32 + 16 * half + 8 * hi + 4 * qd);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int v = 8 * half + 4 * qd + e;
-                            ds[v] = pr[v] * (dp[v] - d[e]);
-                        }
-                    }
-                const bf16x8 db0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-                const bf16x8 db1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-                f32x16* dk = SPLIT ? acc : acc2;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dk[db] = mfma_32x32x16(db0, qT[2 * db], dk[db]);
-                    dk[db] = mfma_32x32x16(db1, qT[2 * db + 1], dk[db]);
-                }
-            }
-        };
-        if (!SPLIT) tile(Tag<0>{});
-        else if (w >= 4) tile(Tag<2>{});
-        else tile(Tag<1>{});
+        }
     }
 
     // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
     // 32*db + (l % 32).  Keys past n hold zeros.
-    const f32x16* dvacc = acc;
-    const f32x16* dkacc = SPLIT ? acc : acc2;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int kr = k0 + 8 * (v >> 2) + 4 * hi + (v & 3);
@@ -576,9 +520,231 @@ bwd_dkdv_kernel(BwdParams p) {
             bf16* dvp = p.dv + kvoff + (size_t)kr * D + (l & 31);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                if (do_dk) dkp[db * 32] = (bf16)(dkacc[db][v] * p.scale);
-                if (do_dv) dvp[db * 32] = (bf16)dvacc[db][v];
+                dkp[db * 32] = (bf16)(acc2[db][v] * p.scale);
+                dvp[db * 32] = (bf16)acc[db][v];
             }
+        }
+    }
+}
+
+
+// D = 128, role-split and pipelined over the query tiles.  Wavefront w owns
+// key block w % 4; w < 4 accumulates dV, w >= 4 dK, each with its own B
+// operand rows (K or V of its 32 keys) in registers.  The dV wavefront forms
+// P one tile ahead and hands it to the dK wavefront through a double buffer
+// in LDS, so within a tile the two roles run independently:
+//   dV role, tile t:  dV += P(t)^T G(t);  S(t+1) = Q(t+1) K^T;  P(t+1) -> LDS
+//   dK role, tile t:  dP(t) = G(t) V^T;  dS = P(t) (dP - delta);  dK += dS^T Q(t)
+// and each SIMD (one wavefront of each role) overlaps one role's products
+// with the other's vector work.  Q and G tiles stream through three LDS
+// stages (tiles t and t+1 are read in step t), copied two steps ahead; one
+// workgroup barrier per tile.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_split_kernel(BwdParams p) {
+    constexpr int D = 128;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int TILE = 32 * D;
+    constexpr int NSTG = 3;
+    __shared__ __attribute__((aligned(16))) bf16 qt[NSTG * TILE];
+    __shared__ __attribute__((aligned(16))) bf16 gt[NSTG * TILE];
+    __shared__ __attribute__((aligned(16))) float stat[NSTG * 64];   // per stage: L2 [0, 32), delta [32, 64)
+    // P of tile t, key block kb, entry chunk c of lane l at (((t % 2) 4 + kb) 4 + c) 64 + l (f32x4).
+    __shared__ __attribute__((aligned(16))) float pshare[2 * 4 * 16 * 64];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int hi = l >> 5;
+    const int kblk = w & 3;
+    const bool role_dv = w < 4;
+    const int nbg = p.B * p.Hkv;
+    const int kb = blockIdx.x / nbg;            // first key blocks first
+    const int bg = blockIdx.x - kb * nbg;       // b * Hkv + g; on XCD bg % 8 when nbg % 8 == 0
+    const int g = bg % p.Hkv;
+    const int b = bg / p.Hkv;
+    const int n = clamp_len(p.kv_lens, b, p.Lk);
+    const int off = n - p.Lq;
+    const int kw0 = kb * 128;
+    const int k0 = kw0 + 32 * kblk;
+    const int key = k0 + (l & 31);
+    const bool active = k0 < n;                 // some key of this wavefront is valid
+    const size_t kvoff = (size_t)bg * p.Lk * D;
+
+    // This wavefront's K (dV role) or V (dK role) rows as B operands: lane l
+    // takes key row l % 32, elements 16 ks + 8 hi .. +7 (zeros past n).
+    bf16x8 kvf[KS];
+    {
+        const rsrc_t buf = make_rsrc((role_dv ? p.k : p.v) + kvoff, (uint32_t)n * D * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kvf[ks] = load16(buf, (uint32_t)(key * D + ks * 16 + hi * 8) * 2);
+    }
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
+
+    int i_lo = 0, i_hi = p.Lq;
+    if (p.causal) i_lo = max(kw0 - off, 0);
+    if (p.window > 0) i_hi = min(p.Lq, max(kw0 + 127 + p.window - off, 0));
+    const int q_first = (i_lo / 32) * 32;
+    const int nqt = (kw0 < n && i_hi > q_first) ? (i_hi - q_first + 31) / 32 : 0;
+    const int total = p.r * nqt;
+
+    TileCopy<D, 512> cp;
+    cp.init(w, l);
+    const uint32_t lds_q = lds_address(qt), lds_g = lds_address(gt);
+    float st_next = 0.0f;                       // wavefront 0: L2 (lanes < 32) or delta of a query
+    auto tile_q0 = [&](int f) __attribute__((always_inline)) {
+        const int hh = f / nqt;
+        return q_first + (f - hh * nqt) * 32;
+    };
+    auto issue = [&](int f) __attribute__((always_inline)) {   // tile f into stage f % 3
+        const int hh = f / nqt;
+        const int q0 = q_first + (f - hh * nqt) * 32;
+        const size_t bh = (size_t)b * p.Hq + g * p.r + hh;
+        const size_t at = (bh * p.Lq + (size_t)q0) * D;
+        const int buf = (f % NSTG) * TILE * 2;
+        cp.issue(p.q + at, p.Lq - q0, lds_q + buf, w);
+        cp.issue(p.dout + at, p.Lq - q0, lds_g + buf, w);
+        if (w == 0) {
+            const int i = q0 + (l & 31);
+            float val = 0.0f;
+            if (i < p.Lq) {
+                if (l < 32) {
+                    const float L = p.lse[bh * p.Lq + i];
+                    val = L == kNegInf ? 0.0f : L * kLog2e;
+                } else {
+                    val = p.delta[bh * p.Lq + i];
+                }
+            }
+            st_next = val;
+        }
+    };
+
+    const int qrow = swap_bits_2_3(l & 31);   // A-operand row of this lane
+    const float c2 = p.c;
+    bf16x8 pb0 = zero_bf16x8(), pb1 = zero_bf16x8();   // dV role: P of the current tile, as the A operand
+
+    // A 32 x 32 product over D with A rows from an LDS tile and B from kvf.
+    auto product = [&](const bf16* tile) __attribute__((always_inline)) {
+        bf16x8 fa[KS];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) fa[i] = read_row_chunk<D>(tile, qrow, 2 * i + hi);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 r = zero_f32x16();
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            r = mfma_32x32x16(fa[i], kvf[i], r);
+            if (i + kAhead < KS) fa[i + kAhead] = read_row_chunk<D>(tile, qrow, 2 * (i + kAhead) + hi);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return r;
+    };
+    // dV role: P of tile f (scores of its Q tile against K), masked where
+    // needed, handed over through LDS and kept as the bf16 A operand.
+    auto form_p = [&](int f) __attribute__((always_inline)) {
+        const int stg = f % NSTG;
+        const int q0 = tile_q0(f);
+        const f32x16 s = product(qt + stg * TILE);
+        const float* St = stat + stg * 64;
+        float pr[16];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int qd = 0; qd < 2; ++qd) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(St + 16 * half + 8 * hi + 4 * qd);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 8 * half + 4 * qd + e;
+                    pr[v] = __builtin_fmaf(s[v], c2, -a[e]);
+                }
+            }
+        const bool need = (q0 + 32 > p.Lq) || (k0 + 32 > n) || (p.causal && k0 + 31 > q0 + off) ||
+                          (p.window > 0 && q0 + 31 + off - k0 >= p.window);
+        if (need) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
+                const int qpos = i + off;
+                const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
+                                ((p.window == 0) | (qpos - key < p.window));
+                pr[v] = ok ? pr[v] : kNegInf;   // 2^-inf = 0
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(pr[v]);
+        f32x4* pbuf = reinterpret_cast<f32x4*>(pshare) + ((f & 1) * 4 + kblk) * 4 * 64 + l;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pbuf[c * 64] = f32x4{pr[4 * c], pr[4 * c + 1], pr[4 * c + 2], pr[4 * c + 3]};
+        pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+        pb1 = to_bf16x8(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+    };
+
+    // ---- prologue: tiles 0 and 1 on their way, P(0) ------------------------
+    if (total > 0) issue(0);
+    wait_all_vector_loads();                    // tile 0, its statistics, this wavefront's K / V rows
+    if (w == 0) stat[l] = st_next;
+    if (total > 1) issue(1);
+    __syncthreads();                            // tile 0 visible
+    if (role_dv && active && total > 0) form_p(0);
+
+    for (int f = 0; f < total; ++f) {
+        wait_all_vector_loads();                // this wavefront's copies of tile f + 1
+        if (w == 0 && f + 1 < total) stat[((f + 1) % NSTG) * 64 + l] = st_next;
+        __syncthreads();                        // tile f + 1 and P(f) visible; step f - 1 done everywhere
+        if (f + 2 < total) issue(f + 2);        // into the stage of tile f - 1
+        if (!active) continue;
+        const int stg = f % NSTG;
+        const bf16* Qs = qt + stg * TILE;
+        const bf16* Gs = gt + stg * TILE;
+        if (role_dv) {
+            // dV += P(f)^T G(f), then P(f + 1).
+            bf16x8 gT[2 * DB];
+#pragma unroll
+            for (int j = 0; j < 2 * DB; ++j) gT[j] = read_transposed<D>(Gs, 16 * (j & 1), 32 * (j >> 1), l);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc[db] = mfma_32x32x16(pb0, gT[2 * db], acc[db]);
+                acc[db] = mfma_32x32x16(pb1, gT[2 * db + 1], acc[db]);
+            }
+            if (f + 1 < total) form_p(f + 1);
+        } else {
+            // dP(f), dS = P(f) (dP - delta), dK += dS^T Q(f).
+            const f32x16 dp = product(Gs);
+            bf16x8 qT[2 * DB];
+#pragma unroll
+            for (int j = 0; j < 2 * DB; ++j) qT[j] = read_transposed<D>(Qs, 16 * (j & 1), 32 * (j >> 1), l);
+            const f32x4* pbuf = reinterpret_cast<const f32x4*>(pshare) + ((f & 1) * 4 + kblk) * 4 * 64 + l;
+            const float* St = stat + stg * 64;
+            float ds[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f32x4 pv = pbuf[c * 64];
+                const int half = c >> 1, qd = c & 1;
+                const f32x4 d = *reinterpret_cast<const f32x4*>(St + 32 + 16 * half + 8 * hi + 4 * qd);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ds[4 * c + e] = pv[e] * (dp[4 * c + e] - d[e]);
+            }
+            const bf16x8 db0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            const bf16x8 db1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc[db] = mfma_32x32x16(db0, qT[2 * db], acc[db]);
+                acc[db] = mfma_32x32x16(db1, qT[2 * db + 1], acc[db]);
+            }
+        }
+    }
+
+    // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
+    // 32*db + (l % 32).  Keys past n hold zeros.
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int kr = k0 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        if (kr < p.Lk) {
+            bf16* out = (role_dv ? p.dv : p.dk) + kvoff + (size_t)kr * D + (l & 31);
+            const float sc = role_dv ? 1.0f : p.scale;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) out[db * 32] = (bf16)(acc[db][v] * sc);
         }
     }
 }
@@ -588,10 +754,10 @@ hipError_t launch_backward(int D, const BwdParams& p, hipStream_t stream) {
     const long long nk = (long long)p.B * p.Hkv * ((p.Lk + 127) / 128);
     if (D == 64) {
         hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3((unsigned)nq), dim3(256), 0, stream, p);
-        if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3((unsigned)nk), dim3(DkdvShape<64>::NT), 0, stream, p);
+        if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3((unsigned)nk), dim3(256), 0, stream, p);
     } else {
         hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3((unsigned)nq), dim3(256), 0, stream, p);
-        if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3((unsigned)nk), dim3(DkdvShape<128>::NT), 0, stream, p);
+        if (nk > 0) hipLaunchKernelGGL(bwd_dkdv_split_kernel, dim3((unsigned)nk), dim3(512), 0, stream, p);
     }
     return hipGetLastError();
 }
