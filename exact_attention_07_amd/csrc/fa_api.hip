@@ -398,8 +398,8 @@ int fa_quantize_fp8(const void* x, void* x8, float* scales, int heads, int L, in
                     heads, L, block_rows);
     if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension D=%d is not supported (64 or 128)", D);
     if (!x || !x8 || !scales) return fail(FA_ERR_INVALID_ARG, "x, x8 and scales must not be NULL");
-    if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4) || !aligned(signs, 4))
-        return fail(FA_ERR_INVALID_ARG, "x and x8 must be 16-byte aligned, scales and signs 4-byte aligned");
+    if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(scales, 4) || !aligned(signs, 16))
+        return fail(FA_ERR_INVALID_ARG, "x, x8 and signs must be 16-byte aligned, scales 4-byte aligned");
     const long long nblk = (L + (long long)block_rows - 1) / block_rows;
     if ((long long)heads * nblk > INT32_MAX || (long long)L * D > INT32_MAX)
         return fail(FA_ERR_INVALID_ARG, "problem too large");

@@ -199,7 +199,8 @@ int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
  *   x      : bf16, device, contiguous [heads, L, D], 16-byte aligned
  *   x8     : uint8 E4M3 codes, device, [heads, L, D], 16-byte aligned, written
  *   scales : fp32, device, [heads, ceil(L / block_rows)], written
- *   signs  : fp32, device, D values each +1 or -1, or NULL for no transform
+ *   signs  : fp32, device, D values each +1 or -1, 16-byte aligned, or NULL
+ *            for no transform
  * Since H H^T = D I, scores from transformed Q and K are D times the
  * original: divide the softmax scale by D (fa_fwd_fp8 takes it as given).
  * The forward expects Q blocks of 256 rows and K blocks of 64 rows.

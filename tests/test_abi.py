@@ -201,6 +201,7 @@ def call_quant(lib, x=P, x8=P, scales=P, heads=2, L=100, D=128, block_rows=64, s
     (dict(scales=None), binding.FA_ERR_INVALID_ARG),
     (dict(x8=MIS), binding.FA_ERR_INVALID_ARG),
     (dict(signs=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(signs=ctypes.c_void_p((1 << 20) + 4)), binding.FA_ERR_INVALID_ARG),   # 4-byte aligned is not enough
     (dict(block_rows=0), binding.FA_ERR_INVALID_ARG),
     (dict(L=0), binding.FA_ERR_INVALID_ARG),
     (dict(heads=-1), binding.FA_ERR_INVALID_ARG),

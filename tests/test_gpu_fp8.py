@@ -59,6 +59,8 @@ QUANT_CASES = [
     (2, 3, 513, 128, 256, True, 2),
     (1, 1, 77, 64, 64, True, 0),
     (2, 2, 130, 64, 256, False, 3),
+    (1, 2, 700, 128, 300, True, 1),   # 19 slices of 16 rows: more than the registers hold
+    (1, 1, 1300, 64, 600, True, 0),   # 19 slices of 32 rows
 ]
 
 
