@@ -179,6 +179,12 @@ prefill_kernel(PrefillParams p) {
     int tb = 0;
     if (WINDOW) tb = max(q0 + off - p.window + 1, 0) / BN;
     const int ntiles = (kv_end + BN - 1) / BN - tb;   // tiles visited, counted from tb
+    // Visit order.  With ALiBi the tiles run from the last one down: under
+    // the bias the nearest keys score highest, so the row maxima are found
+    // first and the reference rarely moves afterwards (in key order the max
+    // of a steep head rises by tens of binades per tile, a move every tile).
+    constexpr bool REV = MOD == kModAlibi;
+    auto tile_abs = [&](int t) { return REV ? tb + ntiles - 1 - t : tb + t; };
 
     const size_t qoff = (size_t)(b * p.Hq + h) * p.Lq * D;
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
@@ -232,8 +238,10 @@ prefill_kernel(PrefillParams p) {
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)smem);
     auto copy_tile = [&](const bf16* base, int t, int buf, const uint32_t (&offs)[NI]) __attribute__((always_inline)) {
-        const int ta = tb + t;              // absolute tile index
-        const int rows = n - ta * BN;       // valid rows from the tile start; <= 0 past the end
+        const int ta = tile_abs(t);         // absolute tile index
+        // Valid rows from the tile start; <= 0 past the end (in reverse order,
+        // the copies past the last visited tile fetch nothing either).
+        const int rows = (REV && t >= ntiles) ? 0 : n - ta * BN;
         const i32x4 d = make_desc(base + kvoff + (size_t)(rows > 0 ? ta : 0) * BN * D,
                                   (uint32_t)(rows > 0 ? rows : 0) * D * 2);
 #pragma unroll
@@ -317,17 +325,25 @@ prefill_kernel(PrefillParams p) {
     // Vector phase for tile t (scores in s): mask where needed, p -> pe and the
     // fp32 row sum, and the rare reference move.
     auto softmax_tile = [&](int t) __attribute__((always_inline)) {
-        const int k0 = (tb + t) * BN;
+        const int k0 = tile_abs(t) * BN;
         const float ct = FP8 ? cq * ksc_next : c;   // this tile's exponent scale
         if (FP8) ksc_next = k_scale_of(t + 1);
-        if constexpr (MOD == kModAlibi) {
-            // |pos_i - pos_j| = |(qpos - k0 - 8 hi) - (32 kb + 16 (v / 8) + v % 8)|
-            const float base = (float)(qrow + off - k0 - 8 * hi);
+        // ALiBi: |pos_i - pos_j| = |base - K_v| with base = qpos - k0 - 8 hi
+        // and K_v = 32 kb + 16 (v / 8) + v % 8.  Where every key of the tile
+        // is on one side of every row of the wavefront (sign sgn of
+        // pos_i - pos_j), the bias is linear in K_v and goes into the
+        // exponent's fma instead (see exponentials); else it is added here.
+        const float base = (float)(qrow + off - k0 - 8 * hi);
+        const int sgn = MOD != kModAlibi ? 0 : (qw0 + off >= k0 + BN - 1) ? 1 : (k0 > qw0 + 31 + off) ? -1 : 0;
+        auto add_alibi = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     s[kb][v] = __builtin_fmaf(-mod_a, fabsf(base - (float)(kb * 32 + 16 * (v >> 3) + (v & 7))), s[kb][v]);
+        };
+        if constexpr (MOD == kModAlibi) {
+            if (sgn == 0) add_alibi();
         } else if constexpr (MOD == kModSoftcap) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -358,8 +374,12 @@ prefill_kernel(PrefillParams p) {
         // reference.  Four partial sums of p and two of bf16(p) keep the
         // dependency chains short.
         float se[4];
+        bool folded = MOD == kModAlibi && sgn != 0;    // bias still to be applied, in the exponent
         auto exponentials = [&]() __attribute__((always_inline)) {
             const float r = ref == kNegInf ? 0.0f : ref;   // never form -inf - (-inf)
+            // Folded ALiBi: s ct - r - a ct sgn (base - K_v) = fma(s, ct, fma(c1, K_v, b0)).
+            const float c1 = folded ? (float)sgn * mod_a * ct : 0.0f;
+            const float b0 = folded ? __builtin_fmaf(-c1, base, -r) : -r;
             se[0] = se[1] = se[2] = se[3] = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -367,7 +387,9 @@ prefill_kernel(PrefillParams p) {
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], ct, -r));
+                        const float kv = (float)(kb * 32 + 16 * half + j);
+                        const float t = (MOD == kModAlibi) ? __builtin_fmaf(c1, kv, b0) : -r;
+                        pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], ct, t));
                         se[j & 3] += pe[kb][half][j];
                     }
         };
@@ -382,6 +404,11 @@ prefill_kernel(PrefillParams p) {
         const float row_sum = sum_with_partner((se[0] + se[1]) + (se[2] + se[3]));
         const bool move = ref == kNegInf || !(row_sum <= kTauSum);
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            if constexpr (MOD == kModAlibi) {
+                // The row max is of the biased scores: apply the bias here.
+                if (folded) add_alibi();
+                folded = false;
+            }
             float m8[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(s[0][j], s[0][j + 8]), fmaxf(s[1][j], s[1][j + 8]));
