@@ -537,7 +537,8 @@ bwd_dkdv_kernel(BwdParams p) {
 //   dK role, tile t:  dP(t) = G(t) V^T;  dS = P(t) (dP - delta);  dK += dS^T Q(t)
 // and each SIMD (one wavefront of each role) overlaps one role's products
 // with the other's vector work.  Q and G tiles stream through three LDS
-// stages (tiles t and t+1 are read in step t), copied two steps ahead; one
+// stages (tiles t and t+1 are read in step t), copied two steps ahead by the
+// dV wavefronts; one
 // workgroup barrier per tile.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_split_kernel(BwdParams p) {
@@ -590,8 +591,12 @@ bwd_dkdv_split_kernel(BwdParams p) {
     const int nqt = (kw0 < n && i_hi > q_first) ? (i_hi - q_first + 31) / 32 : 0;
     const int total = p.r * nqt;
 
-    TileCopy<D, 512> cp;
-    cp.init(w, l);
+    // Only the dV wavefronts copy (two 16-byte copies per lane per tile).
+    // Their step is the shorter one, and copies issued by all eight
+    // wavefronts right after the barrier queue behind each other and delay the
+    // dK chain.
+    TileCopy<D, 256> cp;
+    cp.init(w & 3, l);
     const uint32_t lds_q = lds_address(qt), lds_g = lds_address(gt);
     float st_next = 0.0f;                       // wavefront 0: L2 (lanes < 32) or delta of a query
     auto tile_q0 = [&](int f) __attribute__((always_inline)) {
@@ -604,8 +609,10 @@ bwd_dkdv_split_kernel(BwdParams p) {
         const size_t bh = (size_t)b * p.Hq + g * p.r + hh;
         const size_t at = (bh * p.Lq + (size_t)q0) * D;
         const int buf = (f % NSTG) * TILE * 2;
-        cp.issue(p.q + at, p.Lq - q0, lds_q + buf, w);
-        cp.issue(p.dout + at, p.Lq - q0, lds_g + buf, w);
+        if (role_dv) {
+            cp.issue(p.q + at, p.Lq - q0, lds_q + buf, w);
+            cp.issue(p.dout + at, p.Lq - q0, lds_g + buf, w);
+        }
         if (w == 0) {
             const int i = q0 + (l & 31);
             float val = 0.0f;
