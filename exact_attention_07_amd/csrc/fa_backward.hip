@@ -538,8 +538,7 @@ bwd_dkdv_kernel(BwdParams p) {
 // and each SIMD (one wavefront of each role) overlaps one role's products
 // with the other's vector work.  Q and G tiles stream through three LDS
 // stages (tiles t and t+1 are read in step t), copied two steps ahead by the
-// dV wavefronts; one
-// workgroup barrier per tile.
+// dV wavefronts; one workgroup barrier per tile.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_split_kernel(BwdParams p) {
     constexpr int D = 128;
