@@ -598,34 +598,36 @@ bwd_dkdv_split_kernel(BwdParams p) {
     cp.init(w & 3, l);
     const uint32_t lds_q = lds_address(qt), lds_g = lds_address(gt);
     float st_next = 0.0f;                       // wavefront 0: L2 (lanes < 32) or delta of a query
-    auto tile_q0 = [&](int f) __attribute__((always_inline)) {
-        const int hh = f / nqt;
-        return q_first + (f - hh * nqt) * 32;
-    };
-    auto issue = [&](int f) __attribute__((always_inline)) {   // tile f into stage f % 3
-        const int hh = f / nqt;
-        const int q0 = q_first + (f - hh * nqt) * 32;
-        const size_t bh = (size_t)b * p.Hq + g * p.r + hh;
-        const size_t at = (bh * p.Lq + (size_t)q0) * D;
+    // Tiles are copied, and P formed, in order f = 0, 1, 2, ...: tile f is
+    // query tile f % nqt of query head f / nqt.  Running counters give the
+    // tile's first query and row index with scalar adds; a division per tile,
+    // in every wavefront right after the barrier, kept the CU's scalar unit
+    // busy for hundreds of cycles.
+    const int head_skip = p.Lq - nqt * 32;      // rows from one head's last tile end to the next head's first tile
+    int cp_qi = 0;                              // next tile to copy: tile index within its head
+    long long cp_row = ((long long)b * p.Hq + g * p.r) * p.Lq + q_first;   // ... and its first row, all heads
+    auto issue = [&](int f) __attribute__((always_inline)) {   // tile f into stage f % 3 (dV role only)
+        const int q0 = q_first + cp_qi * 32;
         const int buf = (f % NSTG) * TILE * 2;
-        if (role_dv) {
-            cp.issue(p.q + at, p.Lq - q0, lds_q + buf, w);
-            cp.issue(p.dout + at, p.Lq - q0, lds_g + buf, w);
-        }
+        cp.issue(p.q + cp_row * D, p.Lq - q0, lds_q + buf, w);
+        cp.issue(p.dout + cp_row * D, p.Lq - q0, lds_g + buf, w);
         if (w == 0) {
             const int i = q0 + (l & 31);
             float val = 0.0f;
             if (i < p.Lq) {
                 if (l < 32) {
-                    const float L = p.lse[bh * p.Lq + i];
+                    const float L = p.lse[cp_row + (l & 31)];
                     val = L == kNegInf ? 0.0f : L * kLog2e;
                 } else {
-                    val = p.delta[bh * p.Lq + i];
+                    val = p.delta[cp_row + (l & 31)];
                 }
             }
             st_next = val;
         }
+        cp_row += 32;
+        if (++cp_qi == nqt) { cp_qi = 0; cp_row += head_skip; }
     };
+    int p_qi = 0;                               // dV role: tile index within its head of the next P formed
 
     const int qrow = swap_bits_2_3(l & 31);   // A-operand row of this lane
     const float c2 = p.c;
@@ -650,7 +652,8 @@ bwd_dkdv_split_kernel(BwdParams p) {
     // needed, handed over through LDS and kept as the bf16 A operand.
     auto form_p = [&](int f) __attribute__((always_inline)) {
         const int stg = f % NSTG;
-        const int q0 = tile_q0(f);
+        const int q0 = q_first + p_qi * 32;
+        if (++p_qi == nqt) p_qi = 0;
         const f32x16 s = product(qt + stg * TILE);
         const float* St = stat + stg * 64;
         float pr[16];
@@ -687,10 +690,10 @@ bwd_dkdv_split_kernel(BwdParams p) {
     };
 
     // ---- prologue: tiles 0 and 1 on their way, P(0) ------------------------
-    if (total > 0) issue(0);
+    if (role_dv && total > 0) issue(0);
     wait_all_vector_loads();                    // tile 0, its statistics, this wavefront's K / V rows
     if (w == 0) stat[l] = st_next;
-    if (total > 1) issue(1);
+    if (role_dv && total > 1) issue(1);
     __syncthreads();                            // tile 0 visible
     if (role_dv && active && total > 0) form_p(0);
 
@@ -698,7 +701,7 @@ bwd_dkdv_split_kernel(BwdParams p) {
         wait_all_vector_loads();                // this wavefront's copies of tile f + 1
         if (w == 0 && f + 1 < total) stat[((f + 1) % NSTG) * 64 + l] = st_next;
         __syncthreads();                        // tile f + 1 and P(f) visible; step f - 1 done everywhere
-        if (f + 2 < total) issue(f + 2);        // into the stage of tile f - 1
+        if (role_dv && f + 2 < total) issue(f + 2);   // into the stage of tile f - 1
         if (!active) continue;
         const int stg = f % NSTG;
         const bf16* Qs = qt + stg * TILE;
