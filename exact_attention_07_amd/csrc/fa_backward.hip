@@ -382,28 +382,34 @@ bwd_dkdv_kernel(BwdParams p) {
     cp.init(w, l);
     const uint32_t lds_q = lds_address(qt), lds_g = lds_address(gt);
     float st_next = 0.0f;                       // wavefront 0: L2 (lanes < 32) or delta of a query
+    // Tiles are copied and used in order f = 0, 1, 2, ...: tile f is query
+    // tile f % nqt of query head f / nqt.  Running counters (scalar adds)
+    // stand in for a division per tile on the CU's shared scalar unit.
+    const int head_skip = p.Lq - nqt * 32;      // rows from one head's last tile end to the next head's first tile
+    int cp_qi = 0;                              // next tile to copy: tile index within its head
+    long long cp_row = ((long long)b * p.Hq + g * p.r) * p.Lq + q_first;   // ... and its first row, all heads
     auto issue = [&](int f) __attribute__((always_inline)) {   // tile f into stage f % 2
-        const int hh = f / nqt;
-        const int q0 = q_first + (f - hh * nqt) * 32;
-        const size_t bh = (size_t)b * p.Hq + g * p.r + hh;
-        const size_t at = (bh * p.Lq + (size_t)q0) * D;
+        const int q0 = q_first + cp_qi * 32;
         const int buf = (f & 1) * TILE * 2;
-        cp.issue(p.q + at, p.Lq - q0, lds_q + buf, w);
-        cp.issue(p.dout + at, p.Lq - q0, lds_g + buf, w);
+        cp.issue(p.q + cp_row * D, p.Lq - q0, lds_q + buf, w);
+        cp.issue(p.dout + cp_row * D, p.Lq - q0, lds_g + buf, w);
         if (w == 0) {
             const int i = q0 + (l & 31);
             float val = 0.0f;
             if (i < p.Lq) {
                 if (l < 32) {
-                    const float L = p.lse[bh * p.Lq + i];
+                    const float L = p.lse[cp_row + (l & 31)];
                     val = L == kNegInf ? 0.0f : L * kLog2e;
                 } else {
-                    val = p.delta[bh * p.Lq + i];
+                    val = p.delta[cp_row + (l & 31)];
                 }
             }
             st_next = val;
         }
+        cp_row += 32;
+        if (++cp_qi == nqt) { cp_qi = 0; cp_row += head_skip; }
     };
+    int use_qi = 0;                             // tile index within its head of the tile in use
 
     const int qrow = swap_bits_2_3(l & 31);   // A-operand row of this lane
     const float c2 = p.c;
@@ -413,9 +419,9 @@ bwd_dkdv_kernel(BwdParams p) {
         if (w == 0) stat[(f & 1) * 64 + l] = st_next;
         __syncthreads();                        // tile f visible; every wavefront is done with tile f - 1
         if (f + 1 < total) issue(f + 1);        // into the stage of tile f - 1
+        const int q0 = q_first + use_qi * 32;
+        if (++use_qi == nqt) use_qi = 0;
         if (k0 >= n) continue;                  // this wavefront's keys are all past n
-        const int hh = f / nqt;
-        const int q0 = q_first + (f - hh * nqt) * 32;
         const bf16* Qs = qt + (f & 1) * TILE;
         const bf16* Gs = gt + (f & 1) * TILE;
         const float* St = stat + (f & 1) * 64;
