@@ -251,6 +251,10 @@ bwd_dq_kernel(BwdParams p) {
             fr[i] = read_row_chunk<D>((i & 1) ? Vs : Ks, krow, 2 * (i / 2) + hi);
         };
         f32x16 s = zero_f32x16(), dp = zero_f32x16();
+        // Products at raised priority: of the two wavefronts on a SIMD (from
+        // different workgroups), the one with matrix work to issue goes first
+        // and the other fills the gaps with its elementwise step.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) rd(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -267,6 +271,7 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int f = 0; f < 2 * DB; ++f) kT[f] = read_transposed<D>(Ks, 16 * (f & 1), 32 * (f >> 1), l);
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         // Elementwise masks only on tiles where some pair of this
         // wavefront's rows and the tile is out (a wave-uniform test).
         const int qw = qw0 + 32 * w;            // first query of this wavefront
@@ -290,11 +295,13 @@ bwd_dq_kernel(BwdParams p) {
         for (int v = 0; v < 16; ++v) ds[v] = exp2_fast(x[v]) * (dp[v] - delta);
         const bf16x8 dsb0 = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
         const bf16x8 dsb1 = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             dq[db] = mfma_32x32x16(kT[2 * db], dsb0, dq[db]);
             dq[db] = mfma_32x32x16(kT[2 * db + 1], dsb1, dq[db]);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     if (row_ok) {
