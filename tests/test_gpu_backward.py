@@ -116,6 +116,10 @@ CASES = [
     (2, 4, 2, 150, 170, 64, True, 33, "ragged"),
     (2, 4, 4, 1, 500, 64, False, 0, "ragged"),     # one query per head (decode shape)
     (1, 2, 2, 100, 60, 64, True, 0, None),         # more queries than keys: empty rows
+    (1, 2, 1, 520, 777, 128, False, 0, None),      # 25 KV tiles: a ragged end of the four-stage unroll
+    (1, 4, 2, 600, 650, 128, True, 100, "ragged"),  # GQA, window, ragged, several query blocks
+    (2, 4, 4, 1, 500, 128, False, 0, "ragged"),    # one query per head at D = 128
+    (1, 2, 2, 100, 60, 128, True, 0, None),        # more queries than keys at D = 128
 ]
 
 
