@@ -183,8 +183,11 @@ prefill_kernel(PrefillParams p) {
     // the bias the nearest keys score highest, so the row maxima are found
     // first and the reference rarely moves afterwards (in key order the max
     // of a steep head rises by tens of binades per tile, a move every tile).
+    // Positions t >= ntiles (the prologue's tile when the block sees no key,
+    // and copies past the end) map past the visited range in either order, so
+    // the masks treat them as in key order.
     constexpr bool REV = MOD == kModAlibi;
-    auto tile_abs = [&](int t) { return REV ? tb + ntiles - 1 - t : tb + t; };
+    auto tile_abs = [&](int t) { return (REV && t < ntiles) ? tb + ntiles - 1 - t : tb + t; };
 
     const size_t qoff = (size_t)(b * p.Hq + h) * p.Lq * D;
     const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;

@@ -40,6 +40,8 @@ CASES = [
     (3, 8, 2, 129, 190, 64, False, "ragged"),
     (2, 4, 4, 1, 500, 128, False, "ragged"),       # one query per head
     (1, 2, 2, 100, 60, 64, True, None),            # more queries than keys: empty rows
+    (1, 2, 2, 300, 20, 64, True, None),            # a whole query block before the first key
+    (3, 2, 2, 40, 50, 128, False, [0, 50, 7]),     # a sequence of length 0
 ]
 
 
