@@ -10,8 +10,11 @@ to bf16 before their products, and delta uses the forward's bf16 output; with
 independent roundings the relative L2 error is a small multiple of 2^-9 / 3^0.5
 (about 2.3e-3 measured).  The bar is
   * relative L2 <= 5e-3;
-  * max |error| <= 1e-2 * max |reference| (the largest elements carry the
-    largest absolute rounding);
+  * max |error| <= 1e-2 * max |reference| + 1e-5 (the largest elements
+    carry the largest absolute rounding; the floor covers gradients that are
+    zero by cancellation, e.g. dQ with a single valid key, where P = 1 and
+    dP = delta exactly, which the kernel reaches only up to the rounding of
+    delta from the bf16 output, ~1e-6);
   * no NaN; exact zeros where the reference is exactly zero because no
     allowed pair touches the element (keys past the valid length, rows with no
     allowed key).
@@ -31,6 +34,7 @@ pytestmark = pytest.mark.gpu
 
 REL_L2 = 5e-3
 MAX_REL = 1e-2
+ABS_FLOOR = 1e-5
 
 
 @pytest.fixture(scope="module")
@@ -80,7 +84,7 @@ def compare_grad(name, got, ref, exact_zero=None):
     mx = float(err.max()) if err.size else 0.0
     print(f"[parity] {name}: rel_l2={rel:.3g} max_abs={mx:.3g} max_ref={mref:.3g}", flush=True)
     assert rel <= REL_L2, f"{name}: relative L2 {rel:.3g} > {REL_L2}"
-    assert mx <= MAX_REL * mref + 1e-30, f"{name}: max abs {mx:.3g} > {MAX_REL} * {mref:.3g}"
+    assert mx <= MAX_REL * mref + ABS_FLOOR, f"{name}: max abs {mx:.3g} > {MAX_REL} * {mref:.3g} + {ABS_FLOOR}"
 
 
 def run_case(dev, case, dout, causal, window=0, k=None, v=None):
@@ -120,6 +124,7 @@ CASES = [
     (1, 4, 2, 600, 650, 128, True, 100, "ragged"),  # GQA, window, ragged, several query blocks
     (2, 4, 4, 1, 500, 128, False, 0, "ragged"),    # one query per head at D = 128
     (1, 2, 2, 100, 60, 128, True, 0, None),        # more queries than keys at D = 128
+    (1, 12, 3, 87, 1, 128, False, 0, None),        # one key: dQ is zero by cancellation
 ]
 
 
