@@ -1,4 +1,5 @@
-"""Seeded random shapes through every entry point, each against the fp64
+"""Seeded random shapes through every entry point (forward, window, split
+path, paged cache, modifiers, FP8, backward), each against the fp64
 oracle at the bar of its own tests (tests/parity.py for forwards; the
 backward bar of test_gpu_backward).
 
@@ -127,3 +128,38 @@ def test_random_backward(dev, seed):
     compare_grad("dq", dq, rq, exact_zero=zq)
     compare_grad("dk", dk, rk, exact_zero=zk)
     compare_grad("dv", dv, rv, exact_zero=zk)
+
+
+@pytest.mark.parametrize("seed", SEEDS[:12])
+def test_random_split_path(dev, seed):
+    # Decode and short query chunks through fa_fwd_splits at a random
+    # partition count (1 to 40).
+    B, Hq, Hkv, _, Lk, D, causal, lens = draw(seed)
+    r = np.random.default_rng(seed + 4)
+    Lq = int(r.choice([1, 2, 5]))
+    splits = int(r.integers(1, 41))
+    c = W.random_case(seed, B, Hq, Hkv, Lq, Lk, D, causal, lens)
+    kl = None if c.kv_lens is None else c.kv_lens.to(dev)
+    o, lse = binding.fa_fwd_splits(c.q.to(dev), c.k.to(dev), c.v.to(dev), splits, causal=causal,
+                                   scale=c.scale, kv_lens=kl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward(c.q, c.k, c.v, c.scale, causal, c.kv_lens)
+    compare(o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("seed", SEEDS[:12])
+def test_random_paged(dev, seed):
+    # A shuffled paged cache with a random page size (a multiple of 16),
+    # decode or a short causal chunk, optionally under a window.
+    B, Hq, Hkv, _, Lk, D, causal, _ = draw(seed)
+    r = np.random.default_rng(seed + 5)
+    P = 16 * int(r.integers(1, 9))
+    Lq = 1 if not causal else int(r.choice([1, 3, 8]))
+    w = int(r.integers(1, Lk + 30)) if (causal and r.integers(0, 2)) else 0
+    c = W.random_case(seed, B, Hq, Hkv, Lq, Lk, D, causal, "ragged")
+    kc, vc, table = W.page_kv(c.k, c.v, c.kv_lens, P, seed=seed)
+    o, lse = binding.fa_fwd_paged(c.q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), c.kv_lens.to(dev),
+                                  causal=causal, window=w, scale=c.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_attention_forward(c.q, kc, vc, table, c.kv_lens, P, c.scale, causal, w)
+    compare(o, lse, ro, rl)
