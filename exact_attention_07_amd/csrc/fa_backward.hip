@@ -11,9 +11,11 @@
 // result is deterministic:
 //
 // Both kernels run workgroups whose wavefronts share 32-row tiles: the
-// workgroup streams the tiles through two LDS stages with direct HBM -> LDS
+// workgroup streams the tiles through LDS stages with direct HBM -> LDS
 // copies (range-checked, so rows past the valid length arrive as zeros),
-// issued one tile ahead of their use, with one barrier per tile.
+// issued ahead of their use -- two stages and one tile ahead, or in the
+// D = 128 dk/dv kernel three stages and two tiles ahead -- with one barrier
+// per tile.
 //
 // Launch order (FlashAttention-4 summary, "LPT scheduling for imbalanced
 // grids"): under a causal mask the last query blocks see the most keys and
