@@ -5,21 +5,29 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extr
 
 A step is one fa_fwd call over one batch of the workload's seeded synthetic
 input, resident in HBM before timing starts.  The headline workload is the
-non-causal prefill B=4, Hq=Hkv=16, Lq=Lk=1024, D=64; the causal, long-context
-GQA and split-KV decode workloads, and the follow-on variants (the GQA
-workload under a causal window of 4096 keys; the decode workload served from
-a shuffled paged cache with 16-token pages; the backward of the causal 4K and
-1K prefill workloads, one fa_bwd call per step; the causal 4K and GQA 16K
-forward with FP8 scores, one fa_fwd_fp8 call per step on Q and K quantized
-beforehand, the quantization timed separately; the causal 4K forward with
-ALiBi biases and the 1K prefill with soft-capped scores, one fa_fwd_mod call
-per step), are timed the same way and
-reported under "workloads".  Time is taken with HIP events on the stream the kernels are
-launched on (torch's current stream), bracketed by device synchronisation.
+largest single-GPU configuration, the long-context causal GQA forward
+B=1, Hq=32, Hkv=8, Lq=Lk=16384, D=128 (Q x4 on every 8th head).  The tiny,
+1K prefill, causal 4K and split-KV decode workloads, and the follow-on
+variants (the GQA workload under a causal window of 4096 keys; the decode
+workload served from a shuffled paged cache with 16-token pages; the
+backward of the causal 4K and 1K prefill workloads, one fa_bwd call per
+step; the causal 4K and GQA 16K forward with FP8 scores, one fa_fwd_fp8 call
+per step on Q and K quantized beforehand, the quantization timed separately
+and added for the end-to-end figure; the causal 4K forward with ALiBi biases
+and the 1K prefill with soft-capped scores, one fa_fwd_mod call per step),
+are reported under "workloads".
+
+Timing: W untimed warmup steps, then exactly K steps between two HIP events
+on the stream the kernels are launched on (torch's current stream),
+bracketed by device synchronisation; that gives ``ms_per_step`` and
+``value``.  Every workload is also timed in at least five trials of at least
+50 ms each (back-to-back calls between events); their median and minimum
+per-call times are reported under ``trials``.
 
 Printed: one JSON line with the metric, throughput, a roofline object for the
 dominant kernel of the headline workload and a CPU baseline (the fp64 oracle
-timed on this host on a bounded sample of the same workload).
+timed on this host's cores on a bounded sample of the same workload); the
+other forward workloads of the five carry their own CPU-baseline figure.
 """
 from __future__ import annotations
 
@@ -43,7 +51,12 @@ PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA, twice the bf16 rate
 # FP8-score forward: half the algorithmic FLOPs (S = QK^T) at the fp8 rate and
 # half (PV) at the bf16 rate, so its peak is the harmonic combination.
 PEAK_FP8_SCORES_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
-HEADLINE = "prefill_b4_h16_l1024_d64"
+HEADLINE = "gqa_causal_b1_hq32_hkv8_l16384_d128"
+# The five workloads the metric is stated for (the others are follow-on variants).
+FIVE = ["tiny_b1_h2_l256_d64", "prefill_b4_h16_l1024_d64", "causal_b2_h16_l4096_d128",
+        "gqa_causal_b1_hq32_hkv8_l16384_d128", "decode_b64_hq32_hkv8_d128_ragged"]
+TRIAL_MS = 50.0
+TRIALS = 5
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -71,7 +84,29 @@ def stored_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def time_workload(w, steps, warmup, dev):
+def timed_trials(call, est_ms):
+    """At least TRIALS trials of back-to-back calls, each lasting at least
+    TRIAL_MS (the call count per trial follows from ``est_ms``, one call's
+    time); returns the median and minimum per-call time over the trials."""
+    import statistics
+
+    import torch
+    reps = max(1, int(math.ceil(TRIAL_MS / max(est_ms, 1e-4))))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per_call = []
+    for _ in range(TRIALS):
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            call()
+        end.record()
+        torch.cuda.synchronize()
+        per_call.append(start.elapsed_time(end) / reps)
+    return {"median_ms": statistics.median(per_call), "min_ms": min(per_call), "trials": TRIALS,
+            "calls_per_trial": reps, "trial_ms": statistics.median(per_call) * reps}
+
+
+def time_workload(w, steps, warmup, dev, trials=True):
     import torch
     from exact_attention_07_amd import binding, workloads as W
 
@@ -138,6 +173,8 @@ def time_workload(w, steps, warmup, dev):
     nbytes = W.compulsory_bytes(w, inp.kv_lens)
     rec = {"ms_per_step": ms, "flops": flops, "bytes": nbytes,
            "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9}
+    if trials:
+        rec["trials"] = timed_trials(call, ms)
     if w.Lq == 1 and not w.backward:
         rec.update(bound="hbm", frac=rec["gbs"] / PEAK_HBM_GBS)
     elif w.fp8:
@@ -150,6 +187,9 @@ def time_workload(w, steps, warmup, dev):
         end.record()
         torch.cuda.synchronize()
         rec["quantize_ms"] = start.elapsed_time(end) / steps
+        e2e = ms + rec["quantize_ms"]
+        rec["end_to_end_ms"] = e2e
+        rec["end_to_end_tflops"] = flops / (e2e * 1e-3) / 1e12
     else:
         rec.update(bound="mfma", frac=rec["tflops"] / PEAK_BF16_TFLOPS)
     del call, q, k, v, o, lse, kl
@@ -157,39 +197,81 @@ def time_workload(w, steps, warmup, dev):
     return rec, inp
 
 
-def cpu_baseline(w, inp, seconds):
-    """Time the fp64 oracle on (b, h) heads of the workload until about
-    ``seconds`` of CPU work; report the oracle's algorithmic TFLOP/s (or GB/s)."""
+def host_cores() -> int:
+    """The cores this process may run on (its CPU affinity)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, inp, seconds, chunk=512):
+    """Time the fp64 oracle, as it stands, on the workload's host cores:
+    (batch, query head, chunk of up to ``chunk`` query rows) units in order,
+    one per thread of a pool of ``host_cores()`` threads (numpy's matrix
+    products and elementwise loops release the interpreter lock; BLAS is held
+    to one thread per worker), until about ``seconds`` of wall time; report
+    the algorithmic TFLOP/s of the completed units (GB/s of compulsory bytes
+    for decode)."""
+    from concurrent.futures import ThreadPoolExecutor, FIRST_COMPLETED, wait
+
     import numpy as np
     import oracle
     from exact_attention_07_amd import workloads as W
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS default
-        threads = os.cpu_count() or 1
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - part of the image
+        threadpool_limits = None
+    cores = host_cores()
     ns = W.valid_lengths(w, inp.kv_lens)
-    done_flops = done_bytes = 0
-    heads = 0
-    t0 = time.perf_counter()
-    total_heads = w.B * w.Hq
-    # (batch, query head) units in order, wrapping around the workload until
-    # about ``seconds`` of CPU work is done.
-    while time.perf_counter() - t0 < seconds:
-        b, h = divmod(heads % total_heads, w.Hq)
-        oracle.attention_rows(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens, b, h,
+    units = [(b, h, r0, min(r0 + chunk, w.Lq)) for b in range(w.B) for h in range(w.Hq)
+             for r0 in range(0, w.Lq, chunk)]
+
+    def unit_work(u):
+        b, h, r0, r1 = u
+        rows = np.arange(r0, r1)
+        oracle.attention_rows(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens, b, h, rows,
                               window=w.window)
-        pairs = W.allowed_pairs(w.Lq, ns[b], w.causal, w.window)
-        done_flops += 4 * w.D * pairs
-        done_bytes += (2 * w.Lq * w.D * 2 + w.Lq * 4) + 2 * ns[b] * w.D * 2 // (w.Hq // w.Hkv)
-        heads += 1
+        n = ns[b]
+        off = n - w.Lq
+        pairs = 0
+        for i in range(r0, r1):
+            p = off + i
+            hi = min(p + 1, n) if w.causal else n
+            lo = max(p - w.window + 1, 0) if w.window > 0 else 0
+            pairs += max(hi - lo, 0)
+        kv_bytes = 2 * n * w.D * 2 // (w.Hq // w.Hkv) if r0 == 0 else 0
+        return 4 * w.D * pairs, (r1 - r0) * (2 * w.D * 2 + 4) + kv_bytes
+
+    done_flops = done_bytes = done = 0
+    ctx = threadpool_limits(limits=1, user_api="blas") if threadpool_limits else None
+    t0 = time.perf_counter()
+    try:
+        with ThreadPoolExecutor(max_workers=cores) as ex:
+            nxt = 0
+            running = set()
+            while True:
+                while len(running) < cores and time.perf_counter() - t0 < seconds:
+                    running.add(ex.submit(unit_work, units[nxt % len(units)]))
+                    nxt += 1
+                if not running:
+                    break
+                fin, running = wait(running, return_when=FIRST_COMPLETED)
+                for f in fin:
+                    fl, by = f.result()
+                    done_flops += fl
+                    done_bytes += by
+                    done += 1
+    finally:
+        if ctx is not None:
+            ctx.restore_original_limits()
     dt = time.perf_counter() - t0
-    sample = (f"{heads} (batch, query head) units of {total_heads} in the workload "
-              f"({heads / total_heads:.2f} passes), all rows, fp64, {dt:.1f} s")
+    sample = (f"{done} (batch, query head, {chunk}-row) units of {len(units)} in the workload "
+              f"({done / len(units):.3f} passes) on {cores} threads, fp64 dense S, P, O, {dt:.1f} s")
     if w.Lq == 1:
-        return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
                 "sample": sample}
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": sample}
 
 
@@ -214,7 +296,12 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall time of the oracle baseline on the headline workload")
+    ap.add_argument("--cpu-seconds-each", type=float, default=6.0,
+                    help="wall time of the oracle baseline on each other workload of the five")
+    ap.add_argument("--no-trials", action="store_true",
+                    help="skip the 5 x 50 ms trials (profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     args = ap.parse_args()
 
@@ -236,20 +323,33 @@ def main():
 
     head = W.BY_NAME[args.workload]
     print(f"[bench] timing {head.name}: warmup {args.warmup}, steps {args.steps}", flush=True)
-    rec, inp = time_workload(head, args.steps, args.warmup, dev)
+    rec, inp = time_workload(head, args.steps, args.warmup, dev, trials=not args.no_trials)
+    tr = rec.get("trials")
     print(f"[bench] {head.name}: {rec['ms_per_step'] * 1e3:.1f} us/step"
+          + (f" (trials: median {tr['median_ms'] * 1e3:.1f}, min {tr['min_ms'] * 1e3:.1f} us)" if tr else "")
+          + f", {100 * rec['frac']:.1f}% of peak"
           + (f", quantizing Q and K {rec['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in rec else ""), flush=True)
+
+    def rounded(r):
+        return {k: (round(v, 6) if isinstance(v, float) else (rounded(v) if isinstance(v, dict) else v))
+                for k, v in r.items()}
 
     extra = {}
     if not args.no_extra:
-        for w in W.WORKLOADS[1:]:
+        for w in W.WORKLOADS:
             if w.name == head.name:
                 continue
             steps = max(3, min(args.steps, 20))
-            r, _ = time_workload(w, steps, max(2, min(args.warmup, 5)), dev)
-            extra[w.name] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
-            print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.1f} us/step, "
-                  f"{r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s"
+            r, winp = time_workload(w, steps, max(2, min(args.warmup, 5)), dev, trials=not args.no_trials)
+            if w.name in FIVE and not args.no_cpu:
+                print(f"[bench] CPU oracle baseline on {w.name} (~{args.cpu_seconds_each:.0f} s)", flush=True)
+                r["cpu_baseline"] = cpu_baseline(w, winp, args.cpu_seconds_each)
+            del winp
+            extra[w.name] = rounded(r)
+            tr = r.get("trials")
+            print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.1f} us/step"
+                  + (f" (trials: median {tr['median_ms'] * 1e3:.1f}, min {tr['min_ms'] * 1e3:.1f} us)" if tr else "")
+                  + f", {r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s, {100 * r['frac']:.1f}% of peak"
                   + (f", quantizing Q and K {r['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in r else ""), flush=True)
 
     decode = head.Lq == 1
@@ -274,6 +374,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "trials": rounded(rec["trials"]) if "trials" in rec else None,
         "workloads": extra,
         "kernel_source_hash": kernel_source_hash(),
     }

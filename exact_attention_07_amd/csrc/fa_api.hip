@@ -137,6 +137,14 @@ size_t split_workspace_bytes(const Shape& s, const SplitPlan& pl) {
     return rows * pl.num_splits * ((size_t)s.D + 1) * sizeof(float);
 }
 
+// Workgroup placement of the prefill kernels over the eight XCDs (dispatched
+// round-robin).  With grouped-query attention, the query heads of a KV head
+// can differ widely in cost (a head whose scores spread widely may switch to
+// split probabilities), so instead of whole KV heads per XCD, every XCD takes
+// balanced pairs of query blocks (i, n - 1 - i) of all heads; the r query
+// heads of a (KV head, block) stay adjacent, so they share K/V tiles in L2.
+int xcd_spread(int r, int n_qblocks) { return (r > 1 && n_qblocks % 16 == 0) ? 1 : 0; }
+
 bool use_split_path(const Shape& s, const Extra& x) {
     if (x.requested_splits > 0 || x.page_table) return true;
     return s.Lq == 1;
@@ -213,6 +221,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
         p.n_qblocks = (s.Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
         const int units = s.B * s.Hkv;
         p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+        p.xcd_spread = xcd_spread(r, p.n_qblocks);
         p.window = x.window;
         p.scale = scale;
         p.c = c;
@@ -223,6 +232,11 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
         return FA_OK;
     }
 
+    // The split kernels address the r * Lq query rows that share a KV head
+    // through one buffer descriptor with 32-bit byte offsets.
+    if ((long long)r * s.Lq * s.D * 2 > (long long)UINT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "split-KV path: (Hq/Hkv) * Lq * D * 2 = %lld bytes exceeds the "
+                    "32-bit offsets of one KV head's packed query rows", (long long)r * s.Lq * s.D * 2);
     const SplitPlan pl = plan_splits(s, x.requested_splits, cu_count(), visible_span(s, x.window));
     void* ws = nullptr;
     st = get_workspace(split_workspace_bytes(s, pl), &ws);
@@ -379,6 +393,7 @@ int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
     p.n_qblocks = (Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
     const int units = B * Hkv;
     p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+    p.xcd_spread = xcd_spread(Hq / Hkv, p.n_qblocks);
     p.window = 0;
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
@@ -440,6 +455,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
     p.n_qblocks = (Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
     const int units = B * Hkv;
     p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+    p.xcd_spread = xcd_spread(Hq / Hkv, p.n_qblocks);
     p.window = 0;
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;

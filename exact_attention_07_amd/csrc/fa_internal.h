@@ -28,6 +28,7 @@ struct PrefillParams {
     int r;                 // query heads per KV head
     int n_qblocks;         // ceil(Lq / kPrefillRows)
     int xcd_units;         // (B * Hkv) / 8 when divisible by 8, else 0
+    int xcd_spread;        // 1: every XCD takes balanced pairs of query blocks of all heads (GQA)
     int window;            // causal window width (keys j with 0 <= pos_i - j < window); 0 = none
     float scale;           // softmax scale
     float c;               // scale * log2(e): scores enter exp2 as s * c

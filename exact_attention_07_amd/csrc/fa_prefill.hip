@@ -79,6 +79,23 @@ struct Const { static constexpr int value = N; };
 constexpr float kTau = 8.0f;
 constexpr float kTauSum = 256.0f;
 
+// Exact probabilities for rows that a few keys dominate (D = 128 kernels).  P
+// enters the PV product rounded to bf16 (relative error up to 2^-8), which
+// moves O by up to 2^-8 sum_j P_j |v_j - O|: on rows that a few keys dominate
+// that reaches a few 1e-3 of an output of magnitude 2-4.  Such a row is
+// recognised when its reference moves (the row max is known exactly then):
+// its largest p is at least kPeakFrac of its running sum.  Once kSplitRows
+// rows of a workgroup are (a head whose scores spread widely), the workgroup
+// switches, for the rest of its KV loop, to split probabilities: the residual
+// p - bf16(p), itself rounded to bf16, goes through a second product with the
+// same V fragments, so every weight is exact to ~2^-16, and the normaliser
+// takes the fp32 sum of p for those tiles.  The switch is one counter in LDS
+// that every wavefront adds to and reads at its next vector phase: all
+// wavefronts of a workgroup then do the same work per tile, so the phases stay
+// balanced.
+constexpr float kPeakFrac = 1.0f / 2.0f;
+constexpr int kSplitRows = 16;              // dominated rows that switch a workgroup to split probabilities
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // FP8 instantiation: S^T = K Q^T from E4M3 codes on
@@ -124,6 +141,7 @@ prefill_kernel(PrefillParams p) {
     static_assert(CAUSAL || !WINDOW, "the window is causal");
     static_assert(!FP8 || (D == 128 && !WINDOW), "the FP8 scores are built for D = 128 without a window");
     static_assert(MOD == kModNone || (!FP8 && !WINDOW), "score modifiers are built for the bf16 kernel without a window");
+    constexpr bool CORR = D == 128;         // residual correction of dominant probabilities
     constexpr int KSQ = FP8 ? D / 64 : KS;  // k-steps of S^T
     constexpr int NIK = FP8 ? BN * D / (NT * 16) : NI;   // 16-byte copies per thread per K tile
     static_assert(NIK >= 1, "a K tile must split evenly over the workgroup");
@@ -131,17 +149,36 @@ prefill_kernel(PrefillParams p) {
 
     // K buffers at [0, NB TILE), V buffers at [NB TILE, 2 NB TILE).
     __shared__ __attribute__((aligned(16))) bf16 smem[2 * NB * TILE];
+    // bf16 residuals of corrected 16-key chunks: [wave][chunk][lane], written in
+    // a wavefront's vector phase and read in its next matrix phase.
+    constexpr int NCH = KB * 2;                     // 16-key chunks per tile
+    __shared__ __attribute__((aligned(16))) bf16x8 plo_lds[D == 128 ? NW * NCH * 64 : 1];
+    __shared__ int split_rows;              // rows of the workgroup found dominated by a few keys
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int grp = w >> 2;                 // ping-pong group; waves w and w + 4 share a SIMD
     const int l = tid & 63;
     const int hi = l >> 5;                  // which half of the wave (0 or 1)
+    if (tid == 0) split_rows = 0;           // visible after the prologue's first barrier
 
     // ---- workgroup -> (b, h, query block) ---------------------------------
     const int L = blockIdx.x;
     int qb_rev, unit, hg;
-    if (p.xcd_units > 0) {
+    if (p.xcd_spread) {
+        // XCD x owns the query-block pairs (n-1-q, q) for q = x, x+8, ...: first
+        // its heavy blocks in descending order, then its light ones; within a
+        // block, every (batch, KV head) with its r query heads adjacent.
+        const int xcd = L & 7, slot = L >> 3;
+        const int per = p.B * p.Hq;
+        const int j = slot / per;
+        const int rem = slot - j * per;
+        const int M = p.n_qblocks >> 4;      // pairs per XCD
+        const int q = j < M ? xcd + 8 * j : xcd + 8 * (2 * M - 1 - j);
+        qb_rev = j < M ? q : p.n_qblocks - 1 - q;
+        unit = rem / p.r;
+        hg = rem % p.r;
+    } else if (p.xcd_units > 0) {
         const int xcd = L & 7, slot = L >> 3;
         const int per = p.xcd_units * p.r;
         qb_rev = slot / per;
@@ -310,7 +347,8 @@ prefill_kernel(PrefillParams p) {
     // ---- online-softmax state ----------------------------------------------
     const float c = p.c;
     float ref = kNegInf;                    // reference r = (running max) * c; -inf while the row is empty
-    float ell_e = 0.0f, ell_r = 0.0f;       // this lane's halves of sum p and of sum bf16(p)
+    float ell_e = 0.0f;                     // the row's sum of p (both lanes of the row hold it)
+    float ell_r = 0.0f;                     // this lane's half of the row's sum of bf16(p)
     f32x16 acc[DB];                         // O^T accumulator: rows d, column = this lane's query
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
@@ -319,6 +357,8 @@ prefill_kernel(PrefillParams p) {
     // rounded values) while its score products run.
     float pe[KB][2][8];
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    int corr = 0;                           // the next PV product takes the residual products (wave-uniform)
+    bool split = false;                     // this wavefront splits its probabilities (wave-uniform, sticky)
     float ksc_next = k_scale_of(0);         // FP8: s_k of the tile softmax_tile handles next
     // Modifier constants in raw-score units.
     const float mod_a = MOD == kModAlibi ? p.alibi_slopes[h] / p.scale
@@ -329,6 +369,8 @@ prefill_kernel(PrefillParams p) {
     // fp32 row sum, and the rare reference move.
     auto softmax_tile = [&](int t) __attribute__((always_inline)) {
         const int k0 = tile_abs(t) * BN;
+        // The workgroup's split flag, read early (used after the exponentials).
+        const int flag_seen = CORR ? split_rows : 0;
         const float ct = FP8 ? cq * ksc_next : c;   // this tile's exponent scale
         if (FP8) ksc_next = k_scale_of(t + 1);
         // ALiBi: |pos_i - pos_j| = |base - K_v| with base = qpos - k0 - 8 hi
@@ -404,8 +446,11 @@ prefill_kernel(PrefillParams p) {
         // rise by about 2 kTau before the next move), with A and l rescaled,
         // and the tile is recomputed.  The move is decided per wavefront, so
         // the headroom keeps it rare even on rows whose max keeps climbing.
-        const float row_sum = sum_with_partner((se[0] + se[1]) + (se[2] + se[3]));
+        float se_l = (se[0] + se[1]) + (se[2] + se[3]);
+        float row_sum = sum_with_partner(se_l);
         const bool move = ref == kNegInf || !(row_sum <= kTauSum);
+        if constexpr (CORR)   // counted by all wavefronts at earlier phases
+            split = split || __builtin_amdgcn_readfirstlane(flag_seen) >= kSplitRows;
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
             if constexpr (MOD == kModAlibi) {
                 // The row max is of the biased scores: apply the bias here.
@@ -430,8 +475,35 @@ prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
             exponentials();
+            se_l = (se[0] + se[1]) + (se[2] + se[3]);
+            row_sum = sum_with_partner(se_l);
+            if constexpr (CORR) {
+                // After the move the row's largest p is exactly 2^-kTau.
+                const bool dominated = shift && 1.0f / kTauSum >= kPeakFrac * (ell_e + row_sum);
+                const uint64_t dm = __builtin_amdgcn_ballot_w64(dominated && hi == 0);   // one lane per row
+                if (!split && dm != 0 && l == 0) atomicAdd(&split_rows, (int)__builtin_popcountll(dm));
+            }
         }
-        ell_e += (se[0] + se[1]) + (se[2] + se[3]);
+        corr = 0;
+        if constexpr (CORR) {
+            if (split) {
+                // Residuals of every chunk to LDS for the next matrix phase; the
+                // normaliser takes this tile's fp32 sum (the matrix phase then
+                // leaves out its rounded sum).
+#pragma unroll
+                for (int cc = 0; cc < NCH; ++cc) {
+                    const float* e = pe[cc / 2][cc % 2];
+                    const bf16x8 hi8 = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+                    plo_lds[(w * NCH + cc) * 64 + l] =
+                        to_bf16x8(e[0] - (float)hi8[0], e[1] - (float)hi8[1], e[2] - (float)hi8[2],
+                                  e[3] - (float)hi8[3], e[4] - (float)hi8[4], e[5] - (float)hi8[5],
+                                  e[6] - (float)hi8[6], e[7] - (float)hi8[7]);
+                }
+                ell_r += se_l;
+                corr = 1;
+            }
+        }
+        ell_e += row_sum;
     };
 
     // Matrix phase M(t) as one software pipeline over its products: the KB*KS
@@ -485,7 +557,7 @@ prefill_kernel(PrefillParams p) {
                 const int kb = i / KSQ, ks = i % KSQ;
                 s[kb] = score_mfma(kfrag[i], ks, ks == 0 ? zero_f32x16() : s[kb]);
                 if (i % (NQ / NP) == 0) convert_p(i / (NQ / NP));
-                if (i == NQ - 1) ell_r += sr[0] + sr[1];
+                if (i == NQ - 1) ell_r += corr ? 0.0f : sr[0] + sr[1];
             } else {
                 const int f = i - NQ;
                 const int db = f / (KB * 2), kb = (f / 2) % KB, half = f % 2;
@@ -500,6 +572,32 @@ prefill_kernel(PrefillParams p) {
             mfma_op(i);
             if (i + AHEAD < NOPS) read_op(i + AHEAD);
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // Residual products of a splitting wavefront (wave-uniform): the same V
+        // fragments times bf16(p - bf16(p)).
+        if (CORR && corr != 0) {
+            // Side-effect marker: keeps the compiler from executing these
+            // products speculatively (as a select) on the common path.
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int c = 0; c < NP; ++c) {
+                {
+                    const int kb = c / 2, half = c % 2;
+                    const bf16x8 lo = plo_lds[(w * NP + c) * 64 + l];
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const int row0 = kb * 32 + half * 16 + vrow;
+                        const int col = db * 32 + vcol;
+                        const bf16* base = Vs + row0 * D + (((col >> 3) ^ vxor) * 8) + (col & 7);
+                        const bf16x4 v0 = lds_read_transposed(base);
+                        const bf16x4 v1 = lds_read_transposed(base + 4 * D);
+                        bf16x8 fr;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { fr[e] = v0[e]; fr[4 + e] = v1[e]; }
+                        acc[db] = mfma_32x32x16(fr, lo, acc[db]);
+                    }
+                }
+            }
         }
     };
 
@@ -546,7 +644,7 @@ prefill_kernel(PrefillParams p) {
     wait_all_vector_loads();                // copies past the last tile (zero-range) drained
 
     // ---- epilogue: O = A / l_r, LSE = ln 2 * (r + log2 l_e) ------------------
-    const float le = sum_with_partner(ell_e);
+    const float le = ell_e;
     const float lr = sum_with_partner(ell_r);
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
     if (qrow < p.Lq) {

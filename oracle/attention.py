@@ -51,8 +51,9 @@ def as_f64(x) -> np.ndarray:
 
 
 def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None, window=0,
-               alibi_slope=0.0, softcap=0.0):
-    """Materialised attention for one (batch, head): returns (O, LSE) in fp64.
+               alibi_slope=0.0, softcap=0.0, return_weights=False):
+    """Materialised attention for one (batch, head): returns (O, LSE) in fp64
+    (with ``return_weights`` also the probability matrix P and the value rows).
 
     q: [Lq, D]; k: [Lk, D]; v: [Lk, Dv].  q_pos / k_pos are the absolute
     token positions of the rows (default 0..L-1); with ``causal`` a pair is
@@ -66,6 +67,8 @@ def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None, window=0,
     q_pos = np.arange(Lq) if q_pos is None else np.asarray(q_pos)
     k_pos = np.arange(Lk) if k_pos is None else np.asarray(k_pos)
     if Lk == 0:
+        if return_weights:
+            return np.zeros((Lq, Dv)), np.full(Lq, -np.inf), np.zeros((Lq, 0)), v
         return np.zeros((Lq, Dv)), np.full(Lq, -np.inf)
 
     # Write the whole score matrix.
@@ -94,6 +97,8 @@ def dense_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None, window=0,
     O = P @ v
     O[~has_key] = 0.0
     lse = np.where(has_key, shift + np.log(safe_ell), -np.inf)
+    if return_weights:
+        return O, lse, P, v
     return O, lse
 
 
@@ -104,11 +109,17 @@ def _kv_len(kv_lens, b, Lk):
 
 
 def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None, window=0,
-                   alibi_slopes=None, softcap=0.0):
+                   alibi_slopes=None, softcap=0.0, return_weights=False, trim_keys=False):
     """(O, LSE) of selected query rows of one (b, h) of a batched problem.
 
     Rows are evaluated by the same definition as ``attention_forward``; this
-    lets full-size problems be checked on sampled rows.
+    lets full-size problems be checked on sampled rows or row chunks.  With
+    ``trim_keys``, keys that the causal mask (or the window) removes for EVERY
+    selected row are left out of the materialised S: they would be -inf
+    there, add exp(-inf) = 0 to every sum and never be a row max, so the
+    result is the same up to the rounding order of the matrix products, and a
+    chunk of early causal rows costs what its allowed keys cost.
+    ``return_weights`` also returns P and the value rows it weights.
     """
     Hq, Lq = q.shape[1], q.shape[2]
     Hkv, Lk = k.shape[1], k.shape[2]
@@ -116,12 +127,18 @@ def attention_rows(q, k, v, scale, causal, kv_lens, b, h, rows=None, window=0,
     g = h // r
     n = _kv_len(kv_lens, b, Lk)
     rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
-    q_bh = as_f64(q[b, h])[rows]
-    k_bg = as_f64(k[b, g, :n])
-    v_bg = as_f64(v[b, g, :n])
     q_pos = (n - Lq) + rows          # bottom-right: the queries end the cache
+    lo, hi = 0, n
+    if trim_keys and (causal or window > 0) and rows.size:
+        hi = int(min(n, max(q_pos.max() + 1, 0)))
+        if window > 0:
+            lo = int(min(hi, max(q_pos.min() - window + 1, 0)))
+    q_bh = as_f64(q[b, h])[rows]
+    k_bg = as_f64(k[b, g, lo:hi])
+    v_bg = as_f64(v[b, g, lo:hi])
     slope = 0.0 if alibi_slopes is None else float(as_f64(alibi_slopes)[h])
-    return dense_head(q_bh, k_bg, v_bg, scale, causal, q_pos, np.arange(n), window, slope, softcap)
+    return dense_head(q_bh, k_bg, v_bg, scale, causal, q_pos, np.arange(lo, hi), window, slope, softcap,
+                      return_weights)
 
 
 def attention_forward(q, k, v, scale, causal=False, kv_lens=None, window=0, alibi_slopes=None,

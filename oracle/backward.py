@@ -19,6 +19,11 @@ Sources:
 This module materialises S, P, dP and dS for one (batch, query head) at a
 time; it does not use a saved LSE (P comes from the definition of softmax),
 so it checks the GPU path's reconstruction rather than sharing it.
+
+``o_given`` evaluates the same formulas with delta_i = G_i . o_given_i for a
+given output o_given instead of the exact O (everything else unchanged): the
+gradient a backward computes when it is handed a stored, rounded forward
+output, as the section's recomputation does.
 """
 from __future__ import annotations
 
@@ -27,11 +32,12 @@ import numpy as np
 from .attention import as_f64
 
 
-def dense_backward_head(q, k, v, g, scale, causal=False, q_pos=None, k_pos=None, window=0):
+def dense_backward_head(q, k, v, g, scale, causal=False, q_pos=None, k_pos=None, window=0,
+                        o_given=None):
     """(dQ, dK, dV) of one (batch, head) in fp64 for upstream gradient g.
 
     q: [Lq, D]; k: [Lk, D]; v: [Lk, Dv]; g: [Lq, Dv].  Masks as in
-    ``attention.dense_head``.
+    ``attention.dense_head``.  ``o_given`` [Lq, Dv]: form delta from it.
     """
     q, k, v, g = as_f64(q), as_f64(k), as_f64(v), as_f64(g)
     Lq, Lk = q.shape[0], k.shape[0]
@@ -58,25 +64,27 @@ def dense_backward_head(q, k, v, g, scale, causal=False, q_pos=None, k_pos=None,
     # Backward through O = P V, the row softmax and S = scale * Q K^T.
     dV = P.T @ g
     dP = g @ v.T
-    delta = (g * O).sum(axis=1)
+    delta = (g * (O if o_given is None else as_f64(o_given))).sum(axis=1)
     dS = P * (dP - delta[:, None])
     dQ = scale * (dS @ k)
     dK = scale * (dS.T @ q)
     return dQ, dK, dV
 
 
-def attention_backward(q, k, v, g, scale, causal=False, kv_lens=None, window=0):
+def attention_backward(q, k, v, g, scale, causal=False, kv_lens=None, window=0, o_given=None):
     """Batched gradients for [B, H, L, D] inputs: dQ [B, Hq, Lq, D],
     dK [B, Hkv, Lk, D], dV [B, Hkv, Lk, Dv] in fp64.  Queries sit at the end
     of each sequence's valid keys (bottom-right alignment, as in the
     forward); keys at or past kv_lens[b] get zero gradient; a KV head's
-    gradients sum over the query heads h with floor(h / r) equal to it."""
+    gradients sum over the query heads h with floor(h / r) equal to it.
+    ``o_given`` [B, Hq, Lq, Dv]: delta from this output (module docstring)."""
     q, k, v, g = as_f64(q), as_f64(k), as_f64(v), as_f64(g)
     B, Hq, Lq = q.shape[0], q.shape[1], q.shape[2]
     Hkv, Lk = k.shape[1], k.shape[2]
     assert Hq % Hkv == 0, "query heads must be a multiple of KV heads"
     r = Hq // Hkv
     lens = None if kv_lens is None else as_f64(kv_lens)
+    og = None if o_given is None else as_f64(o_given)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -86,7 +94,8 @@ def attention_backward(q, k, v, g, scale, causal=False, kv_lens=None, window=0):
         for h in range(Hq):
             gk = h // r
             dqh, dkh, dvh = dense_backward_head(q[b, h], k[b, gk, :n], v[b, gk, :n], g[b, h],
-                                                scale, causal, q_pos, np.arange(n), window)
+                                                scale, causal, q_pos, np.arange(n), window,
+                                                None if og is None else og[b, h])
             dq[b, h] = dqh
             dk[b, gk, :n] += dkh
             dv[b, gk, :n] += dvh

@@ -3,18 +3,25 @@
 Used only to pin the dense definition (and to be pinned by it); it shares no
 code with ``attention.py``.  Sources:
   * FlashAttention from Scratch (ryhuang.blog), §4.1 "Maintain three
-    quantities": per query row the state (m, l, u) over the keys seen so far;
-    when a tile arrives, m' = max(m, tile max), alpha = exp(m - m'),
-    l' = alpha l + sum exp(s - m'), u' = alpha u + sum exp(s - m') v; after the
-    last tile o = u / l;
-  * §4.4 "Handle the empty state deliberately": start from m = -inf, l = 0,
-    u = 0, and never form -inf - (-inf);
+    quantities": every query row carries a reference exponent, a normaliser
+    and a weighted sum of value rows, all relative to the reference, over the
+    keys seen so far; a new tile raises the reference to its row maximum if
+    larger, scales the old normaliser and sum by e^(old - new) and adds the
+    tile's terms; the output is the sum over the normaliser;
+  * §4.4 "Handle the empty state deliberately": the state starts empty
+    (reference -inf, zero normaliser and sum), and no -inf - (-inf) is ever
+    formed;
   * §11.3 "Derive conditional rescaling correctly" and "FlashAttention-4:
     Blackwell Attention Kernel Co-Design", "Conditional online-softmax
-    rescaling": keep the reference r unless a tile's max t exceeds it by more
-    than tau; the reference is first set from the first tile with a valid key;
+    rescaling": the reference may stay put while a tile's maximum exceeds it
+    by at most tau; it is first set by the first tile that holds a valid key;
   * FlashAttention Cheat Sheet (mxino.github.io), §5 "Why online softmax is
-    globally exact": tile order may change without changing the result.
+    globally exact": the order in which tiles are visited does not change the
+    result.
+
+Structure: the state of all rows of a query block lives in one ``RowState``;
+the key tiles are the outer loop (in the requested order) and each query
+block absorbs every tile, so tile order and tile sizes are free parameters.
 """
 from __future__ import annotations
 
@@ -27,6 +34,44 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+class RowState:
+    """Running state of a set of query rows: ``ref`` (the exponent every
+    stored term is taken relative to), ``norm`` (sum of e^(s - ref)) and
+    ``acc`` (sum of e^(s - ref) v)."""
+
+    def __init__(self, rows: int, dv: int):
+        self.ref = np.full(rows, -np.inf)
+        self.norm = np.zeros(rows)
+        self.acc = np.zeros((rows, dv))
+
+    def absorb(self, scores: np.ndarray, values: np.ndarray, tau=None) -> np.ndarray:
+        """Fold one tile in: ``scores`` [rows, n] (masked pairs -inf) and the
+        tile's value rows [n, dv].  Returns the factor e^(old ref - new ref)
+        the earlier terms were multiplied by."""
+        peak = scores.max(axis=1)
+        raised = np.maximum(self.ref, peak)
+        if tau is not None:
+            with np.errstate(invalid="ignore"):
+                # -inf - (-inf) is NaN and compares false: an empty row always takes the raise
+                keep = (peak - self.ref) <= tau
+            raised = np.where(keep, self.ref, raised)
+        anchor = np.where(np.isfinite(raised), raised, 0.0)
+        factor = np.exp(self.ref - anchor)        # an empty state gives 0
+        terms = np.exp(scores - anchor[:, None])
+        self.norm = factor * self.norm + terms.sum(axis=1)
+        self.acc = factor[:, None] * self.acc + terms @ values
+        self.ref = raised
+        return factor
+
+    def result(self):
+        """(O, LSE): acc / norm and ref + log(norm), or (0, -inf) for a row
+        that absorbed no valid key."""
+        seen = self.norm > 0
+        den = np.where(seen, self.norm, 1.0)
+        out = np.where(seen[:, None], self.acc / den[:, None], 0.0)
+        return out, np.where(seen, self.ref + np.log(den), -np.inf)
+
+
 def streaming_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None,
                    block_q=32, block_k=64, kv_order=None, tau=None, trace=None):
     """Tile-by-tile forward for one head; returns (O, LSE) in fp64.
@@ -34,8 +79,10 @@ def streaming_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None,
     block_q / block_k: tile sizes.  kv_order: optional permutation of the KV
     tile indices (tile t covers keys [t*block_k, (t+1)*block_k)).  tau: None
     for the plain recurrence, else the conditional-rescale threshold in
-    natural-log units.  trace: optional list that receives, per query block
-    and per visited tile, a dict with the state after that tile.
+    natural-log units.  trace: optional list that receives, per visited
+    (query block, tile) pair in visiting order, a dict with the state after
+    it in the pages' notation (m = reference, ell = normaliser, u = sum,
+    alpha = the factor applied to the earlier terms).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     Lq, Lk, Dv = q.shape[0], k.shape[0], v.shape[1]
@@ -45,40 +92,21 @@ def streaming_head(q, k, v, scale, causal=False, q_pos=None, k_pos=None,
     order = list(range(n_tiles)) if kv_order is None else list(kv_order)
     assert sorted(order) == list(range(n_tiles)), "kv_order must permute the tiles"
 
+    blocks = [(r0, min(r0 + block_q, Lq)) for r0 in range(0, Lq, block_q)]
+    states = [RowState(r1 - r0, Dv) for r0, r1 in blocks]
+    for t in order:
+        keys = slice(t * block_k, min((t + 1) * block_k, Lk))
+        for (r0, r1), st in zip(blocks, states):
+            tile = scale * (q[r0:r1] @ k[keys].T)
+            if causal:
+                tile = np.where(k_pos[keys][None, :] <= q_pos[r0:r1][:, None], tile, -np.inf)
+            factor = st.absorb(tile, v[keys], tau)
+            if trace is not None:
+                trace.append({"q_block": r0, "tile": t, "m": st.ref.copy(), "alpha": factor.copy(),
+                              "ell": st.norm.copy(), "u": st.acc.copy()})
+
     out = np.zeros((Lq, Dv))
     lse = np.full(Lq, -np.inf)
-    for i0 in range(0, Lq, block_q):
-        qt = q[i0:i0 + block_q]
-        qp = q_pos[i0:i0 + block_q]
-        rows = qt.shape[0]
-        m = np.full(rows, -np.inf)       # running reference (max, or stale max under tau)
-        ell = np.zeros(rows)
-        u = np.zeros((rows, Dv))
-        for t in order:
-            j0 = t * block_k
-            kt, vt, kp = k[j0:j0 + block_k], v[j0:j0 + block_k], k_pos[j0:j0 + block_k]
-            s = scale * (qt @ kt.T)
-            if causal:
-                s[kp[None, :] > qp[:, None]] = -np.inf
-            tile_max = s.max(axis=1)
-            if tau is None:
-                new_m = np.maximum(m, tile_max)
-            else:
-                with np.errstate(invalid="ignore"):
-                    jump = tile_max - m      # +inf (or NaN) while the row has no reference yet
-                move = ~(jump <= tau)
-                new_m = np.where(move, np.maximum(m, tile_max), m)
-            shift = np.where(np.isfinite(new_m), new_m, 0.0)
-            alpha = np.exp(m - shift)        # m = -inf gives 0, never NaN
-            p = np.exp(s - shift[:, None])
-            ell = alpha * ell + p.sum(axis=1)
-            u = alpha[:, None] * u + p @ vt
-            m = new_m
-            if trace is not None:
-                trace.append({"q_block": i0, "tile": t, "m": m.copy(), "alpha": alpha.copy(),
-                              "ell": ell.copy(), "u": u.copy()})
-        ok = ell > 0
-        safe = np.where(ok, ell, 1.0)
-        out[i0:i0 + rows] = np.where(ok[:, None], u / safe[:, None], 0.0)
-        lse[i0:i0 + rows] = np.where(ok, m + np.log(safe), -np.inf)
+    for (r0, r1), st in zip(blocks, states):
+        out[r0:r1], lse[r0:r1] = st.result()
     return out, lse

@@ -80,6 +80,15 @@ def test_negative_split_count_is_rejected(lib):
     assert call(lib, splits=-3) == binding.FA_ERR_INVALID_ARG
 
 
+def test_split_path_rejects_packed_rows_past_32_bit_offsets(lib):
+    # 32 query heads per KV head x 2^19 queries x 128 x 2 bytes = 2^32: the
+    # packed rows of one KV head no longer fit the split kernels' 32-bit
+    # buffer offsets, so the split path refuses before any launch.
+    st = call(lib, B=1, Hq=32, Hkv=1, Lq=1 << 19, Lk=8, D=128, splits=1)
+    assert st == binding.FA_ERR_INVALID_ARG
+    assert b"32-bit" in lib.fa_last_error()
+
+
 def test_status_strings(lib):
     assert lib.fa_status_string(0).decode() == "FA_OK"
     for s in (1, 2, 3):

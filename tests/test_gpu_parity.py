@@ -21,8 +21,7 @@ import torch
 import oracle
 from exact_attention_07_amd import binding, workloads as W
 
-sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import compare, sample_rows  # noqa: E402
+from tests.parity import compare, compare_all_rows  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -69,32 +68,30 @@ def report(name, metrics):
 # ---------------------------------------------------------------------------
 
 def test_workload_tiny(dev):
-    case = W.make_inputs(W.WORKLOADS[0])
+    w = W.WORKLOADS[0]
+    case = W.make_inputs(w)
     o, lse = run(case, dev)
     ref_o, ref_lse = full_reference(case)
-    report("tiny", compare(o, lse, ref_o, ref_lse))
+    report(w.name, compare(o, lse, ref_o, ref_lse, name=f"workload:{w.name}"))
 
 
 def test_workload_prefill_1k(dev):
-    case = W.make_inputs(W.WORKLOADS[1])
+    w = W.WORKLOADS[1]
+    case = W.make_inputs(w)
     o, lse = run(case, dev)
     ref_o, ref_lse = full_reference(case)
-    report("prefill_1k", compare(o, lse, ref_o, ref_lse))
+    report(w.name, compare(o, lse, ref_o, ref_lse, name=f"workload:{w.name}"))
 
 
 @pytest.mark.parametrize("index", [2, 3])
-def test_workload_causal_sampled(dev, index):
+def test_workload_causal_every_row(dev, index):
+    # Every row of every head, at full size, in the launch configuration the
+    # benchmark times; the oracle runs in row chunks on the host's cores.
     w = W.WORKLOADS[index]
     case = W.make_inputs(w)
     o, lse = run(case, dev)
-    rows = sample_rows(w.Lq, seed=index)
-    go, gl, ro, rl = [], [], [], []
-    for b in range(w.B):
-        for h in range(w.Hq):
-            ref_o, ref_lse = oracle.attention_rows(case.q, case.k, case.v, case.scale, True,
-                                                   case.kv_lens, b, h, rows)
-            go.append(o[b, h, rows]); gl.append(lse[b, h, rows]); ro.append(ref_o); rl.append(ref_lse)
-    metrics = compare(torch.stack(go), torch.stack(gl), np.stack(ro), np.stack(rl))
+    metrics = compare_all_rows(case, o, lse, name=f"workload:{w.name}")
+    assert metrics["rows"] == w.B * w.Hq * w.Lq
     report(w.name, metrics)
 
 
@@ -103,7 +100,7 @@ def test_workload_decode(dev):
     case = W.make_inputs(w)
     o, lse = run(case, dev)
     ref_o, ref_lse = full_reference(case)
-    report(w.name, compare(o, lse, ref_o, ref_lse))
+    report(w.name, compare(o, lse, ref_o, ref_lse, name=f"workload:{w.name}"))
 
 
 # ---------------------------------------------------------------------------

@@ -7,7 +7,8 @@ The shapes are drawn from a fixed seed: head dimension, batch, KV heads and
 query heads per KV head, query and key lengths from 1 to a few hundred (so
 tiles, query blocks and split partitions end raggedly), causal or not,
 ragged or full lengths, windows, ALiBi slopes or a soft-cap.  Each case is
-small enough for the oracle to finish in well under a second.
+small enough for the oracle to finish in well under a second.  Window and
+ALiBi cases use the variant bar of tests/parity.py.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ import torch
 
 import oracle
 from exact_attention_07_amd import binding, workloads as W
-from tests.parity import compare
+from tests.parity import compare, variant_spread
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +73,7 @@ def test_random_window(dev, seed):
     o, lse = binding.fa_fwd_window(c.q.to(dev), c.k.to(dev), c.v.to(dev), w, scale=c.scale, kv_lens=kl)
     torch.cuda.synchronize()
     ro, rl = oracle.attention_forward(c.q, c.k, c.v, c.scale, True, c.kv_lens, window=w)
-    compare(o, lse, ro, rl)
+    compare(o, lse, ro, rl, spread=variant_spread(c, window=w))
 
 
 @pytest.mark.parametrize("seed", SEEDS[:12])
@@ -87,6 +88,7 @@ def test_random_modifiers(dev, seed):
                                     kv_lens=kl, alibi_slopes=sl.to(dev))
         torch.cuda.synchronize()
         ro, rl = oracle.attention_forward(c.q, c.k, c.v, c.scale, causal, c.kv_lens, alibi_slopes=sl.numpy())
+        spread = variant_spread(c, alibi_slopes=sl.numpy())
     else:
         cap = float(1.0 + 9.0 * torch.rand(1, generator=g))
         q = (c.q.float() * 3).to(torch.bfloat16)
@@ -94,7 +96,8 @@ def test_random_modifiers(dev, seed):
                                     kv_lens=kl, softcap=cap)
         torch.cuda.synchronize()
         ro, rl = oracle.attention_forward(q, c.k, c.v, c.scale, causal, c.kv_lens, softcap=cap)
-    compare(o, lse, ro, rl)
+        spread = None
+    compare(o, lse, ro, rl, spread=spread)
 
 
 @pytest.mark.parametrize("seed", SEEDS[:12])
@@ -162,4 +165,4 @@ def test_random_paged(dev, seed):
                                   causal=causal, window=w, scale=c.scale)
     torch.cuda.synchronize()
     ro, rl = oracle.paged_attention_forward(c.q, kc, vc, table, c.kv_lens, P, c.scale, causal, w)
-    compare(o, lse, ro, rl)
+    compare(o, lse, ro, rl, spread=variant_spread(c, window=w) if w else None)

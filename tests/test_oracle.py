@@ -882,6 +882,66 @@ def check_fp8_attention(orc):
     assert rmse(Oi) < 0.02
 
 
+def check_trimmed_rows(orc):
+    # Leaving out the keys that the causal mask (or window) removes for every
+    # selected row changes nothing but rounding order: chunks of rows with
+    # trimming against the untrimmed rows, for causal, windowed and ragged
+    # problems, including chunks that end before the first key.
+    r = np.random.default_rng(53)
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 37, 45, 8
+    q = r.standard_normal((B, Hq, Lq, D))
+    k = r.standard_normal((B, Hkv, Lk, D))
+    v = r.standard_normal((B, Hkv, Lk, D))
+    for causal, w, lens in ((True, 0, None), (True, 6, None), (True, 0, [45, 20]), (True, 9, [30, 3]),
+                            (False, 0, [45, 11])):
+        for b in range(B):
+            for h in (0, 3):
+                for r0, r1 in ((0, 5), (5, 19), (19, 37), (0, 37), (36, 37)):
+                    rows = np.arange(r0, r1)
+                    o1, l1 = orc.attention_rows(q, k, v, 0.4, causal, lens, b, h, rows, window=w,
+                                                trim_keys=True)
+                    o2, l2 = orc.attention_rows(q, k, v, 0.4, causal, lens, b, h, rows, window=w)
+                    close(o1, o2, 1e-12)
+                    close(l1, l2, 1e-12)
+    # weights returned with the rows: P sums to one over the kept keys and
+    # reproduces O from the returned value rows
+    o, l, P, vv = orc.attention_rows(q, k, v, 0.4, True, None, 1, 2, np.arange(3, 9), window=4,
+                                     trim_keys=True, return_weights=True)
+    close(P.sum(axis=1), np.ones(6), 1e-12)
+    close(P @ vv, o, 1e-12)
+
+
+def check_backward_o_given(orc):
+    # delta formed from a given output: with the exact O it is the ordinary
+    # gradient; a perturbation e of row i's output moves delta_i by g_i . e,
+    # so dV is unchanged, dQ_i moves by -c (g_i . e) sum_j P_ij k_j and dK_j by
+    # -c sum_i P_ij (g_i . e_i) q_i (closed forms of dS = P (dP - delta)).
+    r = np.random.default_rng(59)
+    Lq, Lk, D, c = 5, 7, 3, 0.7
+    q, k, v = r.standard_normal((Lq, D)), r.standard_normal((Lk, D)), r.standard_normal((Lk, D))
+    g = r.standard_normal((Lq, D))
+    O, _ = orc.dense_head(q, k, v, c)
+    base = orc.dense_backward_head(q, k, v, g, c)
+    same = orc.dense_backward_head(q, k, v, g, c, o_given=O)
+    for a, b in zip(base, same):
+        close(a, b, 1e-12)
+    e = r.standard_normal((Lq, D)) * 1e-3
+    pert = orc.dense_backward_head(q, k, v, g, c, o_given=O + e)
+    S = c * (q @ k.T)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    dd = (g * e).sum(axis=1)
+    close(pert[2], base[2], 1e-12)
+    close(pert[0] - base[0], -c * dd[:, None] * (P @ k), 1e-9)
+    close(pert[1] - base[1], -c * (P * dd[:, None]).T @ q, 1e-9)
+    # batched form passes the given output through per (b, h)
+    qb, kb, vb, gb = (x[None, None] for x in (q, k, v, g))
+    ob = (O + e)[None, None]
+    dq, dk, dv = orc.attention_backward(qb, kb, vb, gb, c, o_given=ob)
+    close(dq[0, 0], pert[0], 1e-12)
+    close(dk[0, 0], pert[1], 1e-12)
+
+
 CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, check_two_tile,
           check_mask_table, check_streaming_vs_dense, check_merge_trees,
           check_page_streaming_experiment, check_page_split_experiment, check_brute_force,
@@ -890,7 +950,7 @@ CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, che
           check_paged_matches_contiguous, check_paged_permutation, check_paged_invalid_entries,
           check_backward_page_experiment, check_backward_vs_autograd, check_backward_finite_differences,
           check_backward_gqa_and_lengths, check_score_modifiers, check_fp8_format, check_fp8_hadamard, check_fp8_block_scale,
-          check_fp8_attention]
+          check_fp8_attention, check_trimmed_rows, check_backward_o_given]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -917,18 +977,28 @@ MUTANTS = {
     "scores_transposed": [("attention", "S = scale * (q @ k.T)", "S = scale * (k @ q.T).T[::-1, ::-1]")],
     "empty_row_lse_zero": [("attention", "shift + np.log(safe_ell), -np.inf)", "shift + np.log(safe_ell), 0.0)")],
     "kv_len_ignored": [("attention", "n = _kv_len(kv_lens, b, Lk)", "n = Lk")],
-    "alpha_sign": [("streaming", "alpha = np.exp(m - shift)", "alpha = np.exp(shift - m)")],
-    "ell_not_rescaled": [("streaming", "ell = alpha * ell + p.sum(axis=1)", "ell = ell + p.sum(axis=1)")],
-    "acc_not_rescaled": [("streaming", "u = alpha[:, None] * u + p @ vt", "u = u + p @ vt")],
-    "tau_inverted": [("streaming", "move = ~(jump <= tau)", "move = jump <= tau")],
-    "stream_mask_dropped": [("streaming", "s[kp[None, :] > qp[:, None]] = -np.inf", "pass")],
-    "merge_unweighted_ell": [("merge", "wa * la + wb * lb, wa[:, None] * ua", "la + lb, wa[:, None] * ua")],
-    "merge_lse_max": [("merge", "L = np.logaddexp(la, lb)", "L = np.maximum(la, lb)")],
-    "merge_weight_swapped": [("merge", "return wa[:, None] * oa + wb[:, None] * ob, L",
-                              "return wb[:, None] * oa + wa[:, None] * ob, L")],
+    "alpha_sign": [("streaming", "factor = np.exp(self.ref - anchor)", "factor = np.exp(anchor - self.ref)")],
+    "ell_not_rescaled": [("streaming", "self.norm = factor * self.norm + terms.sum(axis=1)",
+                          "self.norm = self.norm + terms.sum(axis=1)")],
+    "acc_not_rescaled": [("streaming", "self.acc = factor[:, None] * self.acc + terms @ values",
+                          "self.acc = self.acc + terms @ values")],
+    "tau_inverted": [("streaming", "keep = (peak - self.ref) <= tau", "keep = ~((peak - self.ref) <= tau)")],
+    "stream_mask_dropped": [("streaming", "tile = np.where(k_pos[keys][None, :] <= q_pos[r0:r1][:, None], tile, -np.inf)",
+                             "pass")],
+    "merge_unweighted_ell": [("merge", 'norm = np.einsum("pr,pr->r", scale_to_top, np.stack([p[1] for p in parts]))',
+                              'norm = np.stack([p[1] for p in parts]).sum(axis=0)')],
+    "merge_lse_max": [("merge", "total = _anchor(top) + np.log(np.exp(lses - _anchor(top)[None, :]).sum(axis=0))",
+                       "total = top")],
+    "merge_weight_swapped": [("merge", 'return np.einsum("pr,prd->rd", weights, outs), total',
+                              'return np.einsum("pr,prd->rd", weights[::-1], outs), total')],
     "window_off_by_one": [("attention", "(dist >= window)", "(dist > window)")],
     "window_not_causal": [("attention", "(dist < 0) | (dist >= window)", "(dist >= window)")],
-    "window_not_passed": [("attention", "np.arange(n), window, slope, softcap)", "np.arange(n), 0, slope, softcap)")],
+    "window_not_passed": [("attention", "np.arange(lo, hi), window, slope, softcap,", "np.arange(lo, hi), 0, slope, softcap,")],
+    "trim_past_last_row": [("attention", "hi = int(min(n, max(q_pos.max() + 1, 0)))", "hi = int(min(n, max(q_pos.max(), 0)))")],
+    "trim_window_start": [("attention", "lo = int(min(hi, max(q_pos.min() - window + 1, 0)))",
+                           "lo = int(min(hi, max(q_pos.min() - window + 2, 0)))")],
+    "bwd_o_given_ignored": [("backward", "delta = (g * (O if o_given is None else as_f64(o_given))).sum(axis=1)",
+                             "delta = (g * O).sum(axis=1)")],
     "page_offset_swapped": [("paged", "cache[page, :, t % page_size, :]", "cache[page, :, t // page_size, :]")],
     "page_index_mod": [("paged", "page = table[b, t // page_size]", "page = table[b, t % page_size]")],
     "paged_positions_compacted": [("paged", "positions.append(t)", "positions.append(len(positions))")],
@@ -937,7 +1007,8 @@ MUTANTS = {
     "paged_head_map": [("paged", "g = h // r", "g = h % Hkv")],
     "paged_queries_top_left": [("paged", "q_pos = (n - Lq) + np.arange(Lq)", "q_pos = np.arange(Lq)")],
     "bwd_delta_dropped": [("backward", "dS = P * (dP - delta[:, None])", "dS = P * dP")],
-    "bwd_delta_wrong": [("backward", "delta = (g * O).sum(axis=1)", "delta = g.sum(axis=1)")],
+    "bwd_delta_wrong": [("backward", "delta = (g * (O if o_given is None else as_f64(o_given))).sum(axis=1)",
+                         "delta = g.sum(axis=1)")],
     "bwd_dq_unscaled": [("backward", "dQ = scale * (dS @ k)", "dQ = (dS @ k)")],
     "bwd_dk_sign": [("backward", "dK = scale * (dS.T @ q)", "dK = -scale * (dS.T @ q)")],
     "bwd_dv_from_ds": [("backward", "dV = P.T @ g", "dV = dS.T @ g")],
