@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 # Every entry point declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_window", "fa_fwd_paged", "fa_bwd",
+EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_noalloc", "fa_noalloc_scratch_bytes",
+            "fa_fwd_window", "fa_fwd_paged", "fa_bwd",
             "fa_fwd_mod", "fa_quantize_fp8", "fa_fwd_fp8",
             "fa_workspace_bytes", "fa_status_string", "fa_last_error")
 
@@ -52,6 +53,10 @@ def load_library(path: Optional[str] = None):
     lib.fa_fwd.restype = i32
     lib.fa_fwd_splits.argtypes = fwd_args + [i32]
     lib.fa_fwd_splits.restype = i32
+    lib.fa_fwd_noalloc.argtypes = fwd_args + [i32]
+    lib.fa_fwd_noalloc.restype = i32
+    lib.fa_noalloc_scratch_bytes.argtypes = []
+    lib.fa_noalloc_scratch_bytes.restype = ctypes.c_size_t
     # q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, window, scale, kv_lens, stream, num_splits
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, i32]
     lib.fa_fwd_window.restype = i32
@@ -182,6 +187,26 @@ def fa_fwd_splits(q, k, v, num_splits, o=None, lse=None, *, causal=False, scale=
     _check(lib.fa_fwd_splits(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk,
                              D, int(bool(causal)), scale, _ptr(kv_lens), s, int(num_splits)))
     return o, lse
+
+
+def fa_fwd_noalloc(q, k, v, o, lse, *, num_splits=0, causal=False, scale=None, kv_lens=None,
+                   stream=None):
+    """fa_fwd_splits through ``fa_fwd_noalloc``: the split-KV workspace is the
+    library's static scratch.  The caller passes ``o`` (and ``lse`` or None);
+    nothing is allocated here or in the library."""
+    if o is None:
+        raise ValueError("fa_fwd_noalloc needs the output tensor o (it allocates nothing)")
+    o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare(q, k, v, o, lse, kv_lens, lse is not None)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    lib = load_library()
+    _check(lib.fa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lq, Lk,
+                              D, int(bool(causal)), scale, _ptr(kv_lens), s, int(num_splits)))
+    return o, lse
+
+
+def fa_noalloc_scratch_bytes() -> int:
+    return int(load_library().fa_noalloc_scratch_bytes())
 
 
 def fa_fwd_window(q, k, v, window, o=None, lse=None, *, scale=None, kv_lens=None, stream=None,

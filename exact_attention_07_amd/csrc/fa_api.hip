@@ -14,6 +14,12 @@
 
 #include "fa_internal.h"
 
+// Split-KV scratch of fa_fwd_noalloc: one static array per device (each GPU the
+// library runs on holds its own copy until the process ends).  In host code the
+// name is only a stand-in; the device address comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -75,6 +81,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 struct Extra {
     int window = 0;                 // causal window width, 0 = none
     int requested_splits = 0;       // > 0 forces the split-KV path
+    bool no_alloc = false;          // split-KV workspace from the static scratch, no allocation
     // paged cache (page_table != nullptr): Lk of the shape is the capacity
     const int* page_table = nullptr;
     int max_pages = 0, num_pages = 0, page_size = 0;
@@ -179,6 +186,28 @@ int get_workspace(size_t bytes, void** out) {
     return FA_OK;
 }
 
+// Device address of this device's copy of `scratch`, looked up once per device
+// (with that device current) and kept; never the host-side name itself.
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
 int validate_extra(const Shape& s, int causal, const int* kv_lens, const Extra& x) {
     if (x.requested_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
     if (x.window < 0) return fail(FA_ERR_INVALID_ARG, "window must be >= 0");
@@ -239,7 +268,16 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
                     "32-bit offsets of one KV head's packed query rows", (long long)r * s.Lq * s.D * 2);
     const SplitPlan pl = plan_splits(s, x.requested_splits, cu_count(), visible_span(s, x.window));
     void* ws = nullptr;
-    st = get_workspace(split_workspace_bytes(s, pl), &ws);
+    const size_t ws_bytes = split_workspace_bytes(s, pl);
+    if (x.no_alloc) {
+        if (ws_bytes > kNoAllocScratchBytes)
+            return fail(FA_ERR_INVALID_ARG, "split-KV workspace of %zu bytes (%d partitions) exceeds the "
+                        "static scratch of %zu bytes; pass fewer partitions or a smaller problem",
+                        ws_bytes, pl.num_splits, kNoAllocScratchBytes);
+        st = scratch_address(&ws);
+    } else {
+        st = get_workspace(ws_bytes, &ws);
+    }
     if (st != FA_OK) return st;
     const size_t rows = (size_t)s.B * s.Hq * s.Lq;
     float* part_o = static_cast<float*>(ws);
@@ -288,6 +326,19 @@ int fa_fwd_splits(const void* q, const void* k, const void* v, void* o, float* l
     x.requested_splits = num_splits;
     return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream, x);
 }
+
+int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                   int causal, float scale, const int* kv_lens, void* stream,
+                   int num_splits) {
+    g_last_error[0] = '\0';
+    Extra x;
+    x.requested_splits = num_splits;
+    x.no_alloc = true;
+    return run(q, k, v, o, lse, Shape{B, Hq, Hkv, Lq, Lk, D}, causal, scale, kv_lens, stream, x);
+}
+
+size_t fa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Lq, int Lk, int D,

@@ -94,6 +94,30 @@ int fa_fwd_splits(const void* q, const void* k, const void* v, void* o, float* l
                   int num_splits);
 
 /*
+ * fa_fwd_splits for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments, path choice and errors as fa_fwd_splits
+ * (num_splits = 0: fa_fwd's choice), except that the split-KV workspace is a
+ * static device array of fa_noalloc_scratch_bytes() bytes (16 MiB) inside the
+ * library instead of a buffer the library allocates: this entry point calls no
+ * hipMalloc or hipFree.  A call whose workspace
+ * B * Hq * Lq * partitions * (D + 1) * 4 bytes exceeds the scratch returns
+ * FA_ERR_INVALID_ARG (fa_last_error names the sizes) and enqueues nothing.
+ * The prefill path (Lq > 1 without forced splits) needs no workspace.
+ * Every call writes all of the scratch it reads, so nothing must start at
+ * zero.  Each GPU holds its own copy of the scratch (looked up once per device
+ * on first use), shared by every fa_fwd_noalloc call on that GPU: calls that
+ * overlap on one GPU (other streams, other threads) race on it.
+ */
+int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                   int causal, float scale, const int* kv_lens, void* stream,
+                   int num_splits);
+
+/* Size in bytes of fa_fwd_noalloc's static split-KV scratch. */
+size_t fa_noalloc_scratch_bytes(void);
+
+/*
  * Causal attention restricted to a window (FlashAttention from Scratch,
  * section 12 "Programmable attention", a causal window of width w): query i,
  * at absolute position p_i = n_b - Lq + i, sees key j iff 0 <= p_i - j < w and
