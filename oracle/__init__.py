@@ -28,6 +28,10 @@ fp8.round_e4m3 / quantize_rows / fp8_attention_forward
     E4M3 rounding, block quantization with power-of-two scales, incoherent
     processing (Hadamard with random signs), and the attention of the
     quantized Q and K by the dense definition.
+varlen.varlen_attention_forward / packed_mask_forward / lpt_schedule
+    Attention over sequences of different lengths packed end to end (per
+    sequence, and again through one block-diagonal mask), and the
+    longest-tile-first order of the sequences with its query-block prefix.
 
 Every function cites the passage of the pages it follows.  All of them are
 pinned by ``tests/test_oracle.py`` to values the pages print, closed forms,
@@ -39,10 +43,11 @@ from .merge import partition_state, merge_states, finish_state, merge_normalized
 from .paged import gather_sequence, paged_attention_forward
 from .backward import dense_backward_head, attention_backward
 from . import fp8
+from . import varlen
 
 __all__ = [
     "as_f64", "dense_head", "attention_forward", "attention_rows",
     "streaming_head", "partition_state", "merge_states", "finish_state",
     "merge_normalized", "gather_sequence", "paged_attention_forward",
-    "dense_backward_head", "attention_backward", "fp8",
+    "dense_backward_head", "attention_backward", "fp8", "varlen",
 ]

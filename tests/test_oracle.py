@@ -25,7 +25,11 @@ Pins used (none of them retypes the oracle's own formula):
   * paged KV (§9.3): through random page tables over NaN-filled pools the
     result equals the contiguous cache's; the section's own experiment
     (permute the physical pages, the table follows, the output stays
-    identical); out-of-range entries against brute force.
+    identical); out-of-range entries against brute force;
+  * variable-length packed batches: torch SDPA over the whole packed stream
+    with a block-diagonal mask built here from the lengths, a single sequence
+    against the batched definition, reordering the sequences, empty ones; the
+    LPT order against a worked example and its defining properties.
 """
 from __future__ import annotations
 
@@ -55,7 +59,7 @@ def oracle_namespace(mutations=()):
     """Load fresh copies of the oracle modules, optionally with textual
     mutations (module, old, new) applied, and expose their functions."""
     mods = {}
-    for name in ("attention", "streaming", "merge", "paged", "backward", "fp8"):
+    for name in ("attention", "streaming", "merge", "paged", "backward", "fp8", "varlen"):
         path = os.path.join(ORACLE_DIR, name + ".py")
         with open(path) as f:
             src = f.read()
@@ -67,6 +71,11 @@ def oracle_namespace(mutations=()):
         if name == "paged":
             # The paged module evaluates through the (possibly mutated) copy
             # of the dense definition instead of the package's.
+            imp = "from .attention import as_f64, dense_head\n"
+            assert imp in src
+            src = src.replace(imp, "")
+            mod.as_f64, mod.dense_head = mods["attention"].as_f64, mods["attention"].dense_head
+        if name == "varlen":
             imp = "from .attention import as_f64, dense_head\n"
             assert imp in src
             src = src.replace(imp, "")
@@ -93,7 +102,7 @@ def oracle_namespace(mutations=()):
         gather_sequence=pg.gather_sequence,
         paged_attention_forward=pg.paged_attention_forward,
         dense_backward_head=bw.dense_backward_head, attention_backward=bw.attention_backward,
-        fp8=f8)
+        fp8=f8, varlen=mods["varlen"])
 
 
 def row_inputs(scores, values):
@@ -942,6 +951,112 @@ def check_backward_o_given(orc):
     close(dk[0, 0], pert[1], 1e-12)
 
 
+# ---------------------------------------------------------------------------
+# Variable-length packed batches (FlashAttention from Scratch, §11.5 and §12;
+# FlashAttention-4, "LPT scheduling for imbalanced grids")
+# ---------------------------------------------------------------------------
+
+def _packed_case(seed, lens_q, lens_k, Hq=4, Hkv=2, D=6):
+    r = np.random.default_rng(seed)
+    tq, tk = sum(lens_q), sum(lens_k)
+    q = r.standard_normal((Hq, tq, D))
+    k = r.standard_normal((Hkv, tk, D))
+    v = r.standard_normal((Hkv, tk, D))
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    return q, k, v, cu_q, cu_k
+
+
+def _sdpa_packed(q, k, v, lens_q, lens_k, scale, causal):
+    """torch SDPA in fp64 over the whole packed stream with a mask built from
+    the lengths: query i of sequence b may see key j of sequence b at position
+    p_j <= (Lk_b - Lq_b) + i under the causal rule; rows with no key are
+    reported as None (SDPA gives NaN there)."""
+    Hq, Hkv = q.shape[0], k.shape[0]
+    tq, tk = q.shape[1], k.shape[1]
+    mask = torch.zeros(tq, tk, dtype=torch.bool)
+    row, col = 0, 0
+    for lq, lk in zip(lens_q, lens_k):
+        for i in range(lq):
+            last = lk if not causal else min(lk, lk - lq + i + 1)
+            mask[row + i, col:col + max(last, 0)] = True
+        row, col = row + lq, col + lk
+    qt = torch.from_numpy(q)[None]
+    kt = torch.from_numpy(k).repeat_interleave(Hq // Hkv, 0)[None]
+    vt = torch.from_numpy(v).repeat_interleave(Hq // Hkv, 0)[None]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, dropout_p=0.0, scale=scale)
+    s = scale * (qt @ kt.transpose(-1, -2))
+    lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1)
+    return out[0].numpy(), lse[0].numpy(), mask.any(dim=1).numpy()
+
+
+def check_varlen_vs_sdpa(orc):
+    # both routes of the module (per sequence, one block-diagonal mask) against
+    # the library routine, with queries shorter, equal and longer than keys,
+    # a sequence with no key and a sequence with no query
+    lens_q = [5, 1, 7, 3, 0, 4]
+    lens_k = [9, 1, 4, 0, 2, 4]
+    q, k, v, cu_q, cu_k = _packed_case(61, lens_q, lens_k)
+    for causal in (False, True):
+        ref_o, ref_l, seen = _sdpa_packed(q, k, v, lens_q, lens_k, 0.45, causal)
+        for fn in (orc.varlen.varlen_attention_forward, orc.varlen.packed_mask_forward):
+            o, l = fn(q, k, v, cu_q, cu_k, 0.45, causal)
+            close(o[:, seen], ref_o[:, seen])
+            close(l[:, seen], ref_l[:, seen])
+            assert np.all(o[:, ~seen] == 0.0) and np.all(l[:, ~seen] == -np.inf)
+
+
+def check_varlen_single_and_order(orc):
+    # one sequence is the batched definition; reordering the sequences in the
+    # packing reorders the rows of the result and nothing else
+    lens_q, lens_k = [6, 3, 8], [6, 10, 5]
+    q, k, v, cu_q, cu_k = _packed_case(67, lens_q, lens_k)
+    for causal in (False, True):
+        o, l = orc.varlen.varlen_attention_forward(q, k, v, cu_q, cu_k, 0.6, causal)
+        for b in range(3):
+            qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+            ob, lb = orc.attention_forward(q[None, :, qs:qe], k[None, :, ks:ke], v[None, :, ks:ke], 0.6, causal)
+            close(o[:, qs:qe], ob[0], 1e-15)
+            close(l[:, qs:qe], lb[0], 1e-15)
+        perm = [2, 0, 1]
+        qp = np.concatenate([q[:, cu_q[b]:cu_q[b + 1]] for b in perm], axis=1)
+        kp = np.concatenate([k[:, cu_k[b]:cu_k[b + 1]] for b in perm], axis=1)
+        vp = np.concatenate([v[:, cu_k[b]:cu_k[b + 1]] for b in perm], axis=1)
+        cq = np.concatenate([[0], np.cumsum([lens_q[b] for b in perm])])
+        ck = np.concatenate([[0], np.cumsum([lens_k[b] for b in perm])])
+        op, lp = orc.varlen.varlen_attention_forward(qp, kp, vp, cq, ck, 0.6, causal)
+        for j, b in enumerate(perm):
+            close(op[:, cq[j]:cq[j + 1]], o[:, cu_q[b]:cu_q[b + 1]], 1e-15)
+            close(lp[:, cq[j]:cq[j + 1]], l[:, cu_q[b]:cu_q[b + 1]], 1e-15)
+
+
+def check_lpt_schedule(orc):
+    # worked example: query lengths 300, 40, 1000, 0, 513 with key lengths
+    # 300, 700, 1000, 900, 513 -> longest tiles ceil(Lk / 64) = 5, 11, 16, 0 (no
+    # query, however many keys), 9; descending: 2 (16), 1 (11), 4 (9), 0 (5), 3 (0); query blocks
+    # of 256 rows: 4, 1, 3, 2, 0 -> prefix 0, 4, 5, 8, 10, 10
+    cu_q = np.cumsum([0, 300, 40, 1000, 0, 513])
+    cu_k = np.cumsum([0, 300, 700, 1000, 900, 513])
+    for causal in (False, True):
+        order, prefix = orc.varlen.lpt_schedule(cu_q, cu_k, causal)
+        assert list(order) == [2, 1, 4, 0, 3], order
+        assert list(prefix) == [0, 4, 5, 8, 10, 10], prefix
+    # properties on random batches: a permutation, longest tile non-increasing
+    # along it, equal tiles in index order, prefix counting ceil(Lq / 256)
+    r = np.random.default_rng(71)
+    for _ in range(20):
+        B = int(r.integers(1, 40))
+        lq = r.integers(0, 3000, B)
+        lk = r.integers(0, 3000, B)
+        lk[r.random(B) < 0.3] = 640            # force ties
+        order, prefix = orc.varlen.lpt_schedule(np.cumsum(np.r_[0, lq]), np.cumsum(np.r_[0, lk]), True)
+        assert sorted(order) == list(range(B))
+        cost = [(-(-int(lk[b]) // 64)) if lq[b] > 0 else 0 for b in order]
+        assert all(cost[i] >= cost[i + 1] for i in range(B - 1))
+        assert all(order[i] < order[i + 1] for i in range(B - 1) if cost[i] == cost[i + 1])
+        assert list(prefix) == list(np.cumsum(np.r_[0, [-(-int(lq[b]) // 256) for b in order]]))
+
+
 CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, check_two_tile,
           check_mask_table, check_streaming_vs_dense, check_merge_trees,
           check_page_streaming_experiment, check_page_split_experiment, check_brute_force,
@@ -950,7 +1065,8 @@ CHECKS = [check_worked_row, check_shift_invariance, check_mask_renormalises, che
           check_paged_matches_contiguous, check_paged_permutation, check_paged_invalid_entries,
           check_backward_page_experiment, check_backward_vs_autograd, check_backward_finite_differences,
           check_backward_gqa_and_lengths, check_score_modifiers, check_fp8_format, check_fp8_hadamard, check_fp8_block_scale,
-          check_fp8_attention, check_trimmed_rows, check_backward_o_given]
+          check_fp8_attention, check_trimmed_rows, check_backward_o_given, check_varlen_vs_sdpa,
+          check_varlen_single_and_order, check_lpt_schedule]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -1031,6 +1147,17 @@ MUTANTS = {
     "fp8_one_scale": [("fp8", "blk = x32[idx][j * block_rows:(j + 1) * block_rows]\n            k = block_scale_exponent(float(np.abs(blk).max()) if blk.size else 0.0)",
                        "blk = x32[idx][j * block_rows:(j + 1) * block_rows]\n            k = block_scale_exponent(float(np.abs(x32).max()))")],
     "fp8_code_sign_dropped": [("fp8", "codes = np.where(normal, code_norm, code_sub) + np.where(neg, 0x80, 0)", "codes = np.where(normal, code_norm, code_sub)")],
+    "varlen_top_left": [("varlen", "q_pos = (lk - lq) + np.arange(lq)", "q_pos = np.arange(lq)")],
+    "varlen_keys_at_query_offset": [("varlen", "k[g, ks:ks + lk], v[g, ks:ks + lk]", "k[g, qs:qs + lk], v[g, qs:qs + lk]")],
+    "varlen_head_map": [("varlen", "g = h // r", "g = h % Hkv")],
+    "varlen_segment_short": [("varlen", "(int(cu[b]), int(cu[b + 1] - cu[b]))", "(int(cu[b]), int(cu[b + 1] - cu[b]) - 1)")],
+    "packed_leak": [("varlen", "allowed = seg_q[:, None] == seg_k[None, :]", "allowed = seg_q[:, None] >= seg_k[None, :]")],
+    "packed_top_left": [("varlen", "pos_q[qs:qs + lq] = (lk - lq) + np.arange(lq)", "pos_q[qs:qs + lq] = np.arange(lq)")],
+    "lpt_ascending": [("varlen", "key=lambda b: (-cost[b], b)", "key=lambda b: (cost[b], b)")],
+    "lpt_ties_reversed": [("varlen", "key=lambda b: (-cost[b], b)", "key=lambda b: (-cost[b], -b)")],
+    "lpt_prefix_unsorted": [("varlen", "prefix.append(prefix[-1] + blocks[b])", "prefix.append(prefix[-1] + blocks[len(prefix) - 1])")],
+    "lpt_cost_from_queries": [("varlen", "cost.append(-(-lk // kv_tile) if nqb else 0)", "cost.append(-(-lq // kv_tile) if nqb else 0)")],
+    "lpt_empty_costs": [("varlen", "cost.append(-(-lk // kv_tile) if nqb else 0)", "cost.append(-(-lk // kv_tile))")],
 }
 
 
