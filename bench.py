@@ -14,8 +14,11 @@ backward of the causal 4K and 1K prefill workloads, one fa_bwd call per
 step; the causal 4K and GQA 16K forward with FP8 scores, one fa_fwd_fp8 call
 per step on Q and K quantized beforehand, the quantization timed separately
 and added for the end-to-end figure; the causal 4K forward with ALiBi biases
-and the 1K prefill with soft-capped scores, one fa_fwd_mod call per step),
-are reported under "workloads".
+and the 1K prefill with soft-capped scores, one fa_fwd_mod call per step;
+the causal GQA forward over 16 packed sequences of 128-8192 tokens, one
+fa_fwd_varlen call per step with the longest-tile-first schedule computed
+once for the batch and its kernel timed separately), are reported under
+"workloads".
 
 Timing: W untimed warmup steps, then exactly K steps between two HIP events
 on the stream the kernels are launched on (torch's current stream),
@@ -114,10 +117,26 @@ def time_workload(w, steps, warmup, dev, trials=True):
     q = inp.q.to(dev)
     kl = None if inp.kv_lens is None else inp.kv_lens.to(dev)
     o = torch.empty_like(q)
-    lse = torch.empty(w.B, w.Hq, w.Lq, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    lens = None
     # Arguments are checked and marshalled once; each step is one C-ABI call,
     # so host overhead stays below the kernel time.
-    if w.backward:
+    if w.varlen is not None:
+        # Packed batch: the longest-tile-first schedule is computed once for the
+        # batch layout (as a serving loop reuses it); the step is one
+        # fa_fwd_varlen.  The schedule kernel is timed separately below.
+        k, v = inp.k.to(dev), inp.v.to(dev)
+        cq, ck = inp.meta["cu_seqlens_q"].to(dev), inp.meta["cu_seqlens_k"].to(dev)
+        call = binding.PreparedVarlenCall(q, k, v, cq, ck, o, lse, causal=w.causal, scale=w.scale)
+        lens = list(zip(inp.meta["lens_q"], inp.meta["lens_k"]))
+        sched = call.schedule
+        lib = binding.load_library()
+        sargs = (cq.data_ptr(), ck.data_ptr(), w.B, q.shape[1], k.shape[1], sched.data_ptr(),
+                 torch.cuda.current_stream(dev).cuda_stream)
+
+        def schedule():
+            lib.fa_varlen_schedule(*sargs)
+    elif w.backward:
         k, v = inp.k.to(dev), inp.v.to(dev)
         fwd = binding.PreparedCall(q, k, v, o, lse, causal=w.causal, scale=w.scale, kv_lens=kl,
                                    window=w.window if w.window else None)
@@ -169,8 +188,8 @@ def time_workload(w, steps, warmup, dev, trials=True):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    flops = W.algorithmic_flops(w, inp.kv_lens)
-    nbytes = W.compulsory_bytes(w, inp.kv_lens)
+    flops = W.algorithmic_flops(w, inp.kv_lens, lens=lens)
+    nbytes = W.compulsory_bytes(w, inp.kv_lens, lens=lens)
     rec = {"ms_per_step": ms, "flops": flops, "bytes": nbytes,
            "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9}
     if trials:
@@ -192,6 +211,17 @@ def time_workload(w, steps, warmup, dev, trials=True):
         rec["end_to_end_tflops"] = flops / (e2e * 1e-3) / 1e12
     else:
         rec.update(bound="mfma", frac=rec["tflops"] / PEAK_BF16_TFLOPS)
+    if w.varlen is not None:
+        schedule()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            schedule()
+        end.record()
+        torch.cuda.synchronize()
+        rec["schedule_ms"] = start.elapsed_time(end) / steps
+        rec["sequence_lengths"] = inp.meta["lens_q"]
+        rec["total_tokens"] = int(q.shape[1])
     del call, q, k, v, o, lse, kl
     torch.cuda.empty_cache()
     return rec, inp
@@ -350,7 +380,8 @@ def main():
             print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.1f} us/step"
                   + (f" (trials: median {tr['median_ms'] * 1e3:.1f}, min {tr['min_ms'] * 1e3:.1f} us)" if tr else "")
                   + f", {r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s, {100 * r['frac']:.1f}% of peak"
-                  + (f", quantizing Q and K {r['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in r else ""), flush=True)
+                  + (f", quantizing Q and K {r['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in r else "")
+                  + (f", schedule {r['schedule_ms'] * 1e3:.1f} us" if "schedule_ms" in r else ""), flush=True)
 
     decode = head.Lq == 1
     value = rec["gbs"] if decode else rec["tflops"]
@@ -360,7 +391,7 @@ def main():
             "peak": PEAK_HBM_GBS if decode else rec.get("peak", PEAK_BF16_TFLOPS),
             "unit": unit, "frac": round(rec["frac"], 4), "traffic": traffic}
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and head.varlen is None:   # the oracle baseline is for the batched layout
         print(f"[bench] CPU oracle baseline on {head.name} (~{args.cpu_seconds:.0f} s)", flush=True)
         cpu = cpu_baseline(head, inp, args.cpu_seconds)
     out = {

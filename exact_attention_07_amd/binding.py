@@ -23,6 +23,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_noalloc", "fa_noalloc_scratch_bytes",
             "fa_fwd_window", "fa_fwd_paged", "fa_bwd",
             "fa_fwd_mod", "fa_quantize_fp8", "fa_fwd_fp8",
+            "fa_fwd_varlen", "fa_varlen_schedule", "fa_varlen_schedule_ints",
             "fa_workspace_bytes", "fa_status_string", "fa_last_error")
 
 # Block sizes of the FP8 forward's scales (query rows, keys).
@@ -77,6 +78,13 @@ def load_library(path: Optional[str] = None):
     # q8, k8, v, o, lse, q_scales, k_scales, B, Hq, Hkv, Lq, Lk, D, causal, scale, kv_lens, stream
     lib.fa_fwd_fp8.argtypes = [vp] * 7 + [i32] * 7 + [f32, vp, vp]
     lib.fa_fwd_fp8.restype = i32
+    # q, k, v, o, lse, cu_q, cu_k, schedule, B, Hq, Hkv, total_q, total_k, D, causal, scale, stream
+    lib.fa_fwd_varlen.argtypes = [vp] * 8 + [i32] * 7 + [f32, vp]
+    lib.fa_fwd_varlen.restype = i32
+    lib.fa_varlen_schedule.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    lib.fa_varlen_schedule.restype = i32
+    lib.fa_varlen_schedule_ints.argtypes = [i32]
+    lib.fa_varlen_schedule_ints.restype = ctypes.c_size_t
     lib.fa_workspace_bytes.argtypes = [i32] * 6
     lib.fa_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i32]
@@ -467,6 +475,94 @@ class PreparedModCall:
         self._fn = load_library().fa_fwd_mod
         self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, k.shape[1], Lq, k.shape[2], D,
                       int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), sp, ctypes.c_float(cap), s)
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+        return self.o, self.lse
+
+
+def _check_offsets(cu, name, device):
+    if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous() or cu.device != device:
+        raise ValueError(f"{name} must be a contiguous 1-D int32 tensor on the device of q")
+    if cu.numel() < 2:
+        raise ValueError(f"{name} must hold B + 1 >= 2 offsets")
+
+
+def _prepare_varlen(q, k, v, cu_q, cu_k, o, lse, want_lse):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D bfloat16 tensor [H, total, D]")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+    Hq, total_q, D = q.shape
+    Hkv, total_k, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Dk != D:
+        raise ValueError("k and v must be [Hkv, total_k, D] with the D of q")
+    _check_offsets(cu_q, "cu_seqlens_q", q.device)
+    _check_offsets(cu_k, "cu_seqlens_k", q.device)
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length B + 1")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(Hq, total_q, dtype=torch.float32, device=q.device)
+    return o, lse, (cu_q.numel() - 1, Hq, Hkv, total_q, total_k, D)
+
+
+def fa_varlen_schedule_ints(B: int) -> int:
+    return int(load_library().fa_varlen_schedule_ints(B))
+
+
+def fa_varlen_schedule(cu_seqlens_q, cu_seqlens_k, total_q, total_k, schedule=None, stream=None):
+    """The longest-tile-first order of a packed batch through
+    ``fa_varlen_schedule``: an int32 device tensor [2B + 1] (the sequence
+    order, then the prefix of query blocks).  ``schedule`` may be passed in."""
+    _check_offsets(cu_seqlens_q, "cu_seqlens_q", cu_seqlens_q.device)
+    _check_offsets(cu_seqlens_k, "cu_seqlens_k", cu_seqlens_q.device)
+    B = cu_seqlens_q.numel() - 1
+    if schedule is None:
+        schedule = torch.empty(2 * B + 1, dtype=torch.int32, device=cu_seqlens_q.device)
+    s = torch.cuda.current_stream(cu_seqlens_q.device).cuda_stream if stream is None else stream
+    _check(load_library().fa_varlen_schedule(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(total_q),
+                                             int(total_k), _ptr(schedule), s))
+    return schedule
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o=None, lse=None, *, schedule=None, causal=False,
+                  scale=None, stream=None, want_lse=True):
+    """Attention over a packed variable-length batch through ``fa_fwd_varlen``:
+    q [Hq, total_q, D], k and v [Hkv, total_k, D], int32 offsets [B + 1];
+    ``schedule`` from ``fa_varlen_schedule`` or None (computed by the
+    library).  Returns (o, lse) with o like q and lse [Hq, total_q]."""
+    o, lse, (B, Hq, Hkv, tq, tk, D) = _prepare_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    _check(load_library().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                        _ptr(cu_seqlens_k), _ptr(schedule), B, Hq, Hkv, tq, tk, D,
+                                        int(bool(causal)), scale, s))
+    return o, lse
+
+
+class PreparedVarlenCall:
+    """fa_fwd_varlen with its arguments checked and marshalled once (see
+    PreparedCall); the schedule is computed once here unless given."""
+
+    def __init__(self, q, k, v, cu_seqlens_q, cu_seqlens_k, o=None, lse=None, *, schedule=None,
+                 causal=False, scale=None, stream=None, want_lse=True):
+        o, lse, (B, Hq, Hkv, tq, tk, D) = _prepare_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse,
+                                                          want_lse)
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        if schedule is None:
+            schedule = fa_varlen_schedule(cu_seqlens_q, cu_seqlens_k, tq, tk, stream=s)
+        self.o, self.lse, self.schedule = o, lse, schedule
+        self._keep = (q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, schedule)
+        self._fn = load_library().fa_fwd_varlen
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                      _ptr(schedule), B, Hq, Hkv, tq, tk, D, int(bool(causal)), ctypes.c_float(scale), s)
+        self()
 
     def __call__(self):
         status = self._fn(*self._args)

@@ -34,6 +34,12 @@ int fail(int status, const char* fmt, ...) {
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// A launch's work-items (workgroups x threads per workgroup) must fit the 32
+// bits of the dispatch packet's grid size.
+bool grid_fits(long long workgroups, int threads) {
+    return workgroups >= 0 && workgroups * threads <= (long long)UINT32_MAX;
+}
+
 constexpr int kTileKeys = 32;          // split-KV partitions are multiples of one 32-key tile
 constexpr int kMaxDevices = 64;
 
@@ -255,7 +261,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
         p.scale = scale;
         p.c = c;
         const long long total = (long long)s.B * s.Hq * p.n_qblocks;
-        if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+        if (!grid_fits(total, 512)) return fail(FA_ERR_INVALID_ARG, "grid too large");
         hipError_t e = fa::launch_prefill(s.D, causal != 0, p, stream);
         if (e != hipSuccess) return fail(FA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
         return FA_OK;
@@ -293,7 +299,8 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
     sp.page_table = x.page_table; sp.max_pages = x.max_pages;
     sp.num_pages = x.num_pages; sp.page_size = x.page_size;
     const long long total = (long long)s.B * s.Hkv * pl.n_groups * pl.num_splits;
-    if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    if (!grid_fits(total, 64) || !grid_fits(((long long)rows + 3) / 4, 256))
+        return fail(FA_ERR_INVALID_ARG, "grid too large");
     hipError_t e = fa::launch_splitkv(s.D, x.page_table != nullptr, sp, stream);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "split-KV launch: %s", hipGetErrorString(e));
 
@@ -303,6 +310,29 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, const 
     cp.num_splits = pl.num_splits; cp.chunk = pl.chunk;
     e = fa::launch_combine(s.D, cp, stream);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
+constexpr int kMaxVarlenBatch = 1 << 16;   // sequences per packed batch (the schedule is O(B^2))
+
+int validate_varlen_offsets(const int* cu_q, const int* cu_k, int B, int total_q, int total_k) {
+    if (B <= 0 || B > kMaxVarlenBatch)
+        return fail(FA_ERR_INVALID_ARG, "B (%d) must be in [1, %d]", B, kMaxVarlenBatch);
+    if (total_q < 0 || total_k < 0)
+        return fail(FA_ERR_INVALID_ARG, "total_q (%d) and total_k (%d) must be >= 0", total_q, total_k);
+    if (!cu_q || !cu_k) return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must not be NULL");
+    if (!aligned(cu_q, 4) || !aligned(cu_k, 4))
+        return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be 4-byte aligned");
+    return FA_OK;
+}
+
+int enqueue_varlen_schedule(const int* cu_q, const int* cu_k, int B, int total_q, int total_k, int* schedule,
+                            hipStream_t stream) {
+    fa::VarlenScheduleParams sp;
+    sp.cu_q = cu_q; sp.cu_k = cu_k; sp.schedule = schedule;
+    sp.B = B; sp.total_q = total_q; sp.total_k = total_k;
+    hipError_t e = fa::launch_varlen_schedule(sp, stream);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "varlen schedule launch: %s", hipGetErrorString(e));
     return FA_OK;
 }
 
@@ -410,7 +440,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     p.c = scale * 1.4426950408889634f;
     const long long nq = (long long)B * Hq * ((Lq + 31) / 32);
     const long long nk = (long long)B * Hkv * ((Lk + 31) / 32);
-    if (nq > INT32_MAX || nk > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    if (!grid_fits(nq, 256) || !grid_fits(nk, 512)) return fail(FA_ERR_INVALID_ARG, "grid too large");
     hipError_t e = fa::launch_backward(D, p, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return FA_OK;
@@ -449,7 +479,7 @@ int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
     const long long total = (long long)B * Hq * p.n_qblocks;
-    if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    if (!grid_fits(total, 512)) return fail(FA_ERR_INVALID_ARG, "grid too large");
     hipError_t e = fa::launch_prefill_mod(D, causal != 0, alibi_slopes ? 1 : 2, p,
                                           reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
@@ -511,9 +541,82 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
     const long long total = (long long)B * Hq * p.n_qblocks;
-    if (total > INT32_MAX) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    if (!grid_fits(total, 512)) return fail(FA_ERR_INVALID_ARG, "grid too large");
     hipError_t e = fa::launch_prefill_fp8(causal != 0, p, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
+size_t fa_varlen_schedule_ints(int B) {
+    return (B > 0 && B <= kMaxVarlenBatch) ? 2 * (size_t)B + 1 : 0;
+}
+
+int fa_varlen_schedule(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int total_q, int total_k,
+                       int* schedule, void* stream) {
+    g_last_error[0] = '\0';
+    int st = validate_varlen_offsets(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k);
+    if (st != FA_OK) return st;
+    if (!schedule || !aligned(schedule, 4))
+        return fail(FA_ERR_INVALID_ARG, "schedule must be a non-NULL, 4-byte aligned array of 2B + 1 ints");
+    return enqueue_varlen_schedule(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, schedule,
+                                   reinterpret_cast<hipStream_t>(stream));
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, const int* schedule,
+                  int B, int Hq, int Hkv, int total_q, int total_k, int D,
+                  int causal, float scale, void* stream) {
+    g_last_error[0] = '\0';
+    int st = validate_varlen_offsets(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k);
+    if (st != FA_OK) return st;
+    if (Hq <= 0 || Hkv <= 0)
+        return fail(FA_ERR_INVALID_ARG, "Hq (%d) and Hkv (%d) must be positive", Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension D=%d is not supported (64 or 128)", D);
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(FA_ERR_INVALID_ARG, "scale must be finite and positive");
+    if (total_q == 0) return FA_OK;         // no query row: nothing to compute or write
+    if (!q || !o) return fail(FA_ERR_INVALID_ARG, "q and o must not be NULL");
+    if (total_k > 0 && (!k || !v)) return fail(FA_ERR_INVALID_ARG, "k and v must not be NULL when total_k > 0");
+    if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
+        return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if ((lse && !aligned(lse, 4)) || (schedule && !aligned(schedule, 4)))
+        return fail(FA_ERR_INVALID_ARG, "lse and schedule must be 4-byte aligned");
+    // Per-sequence byte offsets (plus one query block of overshoot) must fit
+    // the 32-bit offsets of the buffer loads; packed row counts 32-bit indices.
+    if (((long long)total_q + 256) * D * 2 > (long long)UINT32_MAX ||
+        ((long long)total_k + 256) * D * 2 > (long long)UINT32_MAX ||
+        (long long)Hq * total_q > INT32_MAX || (long long)Hkv * total_k > INT32_MAX)
+        return fail(FA_ERR_INVALID_ARG, "packed batch too large for 32-bit offsets");
+    // Query blocks of the batch: sum_b ceil(Lq_b / 256) <= (total_q + 255 B) / 256,
+    // and never more than total_q (every block holds a row).
+    long long items = ((long long)total_q + 255LL * B) / fa::kPrefillRows;
+    if (items > total_q) items = total_q;
+    if (!grid_fits(items * Hq, 512)) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (!schedule) {
+        void* ws = nullptr;
+        st = get_workspace(fa_varlen_schedule_ints(B) * sizeof(int), &ws);
+        if (st != FA_OK) return st;
+        st = enqueue_varlen_schedule(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, static_cast<int*>(ws), hs);
+        if (st != FA_OK) return st;
+        schedule = static_cast<const int*>(ws);
+    }
+    fa::PrefillParams p;
+    p.q = static_cast<const __bf16*>(q);
+    p.k = static_cast<const __bf16*>(k);
+    p.v = static_cast<const __bf16*>(v);
+    p.o = static_cast<__bf16*>(o);
+    p.lse = lse; p.kv_lens = nullptr;
+    p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k; p.schedule = schedule;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = total_q; p.Lk = total_k;
+    p.r = Hq / Hkv;
+    p.n_qblocks = 0; p.xcd_units = 0; p.xcd_spread = 0;
+    p.window = 0;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    hipError_t e = fa::launch_prefill_varlen(D, causal != 0, p, (int)items, hs);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "varlen prefill launch: %s", hipGetErrorString(e));
     return FA_OK;
 }
 

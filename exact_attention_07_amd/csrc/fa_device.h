@@ -64,6 +64,17 @@ __device__ __forceinline__ int swap_bits_2_3(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
+// Sequence b of a packed batch from its cumulative offsets cu[B + 1]: start
+// and length, clamped to [0, total] and to a non-negative length, so that
+// malformed offsets give empty or shortened sequences, never an access outside
+// the packed tensors.
+__device__ __forceinline__ void varlen_segment(const int* cu, int b, int total, int& start, int& len) {
+    const int s = min(max(cu[b], 0), total);
+    const int e = min(max(cu[b + 1], s), total);
+    start = s;
+    len = e - s;
+}
+
 // Buffer resource over [base, base + bytes): a raw buffer load whose 16 bytes
 // lie past `bytes` returns zeros (hardware range check), so rows beyond a
 // sequence's valid length read as zero without a branch and are never fetched.

@@ -42,6 +42,22 @@ struct PrefillParams {
     // and the soft-cap of the scaled scores.
     const float* alibi_slopes = nullptr;
     float softcap = 0.0f;
+    // Variable-length batches (the varlen instantiation only): B sequences
+    // packed end to end, Lq and Lk then being the packed totals: Q and O
+    // [Hq, Lq, D], K and V [Hkv, Lk, D], the LSE [Hq, Lq]; sequence b owns
+    // query rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1.
+    // schedule [2B + 1]: the sequences in longest-tile-first order, then the
+    // running count of their query blocks in that order (B + 1 entries).
+    const int* cu_q = nullptr;
+    const int* cu_k = nullptr;
+    const int* schedule = nullptr;
+};
+
+struct VarlenScheduleParams {
+    const int* cu_q;       // [B + 1]
+    const int* cu_k;       // [B + 1]
+    int* schedule;         // [2B + 1]
+    int B, total_q, total_k;
 };
 
 struct QuantParams {
@@ -115,6 +131,10 @@ hipError_t launch_prefill_fp8(bool causal, const PrefillParams& p, hipStream_t s
 hipError_t launch_quantize_fp8(int D, const QuantParams& p, hipStream_t stream);
 // The prefill with a score modifier: mod 1 = ALiBi (p.alibi_slopes), 2 = soft-cap (p.softcap).
 hipError_t launch_prefill_mod(int D, bool causal, int mod, const PrefillParams& p, hipStream_t stream);
+// Longest-tile-first order of a packed batch's sequences, then the prefill of
+// the packed batch over `items` (an upper bound of its query blocks) work items.
+hipError_t launch_varlen_schedule(const VarlenScheduleParams& p, hipStream_t stream);
+hipError_t launch_prefill_varlen(int D, bool causal, const PrefillParams& p, int items, hipStream_t stream);
 hipError_t launch_splitkv(int D, bool paged, const SplitParams& p, hipStream_t stream);
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
 // The dq kernel (which also writes delta) then the dk/dv kernel.

@@ -122,7 +122,7 @@ struct ScoreOperand<true> { typedef i32x8 type; };
 // 2^(-large) = 0 gives -1).
 constexpr int kModNone = 0, kModAlibi = 1, kModSoftcap = 2;
 
-template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false, int MOD = kModNone>
+template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false, int MOD = kModNone, bool VARLEN = false>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
     constexpr int NW = 8;                   // wavefronts: two groups of four
@@ -141,6 +141,7 @@ prefill_kernel(PrefillParams p) {
     static_assert(CAUSAL || !WINDOW, "the window is causal");
     static_assert(!FP8 || (D == 128 && !WINDOW), "the FP8 scores are built for D = 128 without a window");
     static_assert(MOD == kModNone || (!FP8 && !WINDOW), "score modifiers are built for the bf16 kernel without a window");
+    static_assert(!VARLEN || (!FP8 && !WINDOW && MOD == kModNone), "packed batches are built for the plain bf16 kernel");
     constexpr bool CORR = D == 128;         // residual correction of dominant probabilities
     constexpr int KSQ = FP8 ? D / 64 : KS;  // k-steps of S^T
     constexpr int NIK = FP8 ? BN * D / (NT * 16) : NI;   // 16-byte copies per thread per K tile
@@ -177,51 +178,101 @@ prefill_kernel(PrefillParams p) {
         const int x = rem >> 2;
         return rem ^ ((x ^ (x >> 2) ^ (x >> 4) ^ (x >> 6)) & 3);
     };
-    int qb_rev, unit, hg;
-    if (p.xcd_spread) {
-        // XCD x owns the query-block pairs (n-1-q, q) for q = x, x+8, ...: first
-        // its heavy blocks in descending order, then its light ones; within a
-        // block, every (batch, KV head) with its r query heads adjacent.
-        const int xcd = L & 7, slot = L >> 3;
-        const int per = p.B * p.Hq;
-        const int j = slot / per;
-        const int rem = spread_heads(slot - j * per, per);
-        const int M = p.n_qblocks >> 4;      // pairs per XCD
-        const int q = j < M ? xcd + 8 * j : xcd + 8 * (2 * M - 1 - j);
-        qb_rev = j < M ? q : p.n_qblocks - 1 - q;
-        unit = rem / p.r;
-        hg = rem % p.r;
-    } else if (p.xcd_units > 0) {
-        const int xcd = L & 7, slot = L >> 3;
-        const int per = p.xcd_units * p.r;
-        qb_rev = slot / per;
-        const int rem = spread_heads(slot - qb_rev * per, per);
-        unit = xcd * p.xcd_units + rem / p.r;
-        hg = rem % p.r;
+    int qblk, b, g, h;                      // query block, sequence, KV head, query head
+    int Lq, n;                              // the sequence's query rows and valid keys
+    size_t qoff, kvoff, lse_off;            // element offsets of its Q/O rows, K/V rows and LSE
+    if constexpr (VARLEN) {
+        // Packed batch.  Work item `it` is one query block of one sequence
+        // with all its query heads (Hq consecutive workgroups); the items run
+        // through the sequences in the schedule's longest-tile-first order,
+        // each sequence's query blocks last-first (the longest first under the
+        // causal rule).  The grid is an upper bound: workgroups past the
+        // batch's items, or that a schedule inconsistent with the offsets
+        // leaves without a query block, exit at once.
+        const int it = L / p.Hq;
+        const int s = L - it * p.Hq;
+        const int* prefix = p.schedule + p.B;
+        if (it >= prefix[p.B]) return;
+        int lo = 0, up = p.B - 1;           // the last position whose items start at or before it
+        while (lo < up) {
+            const int mid = (lo + up + 1) >> 1;
+            if (prefix[mid] <= it) lo = mid; else up = mid - 1;
+        }
+        b = min(max(p.schedule[lo], 0), p.B - 1);
+        int q_start, k_start;
+        varlen_segment(p.cu_q, b, p.Lq, q_start, Lq);
+        varlen_segment(p.cu_k, b, p.Lk, k_start, n);
+        const int nqb = (Lq + BM - 1) / BM;
+        const int j = it - prefix[lo];
+        if (j < 0 || j >= nqb) return;
+        qblk = nqb - 1 - j;
+        // Heads.  The XCD of a workgroup is s % 8 (round-robin dispatch, Hq a
+        // multiple of 8); it takes one block of Hq / 8 adjacent query heads --
+        // whole KV heads, so their K/V tiles are shared in its L2 -- and the
+        // block rotates with the item, so heads that differ in cost are spread
+        // over the XCDs; within the block, the position rotates every second
+        // item, which spreads them over the XCD's shader engines too.
+        const int per = p.Hq >> 3;
+        if ((p.Hq & 7) == 0 && per % p.r == 0) {
+            const int blk = ((s & 7) + it) & 7;
+            h = blk * per + ((s >> 3) + (it >> 1)) % per;
+        } else {
+            h = s;
+        }
+        g = h / p.r;
+        qoff = ((size_t)h * p.Lq + q_start) * D;
+        kvoff = ((size_t)g * p.Lk + k_start) * D;
+        lse_off = (size_t)h * p.Lq + q_start;
     } else {
-        const int per = p.B * p.Hq;
-        qb_rev = L / per;
-        const int rem = spread_heads(L - qb_rev * per, per);
-        unit = rem / p.r;
-        hg = rem % p.r;
+        int qb_rev, unit, hg;
+        if (p.xcd_spread) {
+            // XCD x owns the query-block pairs (n-1-q, q) for q = x, x+8, ...: first
+            // its heavy blocks in descending order, then its light ones; within a
+            // block, every (batch, KV head) with its r query heads adjacent.
+            const int xcd = L & 7, slot = L >> 3;
+            const int per = p.B * p.Hq;
+            const int j = slot / per;
+            const int rem = spread_heads(slot - j * per, per);
+            const int M = p.n_qblocks >> 4;      // pairs per XCD
+            const int q = j < M ? xcd + 8 * j : xcd + 8 * (2 * M - 1 - j);
+            qb_rev = j < M ? q : p.n_qblocks - 1 - q;
+            unit = rem / p.r;
+            hg = rem % p.r;
+        } else if (p.xcd_units > 0) {
+            const int xcd = L & 7, slot = L >> 3;
+            const int per = p.xcd_units * p.r;
+            qb_rev = slot / per;
+            const int rem = spread_heads(slot - qb_rev * per, per);
+            unit = xcd * p.xcd_units + rem / p.r;
+            hg = rem % p.r;
+        } else {
+            const int per = p.B * p.Hq;
+            qb_rev = L / per;
+            const int rem = spread_heads(L - qb_rev * per, per);
+            unit = rem / p.r;
+            hg = rem % p.r;
+        }
+        qblk = p.n_qblocks - 1 - qb_rev;
+        b = unit / p.Hkv;
+        g = unit - b * p.Hkv;
+        h = g * p.r + hg;
+        Lq = p.Lq;
+        n = p.Lk;
+        if (p.kv_lens) {
+            n = p.kv_lens[b];
+            n = n < 0 ? 0 : (n > p.Lk ? p.Lk : n);
+        }
+        qoff = (size_t)(b * p.Hq + h) * p.Lq * D;
+        kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
+        lse_off = (size_t)(b * p.Hq + h) * p.Lq;
     }
-    const int qblk = p.n_qblocks - 1 - qb_rev;
-    const int b = unit / p.Hkv;
-    const int g = unit - b * p.Hkv;
-    const int h = g * p.r + hg;
-
-    int n = p.Lk;
-    if (p.kv_lens) {
-        n = p.kv_lens[b];
-        n = n < 0 ? 0 : (n > p.Lk ? p.Lk : n);
-    }
-    const int off = n - p.Lq;               // query i sits at key position i + off
+    const int off = n - Lq;                 // query i sits at key position i + off
     const int q0 = qblk * BM;
     const int qw0 = q0 + w * 32;            // first row of this wavefront
     const int qrow = qw0 + (l & 31);        // the row this lane's column holds
     int kv_end = n;
     if (CAUSAL) {
-        const int last = min(q0 + BM, p.Lq) + off;  // keys < last are visible to some row
+        const int last = min(q0 + BM, Lq) + off;    // keys < last are visible to some row
         kv_end = min(n, max(last, 0));
     }
     // First visited tile: under a window, the one holding the lowest key
@@ -239,13 +290,10 @@ prefill_kernel(PrefillParams p) {
     constexpr bool REV = MOD == kModAlibi;
     auto tile_abs = [&](int t) { return (REV && t < ntiles) ? tb + ntiles - 1 - t : tb + t; };
 
-    const size_t qoff = (size_t)(b * p.Hq + h) * p.Lq * D;
-    const size_t kvoff = (size_t)(b * p.Hkv + g) * p.Lk * D;
-
     // ---- Q tile: B operand of S^T, resident in registers -------------------
     SA qf[KSQ];
     if constexpr (FP8) {
-        const rsrc_t qbuf = make_rsrc(p.q8 + qoff, (uint32_t)p.Lq * D);   // rows >= Lq read as zero
+        const rsrc_t qbuf = make_rsrc(p.q8 + qoff, (uint32_t)Lq * D);   // rows >= Lq read as zero
 #pragma unroll
         for (int ks = 0; ks < KSQ; ++ks) {
             const uint32_t at = (uint32_t)(qrow * D + 64 * ks + 32 * hi);
@@ -254,7 +302,7 @@ prefill_kernel(PrefillParams p) {
             qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
         }
     } else {
-        const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)p.Lq * D * 2);   // rows >= Lq read as zero
+        const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)Lq * D * 2);   // rows >= Lq read as zero
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[ks] = load16(qbuf, (uint32_t)(qrow * D + ks * 16 + hi * 8) * 2);
@@ -660,7 +708,7 @@ prefill_kernel(PrefillParams p) {
     const float le = ell_e;
     const float lr = sum_with_partner(ell_r);
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-    if (qrow < p.Lq) {
+    if (qrow < Lq) {
         bf16* Op = p.o + qoff + (size_t)qrow * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -672,7 +720,7 @@ prefill_kernel(PrefillParams p) {
                 *reinterpret_cast<bf16x4*>(Op + db * 32 + 8 * gq + 4 * hi) = ov;
             }
         if (p.lse && hi == 0)
-            p.lse[(size_t)(b * p.Hq + h) * p.Lq + qrow] =
+            p.lse[lse_off + qrow] =
                 le > 0.0f ? (ref + log2_fast(le)) * kLn2 : kNegInf;
     }
 }
@@ -708,6 +756,18 @@ hipError_t launch_prefill_mod(int D, bool causal, int mod, const PrefillParams& 
     } else {
         if (mod == kModAlibi) launch_prefill_mod_d<128, kModAlibi>(causal, p, grid, block, stream);
         else                  launch_prefill_mod_d<128, kModSoftcap>(causal, p, grid, block, stream);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_varlen(int D, bool causal, const PrefillParams& p, int items, hipStream_t stream) {
+    const dim3 grid((unsigned)((long long)items * p.Hq)), block(512);
+    if (D == 64) {
+        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true, false, false, kModNone, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<64, false, false, false, kModNone, true>), grid, block, 0, stream, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, false, false, kModNone, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<128, false, false, false, kModNone, true>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }

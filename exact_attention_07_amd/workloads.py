@@ -22,6 +22,11 @@ Generation recipe (fixed; never changed to make a comparison pass):
   * the decode workload then draws ``kv_lens`` uniformly in [512, 8192] with
     ``torch.randint(512, 8193)``; K and V are allocated at the full capacity
     of 8192 rows per sequence and only the first ``kv_lens[b]`` are valid.
+  * the packed variable-length workload first draws its B sequence lengths
+    uniformly in [128, 8192] (``torch.randint(128, 8193)``, the same length
+    for queries and keys: self-attention over packed documents), then Q
+    [Hq, total, D], K and V [Hkv, total, D] as above; the offsets are the
+    running sums of the lengths.
 
 Follow-on workloads reuse the draws of a base workload (its seed index) and
 change one thing: a causal window (FlashAttention from Scratch, §12) or a
@@ -59,6 +64,7 @@ class Workload:
     fp8: bool = False           # FP8 scores: Q, K block-quantized after the random-sign Hadamard transform
     alibi: bool = False         # ALiBi score modifier, slopes 2^(-8 (h + 1) / Hq)
     softcap: float = 0.0        # soft-cap score modifier (0 = none)
+    varlen: Optional[tuple] = None  # (lo, hi): B packed sequences, lengths uniform in [lo, hi]
 
     @property
     def seed(self) -> int:
@@ -102,6 +108,10 @@ WORKLOADS = [
     Workload("fp8_gqa_causal_b1_hq32_hkv8_l16384_d128", 1, 32, 8, 16384, 16384, 128, True, 3,
              q_boost_every=8, q_boost=4.0, fp8=True,
              description="long-context causal GQA forward with FP8 scores"),
+    # Packed variable-length batch: Lq and Lk are the largest possible length.
+    Workload("varlen_causal_b16_hq32_hkv8_d128", 16, 32, 8, 8192, 8192, 128, True, 5,
+             varlen=(128, 8192),
+             description="causal GQA forward over 16 packed sequences of 128-8192 tokens"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -120,6 +130,8 @@ class Inputs:
 def make_inputs(w: Workload) -> Inputs:
     """Draw the workload's inputs on the CPU (bf16 Q, K, V; int32 kv_lens)."""
     g = torch.Generator().manual_seed(w.seed)
+    if w.varlen is not None:
+        return _make_varlen(w, g)
     q = torch.randn(w.B, w.Hq, w.Lq, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
     k = torch.randn(w.B, w.Hkv, w.Lk, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
     v = torch.randn(w.B, w.Hkv, w.Lk, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
@@ -150,6 +162,38 @@ def make_inputs(w: Workload) -> Inputs:
         # The paged copy of the same K and V; the contiguous tensors stay for reference.
         meta["paged"] = page_kv(k, v, kv_lens, w.page_size, seed=w.seed + 7919)
     return Inputs(q, k, v, kv_lens, w.scale, w.causal, meta)
+
+
+def _make_varlen(w: Workload, g: torch.Generator) -> Inputs:
+    lo, hi = w.varlen
+    lens = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64)
+    total = int(lens.sum())
+    q = torch.randn(w.Hq, total, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn(w.Hkv, total, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(w.Hkv, total, w.D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    cu = torch.zeros(w.B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    meta = {"workload": w.name, "seed": w.seed, "cu_seqlens_q": cu, "cu_seqlens_k": cu.clone(),
+            "lens_q": [int(x) for x in lens], "lens_k": [int(x) for x in lens]}
+    return Inputs(q, k, v, None, w.scale, w.causal, meta)
+
+
+def varlen_case(seed: int, lens_q, lens_k, Hq: int, Hkv: int, D: int, causal: bool = False,
+                scale: Optional[float] = None) -> Inputs:
+    """A seeded N(0,1) packed batch of arbitrary sequence lengths for parity
+    tests: q [Hq, sum(lens_q), D], k and v [Hkv, sum(lens_k), D]."""
+    g = torch.Generator().manual_seed(seed)
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+    q = torch.randn(Hq, tq, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(Hkv, tk, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(Hkv, tk, D, generator=g).to(torch.bfloat16)
+    cq = torch.zeros(len(lens_q) + 1, dtype=torch.int32)
+    ck = torch.zeros(len(lens_k) + 1, dtype=torch.int32)
+    cq[1:] = torch.cumsum(torch.tensor(list(lens_q), dtype=torch.int64), 0).to(torch.int32)
+    ck[1:] = torch.cumsum(torch.tensor(list(lens_k), dtype=torch.int64), 0).to(torch.int32)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    return Inputs(q, k, v, None, scale, causal, {"seed": seed, "cu_seqlens_q": cq, "cu_seqlens_k": ck,
+                                                 "lens_q": list(lens_q), "lens_k": list(lens_k)})
 
 
 def page_kv(k: torch.Tensor, v: torch.Tensor, kv_lens, page_size: int, seed: int,
@@ -243,20 +287,33 @@ def allowed_pairs(Lq: int, n: int, causal: bool, window: int = 0) -> int:
     return tot
 
 
-def algorithmic_flops(w, kv_lens=None) -> int:
+def algorithmic_flops(w, kv_lens=None, lens=None) -> int:
     """4 * D FLOPs per allowed pair for the forward: two matrix products with
     multiply and add counted separately (FlashAttention from Scratch, §11.1
-    counts 4MNd per tile); 10 * D for the backward's five products (§8)."""
+    counts 4MNd per tile); 10 * D for the backward's five products (§8).
+    A packed batch passes its (Lq_b, Lk_b) pairs as ``lens``."""
+    if lens is not None:
+        return sum(4 * w.D * allowed_pairs(lq, lk, w.causal) * w.Hq for lq, lk in lens)
     ns = valid_lengths(w, kv_lens)
     per_pair = 10 * w.D if w.backward else 4 * w.D
     return sum(per_pair * allowed_pairs(w.Lq, n, w.causal, w.window) * w.Hq for n in ns)
 
 
-def compulsory_bytes(w, kv_lens=None) -> int:
+def compulsory_bytes(w, kv_lens=None, lens=None) -> int:
     """Bytes that must cross HBM once: Q read, the K and V rows some query can
     see read once per KV head, O written (bf16) and the LSE written (fp32);
     with a paged cache also the page-table entries of those rows (int32);
-    with FP8 scores Q and K are one byte per element plus their block scales."""
+    with FP8 scores Q and K are one byte per element plus their block scales.
+    A packed batch passes its (Lq_b, Lk_b) pairs as ``lens`` (plus its two
+    offset arrays, int32)."""
+    if lens is not None:
+        total = 0
+        for lq, lk in lens:
+            # every key of a sequence is seen by its last query (bottom-right
+            # alignment), unless the sequence has no query at all
+            seen = lk if lq > 0 else 0
+            total += 2 * w.Hq * lq * w.D * 2 + w.Hq * lq * 4 + 2 * w.Hkv * seen * w.D * 2
+        return total + 2 * 4 * (len(lens) + 1)
     ns = valid_lengths(w, kv_lens)
     if w.fp8:
         q = w.B * w.Hq * w.Lq * w.D + w.B * w.Hq * -(-w.Lq // 256) * 4

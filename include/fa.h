@@ -252,6 +252,64 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
                int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
                const int* kv_lens, void* stream);
 
+/*
+ * Attention over a batch of variable-length sequences packed end to end
+ * (FlashAttention from Scratch, section 11.5: variable-length batches are a
+ * source of imbalance; section 12: packed sequences must not see each other).
+ * Sequence b is fa_fwd's problem on its own rows: query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 against key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1, Lq_b and Lk_b the differences,
+ * with the causal rule bottom-right aligned per sequence (query i of the
+ * sequence at key position Lk_b - Lq_b + i) and the GQA head mapping.
+ *   q : bf16, device, contiguous [Hq, total_q, D]   (head-major, packed rows)
+ *   k, v: bf16, device, contiguous [Hkv, total_k, D]
+ *   o : bf16, device, contiguous [Hq, total_q, D], written on every row
+ *       that belongs to a sequence
+ *   lse : fp32, device, [Hq, total_q], written likewise; may be NULL
+ *   cu_seqlens_q, cu_seqlens_k : int32, device, [B + 1], non-decreasing,
+ *       from 0 to total_q / total_k.  Offsets are read on the device and
+ *       clamped there (to [0, total] and to non-negative lengths), so any
+ *       values keep every access inside the tensors; offsets that are not
+ *       non-decreasing give undefined (but in-bounds) results.
+ *   schedule : int32, device, [2B + 1] from fa_varlen_schedule over the same
+ *       offsets, or NULL: then the library computes it first, on `stream`,
+ *       into its workspace (allocated and shared as fa_fwd's split-KV
+ *       workspace).  A schedule computed for other offsets gives undefined
+ *       (in-bounds) results.
+ *   B in [1, 65536]; total_q, total_k >= 0 (total_q = 0: nothing is
+ *   enqueued and the tensor pointers are not checked); Hq, Hkv > 0, Hq % Hkv == 0; D in {64, 128}; causal 0 or 1;
+ *   scale finite and > 0.  q, k, v, o 16-byte aligned; lse, the offsets
+ *   and the schedule 4-byte aligned.  Errors as for fa_fwd.
+ * Work order (FlashAttention-4 summary, "LPT scheduling for imbalanced
+ * grids"): the query blocks run sequence by sequence in the schedule's
+ * longest-tile-first order, each sequence's last block first.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, const int* schedule,
+                  int B, int Hq, int Hkv, int total_q, int total_k, int D,
+                  int causal, float scale, void* stream);
+
+/*
+ * The longest-tile-first order of a packed batch's sequences (the
+ * FlashAttention-4 summary's preprocessing sort for variable lengths, "LPT
+ * scheduling for imbalanced grids"), for fa_fwd_varlen; computed on the
+ * device, enqueued on `stream`, so it can be computed once per batch layout
+ * and reused.  A sequence's cost is ceil(Lk_b / 64), the KV tiles of its
+ * longest work tile (its last 256-row query block sees every key), or 0 if
+ * Lq_b = 0.  Written: schedule[0 .. B-1] = the sequence indices by cost
+ * descending, equal costs by index ascending; schedule[B .. 2B] = 0 followed
+ * by the running sum of ceil(Lq_b / 256) in that order.  The order and the
+ * blocks do not depend on the causal flag.
+ *   cu_seqlens_q, cu_seqlens_k, B, total_q, total_k: as for fa_fwd_varlen;
+ *   schedule: int32, device, [fa_varlen_schedule_ints(B)], 4-byte aligned,
+ *   owned by the caller.  Errors as for fa_fwd_varlen.
+ */
+int fa_varlen_schedule(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int total_q, int total_k,
+                       int* schedule, void* stream);
+/* Number of int32 entries of a schedule for B sequences (2B + 1; 0 for a B
+ * outside [1, 65536]). */
+size_t fa_varlen_schedule_ints(int B);
+
 /* Bytes of split-KV workspace fa_fwd would use for this shape (0 when it
  * takes the prefill path, or for invalid sizes). */
 size_t fa_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int D);

@@ -38,6 +38,14 @@ def segments(cu):
     return [(int(cu[b]), int(cu[b + 1] - cu[b])) for b in range(len(cu) - 1)]
 
 
+def sequence_view(q, k, v, cu_q, cu_k, b):
+    """Sequence b of the packed batch as a batch of one: q [1, Hq, Lq_b, D],
+    k and v [1, Hkv, Lk_b, D] (views of the packed rows), for the batched
+    definition in ``attention``."""
+    (qs, lq), (ks, lk) = segments(cu_q)[b], segments(cu_k)[b]
+    return q[None, :, qs:qs + lq], k[None, :, ks:ks + lk], v[None, :, ks:ks + lk]
+
+
 def varlen_attention_forward(q, k, v, cu_q, cu_k, scale, causal=False):
     """O [Hq, total_q, Dv] and LSE [Hq, total_q] (fp64): every sequence by the
     dense definition on its own rows, with its queries at key positions
@@ -49,14 +57,15 @@ def varlen_attention_forward(q, k, v, cu_q, cu_k, scale, causal=False):
     r = Hq // Hkv
     O = np.zeros((Hq, total_q, Dv))
     lse = np.full((Hq, total_q), -np.inf)
-    for (qs, lq), (ks, lk) in zip(segments(cu_q), segments(cu_k)):
+    for b, ((qs, lq), (ks, lk)) in enumerate(zip(segments(cu_q), segments(cu_k))):
         if lq == 0:
             continue
+        qb, kb, vb = sequence_view(q, k, v, cu_q, cu_k, b)
         q_pos = (lk - lq) + np.arange(lq)
         for h in range(Hq):
             g = h // r
             O[h, qs:qs + lq], lse[h, qs:qs + lq] = dense_head(
-                q[h, qs:qs + lq], k[g, ks:ks + lk], v[g, ks:ks + lk], scale, causal, q_pos, np.arange(lk))
+                qb[0, h], kb[0, g], vb[0, g], scale, causal, q_pos, np.arange(lk))
     return O, lse
 
 

@@ -313,3 +313,48 @@ def compare_all_rows(case, got_o, got_lse, name: str | None = None, chunk: int =
         if ctx is not None:
             ctx.restore_original_limits()
     return st.finish(name)
+
+
+def compare_varlen(case, got_o, got_lse, name: str | None = None, chunk: int = 512, sequences=None):
+    """Compare EVERY query row of every head of the packed batch's sequences
+    (or of the listed ``sequences``) with the oracle, on the strict bar.
+    Sequence b is taken as a batch of one (``oracle.varlen.sequence_view``)
+    and its rows evaluated in chunks by ``oracle.attention_rows`` on a thread
+    pool, as in ``compare_all_rows``.  got_o [Hq, total_q, D], got_lse
+    [Hq, total_q]."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - threadpoolctl is part of the image
+        threadpool_limits = None
+    cq, ck = case.meta["cu_seqlens_q"], case.meta["cu_seqlens_k"]
+    B = cq.numel() - 1
+    Hq = case.q.shape[0]
+    go = got_o.detach().cpu() if hasattr(got_o, "detach") else got_o
+    gl = got_lse.detach().cpu() if hasattr(got_lse, "detach") else got_lse
+    seqs = list(range(B)) if sequences is None else list(sequences)
+    views = {b: oracle.varlen.sequence_view(case.q, case.k, case.v, cq, ck, b) for b in seqs}
+    tasks = [(b, h, r0, min(r0 + chunk, views[b][0].shape[2]))
+             for b in seqs for h in range(Hq) for r0 in range(0, views[b][0].shape[2], chunk)]
+
+    def work(t):
+        b, h, r0, r1 = t
+        qb, kb, vb = views[b]
+        ro, rl = oracle.attention_rows(qb, kb, vb, case.scale, case.causal, None, 0, h, np.arange(r0, r1),
+                                       trim_keys=True)
+        return t, ro, rl
+
+    st = Stats()
+    ctx = threadpool_limits(limits=1, user_api="blas") if threadpool_limits else None
+    try:
+        with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+            for (b, h, r0, r1), ro, rl in ex.map(work, tasks):
+                s0 = int(cq[b])
+                st.add(go[h, s0 + r0:s0 + r1], gl[h, s0 + r0:s0 + r1], ro, rl, bh=(b, h))
+    finally:
+        if ctx is not None:
+            ctx.restore_original_limits()
+    return st.finish(name)

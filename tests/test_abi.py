@@ -276,3 +276,78 @@ def test_fwd_mod_validation(lib, kw, status):
     got = call_mod(lib, **kw)
     assert got == status, (kw, got, lib.fa_last_error())
     assert lib.fa_last_error().decode() != ""
+
+
+def test_prefill_grid_past_32_bit_work_items_is_rejected(lib):
+    # 2^17 sequences x 64 heads x one 256-row block = 2^23 workgroups of 512
+    # threads = 2^32 work-items: more than the dispatch packet's 32-bit grid.
+    st = call(lib, B=1 << 17, Hq=64, Hkv=64, Lq=2, Lk=8, D=64)
+    assert st == binding.FA_ERR_INVALID_ARG
+    assert b"grid" in lib.fa_last_error()
+
+
+def call_varlen(lib, q=P, k=P, v=P, o=P, lse=None, cu_q=P, cu_k=P, schedule=None, B=2, Hq=2, Hkv=1,
+                total_q=16, total_k=32, D=64, causal=0, scale=0.125):
+    return lib.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, schedule, B, Hq, Hkv, total_q, total_k, D, causal,
+                             ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), binding.FA_ERR_INVALID_ARG),
+    (dict(B=(1 << 16) + 1), binding.FA_ERR_INVALID_ARG),
+    (dict(total_q=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(total_k=-1), binding.FA_ERR_INVALID_ARG),
+    (dict(cu_q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(cu_k=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(schedule=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), binding.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), binding.FA_ERR_INVALID_ARG),
+    (dict(D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), binding.FA_ERR_INVALID_ARG),
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(k=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=ctypes.c_void_p((1 << 20) + 1)), binding.FA_ERR_INVALID_ARG),
+    (dict(total_q=1 << 24, D=128), binding.FA_ERR_INVALID_ARG),          # 32-bit byte offsets
+    (dict(total_k=1 << 24, D=128), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=256, Hkv=256, total_q=1 << 23), binding.FA_ERR_INVALID_ARG),  # packed rows past int32
+])
+def test_varlen_validation(lib, kw, status):
+    got = call_varlen(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_varlen_without_queries_enqueues_nothing(lib):
+    # total_q = 0: valid, nothing to compute; returns before any HIP call
+    # and before the tensor pointers are looked at.
+    assert call_varlen(lib, total_q=0) == binding.FA_OK
+    assert call_varlen(lib, total_q=0, total_k=0, q=None, k=None, v=None, o=None) == binding.FA_OK
+    # sizes are still validated first
+    assert call_varlen(lib, total_q=0, D=96) == binding.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(total_q=-1), dict(cu_q=None), dict(schedule=None),
+                                dict(schedule=ctypes.c_void_p((1 << 20) + 2))])
+def test_varlen_schedule_validation(lib, kw):
+    args = dict(cu_q=P, cu_k=P, B=2, total_q=16, total_k=32, schedule=P)
+    args.update(kw)
+    got = lib.fa_varlen_schedule(args["cu_q"], args["cu_k"], args["B"], args["total_q"], args["total_k"],
+                                 args["schedule"], None)
+    assert got == binding.FA_ERR_INVALID_ARG, (kw, got)
+
+
+def test_varlen_schedule_ints(lib):
+    assert lib.fa_varlen_schedule_ints(1) == 3
+    assert lib.fa_varlen_schedule_ints(16) == 33
+    assert lib.fa_varlen_schedule_ints(0) == 0
+    assert lib.fa_varlen_schedule_ints(1 << 17) == 0
+
+
+def test_varlen_binding_requires_gpu_tensors():
+    import torch
+    x = torch.zeros(2, 8, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        binding.fa_fwd_varlen(x, x, x, cu, cu)

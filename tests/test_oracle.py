@@ -1148,7 +1148,8 @@ MUTANTS = {
                        "blk = x32[idx][j * block_rows:(j + 1) * block_rows]\n            k = block_scale_exponent(float(np.abs(x32).max()))")],
     "fp8_code_sign_dropped": [("fp8", "codes = np.where(normal, code_norm, code_sub) + np.where(neg, 0x80, 0)", "codes = np.where(normal, code_norm, code_sub)")],
     "varlen_top_left": [("varlen", "q_pos = (lk - lq) + np.arange(lq)", "q_pos = np.arange(lq)")],
-    "varlen_keys_at_query_offset": [("varlen", "k[g, ks:ks + lk], v[g, ks:ks + lk]", "k[g, qs:qs + lk], v[g, qs:qs + lk]")],
+    "varlen_keys_at_query_offset": [("varlen", "k[None, :, ks:ks + lk], v[None, :, ks:ks + lk]",
+                                     "k[None, :, qs:qs + lk], v[None, :, qs:qs + lk]")],
     "varlen_head_map": [("varlen", "g = h // r", "g = h % Hkv")],
     "varlen_segment_short": [("varlen", "(int(cu[b]), int(cu[b + 1] - cu[b]))", "(int(cu[b]), int(cu[b + 1] - cu[b]) - 1)")],
     "packed_leak": [("varlen", "allowed = seg_q[:, None] == seg_k[None, :]", "allowed = seg_q[:, None] >= seg_k[None, :]")],

@@ -74,3 +74,31 @@ def test_random_case_ragged_lengths_in_range():
     c = W.random_case(3, 5, 4, 2, 3, 40, 64, kv_lens="ragged")
     assert c.kv_lens.dtype == torch.int32 and c.kv_lens.shape == (5,)
     assert int(c.kv_lens.min()) >= 0 and int(c.kv_lens.max()) <= 40
+
+
+def test_packed_workload_recipe_and_accounting():
+    w = W.BY_NAME["varlen_causal_b16_hq32_hkv8_d128"]
+    a = W.make_inputs(w)
+    lens = a.meta["lens_q"]
+    assert len(lens) == 16 and all(128 <= n <= 8192 for n in lens) and lens == a.meta["lens_k"]
+    total = sum(lens)
+    assert tuple(a.q.shape) == (32, total, 128) and tuple(a.k.shape) == (8, total, 128)
+    cu = a.meta["cu_seqlens_q"]
+    assert cu.dtype == torch.int32 and int(cu[0]) == 0 and int(cu[-1]) == total
+    assert [int(cu[i + 1] - cu[i]) for i in range(16)] == lens
+    # The recipe: lengths first, then Q, K, V from seed 1000 + index.
+    g = torch.Generator().manual_seed(1005)
+    assert torch.randint(128, 8193, (16,), generator=g).tolist() == lens
+    assert torch.equal(torch.randn(32, total, 128, generator=g).to(torch.bfloat16), a.q)
+    # Work: causal square sequences give L(L+1)/2 pairs per head.
+    pairs = sum(n * (n + 1) // 2 for n in lens)
+    assert W.algorithmic_flops(w, lens=list(zip(lens, lens))) == 4 * 128 * pairs * 32
+    by = W.compulsory_bytes(w, lens=list(zip(lens, lens)))
+    assert by == 2 * 32 * total * 128 * 2 + 32 * total * 4 + 2 * 8 * total * 128 * 2 + 8 * 17
+
+
+def test_varlen_case_offsets():
+    c = W.varlen_case(5, [3, 0, 7], [4, 2, 7], 4, 2, 64, causal=True)
+    assert c.meta["cu_seqlens_q"].tolist() == [0, 3, 3, 10]
+    assert c.meta["cu_seqlens_k"].tolist() == [0, 4, 6, 13]
+    assert tuple(c.q.shape) == (4, 10, 64) and tuple(c.k.shape) == (2, 13, 64)
