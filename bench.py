@@ -23,7 +23,8 @@ once for the batch and its kernel timed separately), are reported under
 Timing: W untimed warmup steps, then exactly K steps between two HIP events
 on the stream the kernels are launched on (torch's current stream),
 bracketed by device synchronisation; that gives ``ms_per_step`` and
-``value``.  Every workload is also timed in at least five trials of at least
+``value``.  The other workloads are warmed for at least 100 ms of calls
+before their K steps (the clock settles under a sustained load).  Every workload is also timed in at least five trials of at least
 50 ms each (back-to-back calls between events); their median and minimum
 per-call times are reported under ``trials``.
 
@@ -36,6 +37,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import glob
 import math
@@ -109,7 +111,7 @@ def timed_trials(call, est_ms):
             "calls_per_trial": reps, "trial_ms": statistics.median(per_call) * reps}
 
 
-def time_workload(w, steps, warmup, dev, trials=True):
+def time_workload(w, steps, warmup, dev, trials=True, warm_ms=0.0):
     import torch
     from exact_attention_07_amd import binding, workloads as W
 
@@ -181,6 +183,13 @@ def time_workload(w, steps, warmup, dev, trials=True):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    # Optionally keep warming for warm_ms of wall time (clocks settle under a
+    # sustained load; a few short calls from idle run at a lower clock).
+    t_warm = time.perf_counter()
+    while (time.perf_counter() - t_warm) * 1e3 < warm_ms:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
@@ -220,6 +229,15 @@ def time_workload(w, steps, warmup, dev, trials=True):
         end.record()
         torch.cuda.synchronize()
         rec["schedule_ms"] = start.elapsed_time(end) / steps
+        # Ablation of the sort: the same call with the sequences in the order
+        # given (a schedule in the same layout without the sort).
+        nqb = [-(-n // 256) for n in inp.meta["lens_q"]]
+        plain = torch.tensor(list(range(w.B)) + [0] + list(itertools.accumulate(nqb)), dtype=torch.int32,
+                             device=dev)
+        unsorted = binding.PreparedVarlenCall(q, k, v, cq, ck, o, lse, schedule=plain, causal=w.causal,
+                                              scale=w.scale)
+        rec["unsorted_trials"] = timed_trials(unsorted, ms)
+        del unsorted
         rec["sequence_lengths"] = inp.meta["lens_q"]
         rec["total_tokens"] = int(q.shape[1])
     del call, q, k, v, o, lse, kl
@@ -370,7 +388,8 @@ def main():
             if w.name == head.name:
                 continue
             steps = max(3, min(args.steps, 20))
-            r, winp = time_workload(w, steps, max(2, min(args.warmup, 5)), dev, trials=not args.no_trials)
+            r, winp = time_workload(w, steps, max(2, min(args.warmup, 5)), dev, trials=not args.no_trials,
+                                    warm_ms=100.0)
             if w.name in FIVE and not args.no_cpu:
                 print(f"[bench] CPU oracle baseline on {w.name} (~{args.cpu_seconds_each:.0f} s)", flush=True)
                 r["cpu_baseline"] = cpu_baseline(w, winp, args.cpu_seconds_each)
@@ -381,7 +400,8 @@ def main():
                   + (f" (trials: median {tr['median_ms'] * 1e3:.1f}, min {tr['min_ms'] * 1e3:.1f} us)" if tr else "")
                   + f", {r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s, {100 * r['frac']:.1f}% of peak"
                   + (f", quantizing Q and K {r['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in r else "")
-                  + (f", schedule {r['schedule_ms'] * 1e3:.1f} us" if "schedule_ms" in r else ""), flush=True)
+                  + (f", schedule {r['schedule_ms'] * 1e3:.1f} us, unsorted order median "
+                     f"{r['unsorted_trials']['median_ms'] * 1e3:.1f} us" if "schedule_ms" in r else ""), flush=True)
 
     decode = head.Lq == 1
     value = rec["gbs"] if decode else rec["tflops"]

@@ -274,8 +274,11 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
  *   schedule : int32, device, [2B + 1] from fa_varlen_schedule over the same
  *       offsets, or NULL: then the library computes it first, on `stream`,
  *       into its workspace (allocated and shared as fa_fwd's split-KV
- *       workspace).  A schedule computed for other offsets gives undefined
- *       (in-bounds) results.
+ *       workspace).  Any order of the sequences is accepted in the same
+ *       layout (the sequence indices in the order to run them, then 0 and
+ *       the running sum of their ceil(Lq_b / 256) query blocks): the result
+ *       does not depend on the order, only the time does.  A schedule that
+ *       does not match the offsets gives undefined (in-bounds) results.
  *   B in [1, 65536]; total_q, total_k >= 0 (total_q = 0: nothing is
  *   enqueued and the tensor pointers are not checked); Hq, Hkv > 0, Hq % Hkv == 0; D in {64, 128}; causal 0 or 1;
  *   scale finite and > 0.  q, k, v, o 16-byte aligned; lse, the offsets

@@ -7,8 +7,8 @@ wavefront, ragged tails past 256-row blocks, more queries than keys and the
 reverse), GQA with every head mapping (Hq a multiple of 8 with whole KV heads
 per block, and not), D = 64 and 128, causal and not; the schedule against the
 oracle's order integer for integer (including batches of more than one
-schedule workgroup); a precomputed schedule and the library's own giving
-identical bits; reordering the sequences, and the batched forward on
+schedule workgroup); a precomputed schedule, the library's own and schedules
+in other orders giving identical bits; reordering the sequences, and the batched forward on
 equal-length sequences, giving identical bits; the packed workload of the
 benchmark on every row."""
 from __future__ import annotations
@@ -94,6 +94,21 @@ def test_precomputed_schedule_is_bitwise_the_same(dev):
     o1, l1 = run(case, dev)
     o2, l2 = run(case, dev, schedule=sched)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_any_sequence_order_is_bitwise_the_same(dev):
+    # A schedule in the given order (no sort) and one in the reverse of the
+    # longest-tile-first order: same bits as the library's own schedule.
+    lens_q = [700, 64, 1500, 3, 300, 0, 260]
+    lens_k = [700, 90, 1500, 3, 300, 12, 900]
+    case = W.varlen_case(2315, lens_q, lens_k, 32, 8, 128, True)
+    o1, l1 = run(case, dev)
+    order, _ = oracle.varlen.lpt_schedule(case.meta["cu_seqlens_q"], case.meta["cu_seqlens_k"], True)
+    for seq in (list(range(len(lens_q))), list(order)[::-1]):
+        blocks = [-(-lens_q[b] // 256) for b in seq]
+        sched = torch.tensor(seq + [0] + list(np.cumsum(blocks)), dtype=torch.int32, device=dev)
+        o2, l2 = run(case, dev, schedule=sched)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), seq
 
 
 def test_reordering_sequences_is_bitwise_the_same(dev):
