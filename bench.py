@@ -234,10 +234,11 @@ def time_workload(w, steps, warmup, dev, trials=True, warm_ms=0.0):
         nqb = [-(-n // 256) for n in inp.meta["lens_q"]]
         plain = torch.tensor(list(range(w.B)) + [0] + list(itertools.accumulate(nqb)), dtype=torch.int32,
                              device=dev)
-        unsorted = binding.PreparedVarlenCall(q, k, v, cq, ck, o, lse, schedule=plain, causal=w.causal,
-                                              scale=w.scale)
-        rec["unsorted_trials"] = timed_trials(unsorted, ms)
-        del unsorted
+        if trials:
+            unsorted = binding.PreparedVarlenCall(q, k, v, cq, ck, o, lse, schedule=plain, causal=w.causal,
+                                                  scale=w.scale)
+            rec["unsorted_trials"] = timed_trials(unsorted, ms)
+            del unsorted
         rec["sequence_lengths"] = inp.meta["lens_q"]
         rec["total_tokens"] = int(q.shape[1])
     del call, q, k, v, o, lse, kl
@@ -394,14 +395,16 @@ def main():
                 print(f"[bench] CPU oracle baseline on {w.name} (~{args.cpu_seconds_each:.0f} s)", flush=True)
                 r["cpu_baseline"] = cpu_baseline(w, winp, args.cpu_seconds_each)
             del winp
+            r["traffic"] = stored_traffic(w.name)
             extra[w.name] = rounded(r)
             tr = r.get("trials")
             print(f"[bench] {w.name}: {r['ms_per_step'] * 1e3:.1f} us/step"
                   + (f" (trials: median {tr['median_ms'] * 1e3:.1f}, min {tr['min_ms'] * 1e3:.1f} us)" if tr else "")
                   + f", {r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s, {100 * r['frac']:.1f}% of peak"
                   + (f", quantizing Q and K {r['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in r else "")
-                  + (f", schedule {r['schedule_ms'] * 1e3:.1f} us, unsorted order median "
-                     f"{r['unsorted_trials']['median_ms'] * 1e3:.1f} us" if "schedule_ms" in r else ""), flush=True)
+                  + (f", schedule {r['schedule_ms'] * 1e3:.1f} us" if "schedule_ms" in r else "")
+                  + (f", unsorted order median {r['unsorted_trials']['median_ms'] * 1e3:.1f} us"
+                     if "unsorted_trials" in r else ""), flush=True)
 
     decode = head.Lq == 1
     value = rec["gbs"] if decode else rec["tflops"]
