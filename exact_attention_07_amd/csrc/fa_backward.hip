@@ -106,6 +106,10 @@ struct TileCopy {
 };
 
 
+// A compile-time step index of an unrolled tile loop.
+template <int N>
+struct BwdStage { static constexpr int value = N; };
+
 // Products per pipeline step are issued AHEAD steps after their operands'
 // LDS reads, with a scheduling fence after every step so the compiler keeps
 // that distance (otherwise it places each read right before its product and
@@ -621,9 +625,12 @@ bwd_dkdv_split_kernel(BwdParams p) {
     const int head_skip = p.Lq - nqt * 32;      // rows from one head's last tile end to the next head's first tile
     int cp_qi = 0;                              // next tile to copy: tile index within its head
     long long cp_row = ((long long)b * p.Hq + g * p.r) * p.Lq + q_first;   // ... and its first row, all heads
-    auto issue = [&](int f) __attribute__((always_inline)) {   // tile f into stage f % 3 (dV role only)
+    // Step f of the loop below runs with f % 6 as a compile-time constant
+    // (the LDS stage f % 3 and the P buffer f % 2), so every LDS address is a
+    // per-lane base plus an immediate offset: no address arithmetic per step.
+    auto issue = [&](auto stage) __attribute__((always_inline)) {   // the next tile into LDS stage `stage` (dV role only)
         const int q0 = q_first + cp_qi * 32;
-        const int buf = (f % NSTG) * TILE * 2;
+        constexpr int buf = (decltype(stage)::value % NSTG) * TILE * 2;
         cp.issue(p.q + cp_row * D, p.Lq - q0, lds_q + buf, w);
         cp.issue(p.dout + cp_row * D, p.Lq - q0, lds_g + buf, w);
         if (w == 0) {
@@ -665,8 +672,9 @@ bwd_dkdv_split_kernel(BwdParams p) {
     };
     // dV role: P of tile f (scores of its Q tile against K), masked where
     // needed, handed over through LDS and kept as the bf16 A operand.
-    auto form_p = [&](int f) __attribute__((always_inline)) {
-        const int stg = f % NSTG;
+    auto form_p = [&](auto stage) __attribute__((always_inline)) {   // P of the tile of step `stage` (mod 6)
+        constexpr int stg = decltype(stage)::value % NSTG;
+        constexpr int pbf = decltype(stage)::value & 1;
         const int q0 = q_first + p_qi * 32;
         if (++p_qi == nqt) p_qi = 0;
         const f32x16 s = product(qt + stg * TILE);
@@ -697,7 +705,7 @@ bwd_dkdv_split_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) pr[v] = exp2_fast(pr[v]);
-        f32x4* pbuf = reinterpret_cast<f32x4*>(pshare) + ((f & 1) * 4 + kblk) * 4 * 64 + l;
+        f32x4* pbuf = reinterpret_cast<f32x4*>(pshare) + (pbf * 4 + kblk) * 4 * 64 + l;
 #pragma unroll
         for (int c = 0; c < 4; ++c) pbuf[c * 64] = f32x4{pr[4 * c], pr[4 * c + 1], pr[4 * c + 2], pr[4 * c + 3]};
         pb0 = to_bf16x8(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
@@ -705,20 +713,22 @@ bwd_dkdv_split_kernel(BwdParams p) {
     };
 
     // ---- prologue: tiles 0 and 1 on their way, P(0) ------------------------
-    if (role_dv && total > 0) issue(0);
+    if (role_dv && total > 0) issue(BwdStage<0>{});
     wait_all_vector_loads();                    // tile 0, its statistics, this wavefront's K / V rows
     if (w == 0) stat[l] = st_next;
-    if (role_dv && total > 1) issue(1);
+    if (role_dv && total > 1) issue(BwdStage<1>{});
     __syncthreads();                            // tile 0 visible
-    if (role_dv && active && total > 0) form_p(0);
+    if (role_dv && active && total > 0) form_p(BwdStage<0>{});
 
-    for (int f = 0; f < total; ++f) {
+    auto step = [&](const int f, auto stage) __attribute__((always_inline)) {
+        constexpr int S6 = decltype(stage)::value;   // f % 6
+        constexpr int stg = S6 % NSTG;
+        constexpr int pbf = S6 & 1;
         wait_all_vector_loads();                // this wavefront's copies of tile f + 1
-        if (w == 0 && f + 1 < total) stat[((f + 1) % NSTG) * 64 + l] = st_next;
+        if (w == 0 && f + 1 < total) stat[((S6 + 1) % NSTG) * 64 + l] = st_next;
         __syncthreads();                        // tile f + 1 and P(f) visible; step f - 1 done everywhere
-        if (role_dv && f + 2 < total) issue(f + 2);   // into the stage of tile f - 1
-        if (!active) continue;
-        const int stg = f % NSTG;
+        if (role_dv && f + 2 < total) issue(BwdStage<(S6 + 2) % 6>{});   // into the stage of tile f - 1
+        if (!active) return;
         const bf16* Qs = qt + stg * TILE;
         const bf16* Gs = gt + stg * TILE;
         if (role_dv) {
@@ -731,14 +741,14 @@ bwd_dkdv_split_kernel(BwdParams p) {
                 acc[db] = mfma_32x32x16(pb0, gT[2 * db], acc[db]);
                 acc[db] = mfma_32x32x16(pb1, gT[2 * db + 1], acc[db]);
             }
-            if (f + 1 < total) form_p(f + 1);
+            if (f + 1 < total) form_p(BwdStage<(S6 + 1) % 6>{});
         } else {
             // dP(f), dS = P(f) (dP - delta), dK += dS^T Q(f).
             const f32x16 dp = product(Gs);
             bf16x8 qT[2 * DB];
 #pragma unroll
             for (int j = 0; j < 2 * DB; ++j) qT[j] = read_transposed<D>(Qs, 16 * (j & 1), 32 * (j >> 1), l);
-            const f32x4* pbuf = reinterpret_cast<const f32x4*>(pshare) + ((f & 1) * 4 + kblk) * 4 * 64 + l;
+            const f32x4* pbuf = reinterpret_cast<const f32x4*>(pshare) + (pbf * 4 + kblk) * 4 * 64 + l;
             const float* St = stat + stg * 64;
             float ds[16];
 #pragma unroll
@@ -757,6 +767,14 @@ bwd_dkdv_split_kernel(BwdParams p) {
                 acc[db] = mfma_32x32x16(db1, qT[2 * db + 1], acc[db]);
             }
         }
+    };
+    for (int f = 0; f < total; f += 6) {
+        step(f, BwdStage<0>{});
+        if (f + 1 < total) step(f + 1, BwdStage<1>{});
+        if (f + 2 < total) step(f + 2, BwdStage<2>{});
+        if (f + 3 < total) step(f + 3, BwdStage<3>{});
+        if (f + 4 < total) step(f + 4, BwdStage<4>{});
+        if (f + 5 < total) step(f + 5, BwdStage<5>{});
     }
 
     // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
