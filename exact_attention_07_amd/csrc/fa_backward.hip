@@ -227,9 +227,9 @@ bwd_dq_kernel(BwdParams p) {
     TileCopy<D> cp;
     cp.init(w, l);
     const uint32_t lds_k = lds_address(kt), lds_v = lds_address(vt);
-    auto issue = [&](int j) __attribute__((always_inline)) {   // tile j into stage j % 2
+    auto issue = [&](int j, auto stage) __attribute__((always_inline)) {   // tile j into stage j % 2
         const int k0 = (t_lo + j) * 32;
-        const int buf = (j & 1) * TILE * 2;
+        constexpr int buf = decltype(stage)::value * TILE * 2;
         cp.issue(p.k + kvoff + (size_t)k0 * D, n - k0, lds_k + buf, w);
         cp.issue(p.v + kvoff + (size_t)k0 * D, n - k0, lds_v + buf, w);
     };
@@ -240,14 +240,16 @@ bwd_dq_kernel(BwdParams p) {
     for (int db = 0; db < DB; ++db) dq[db] = zero_f32x16();
     const float c2 = p.c;
 
-    if (ntiles > 0) issue(0);
-    for (int j = 0; j < ntiles; ++j) {
+    // Tile j runs with j % 2 as a compile-time constant, so every LDS address
+    // is a per-lane base plus an immediate offset.
+    auto tile = [&](const int j, auto stage) __attribute__((always_inline)) {
+        constexpr int stg = decltype(stage)::value;
         wait_all_vector_loads();                // this wavefront's copies of tile j
         __syncthreads();                        // tile j visible; every wavefront is done with tile j - 1
-        if (j + 1 < ntiles) issue(j + 1);       // into the stage of tile j - 1
+        if (j + 1 < ntiles) issue(j + 1, BwdStage<1 - stg>{});   // into the stage of tile j - 1
         const int k0 = (t_lo + j) * 32;
-        const bf16* Ks = kt + (j & 1) * TILE;
-        const bf16* Vs = vt + (j & 1) * TILE;
+        const bf16* Ks = kt + stg * TILE;
+        const bf16* Vs = vt + stg * TILE;
 
         // S^T (even steps) and dP^T (odd steps), pipelined over their K and V
         // fragments.
@@ -308,6 +310,11 @@ bwd_dq_kernel(BwdParams p) {
             dq[db] = mfma_32x32x16(kT[2 * db + 1], dsb1, dq[db]);
         }
         __builtin_amdgcn_s_setprio(0);
+    };
+    if (ntiles > 0) issue(0, BwdStage<0>{});
+    for (int j = 0; j < ntiles; j += 2) {
+        tile(j, BwdStage<0>{});
+        if (j + 1 < ntiles) tile(j + 1, BwdStage<1>{});
     }
 
     if (row_ok) {
@@ -401,9 +408,9 @@ bwd_dkdv_kernel(BwdParams p) {
     const int head_skip = p.Lq - nqt * 32;      // rows from one head's last tile end to the next head's first tile
     int cp_qi = 0;                              // next tile to copy: tile index within its head
     long long cp_row = ((long long)b * p.Hq + g * p.r) * p.Lq + q_first;   // ... and its first row, all heads
-    auto issue = [&](int f) __attribute__((always_inline)) {   // tile f into stage f % 2
+    auto issue = [&](auto stage) __attribute__((always_inline)) {   // the next tile into LDS stage `stage`
         const int q0 = q_first + cp_qi * 32;
-        const int buf = (f & 1) * TILE * 2;
+        constexpr int buf = decltype(stage)::value * TILE * 2;
         cp.issue(p.q + cp_row * D, p.Lq - q0, lds_q + buf, w);
         cp.issue(p.dout + cp_row * D, p.Lq - q0, lds_g + buf, w);
         if (w == 0) {
@@ -426,18 +433,20 @@ bwd_dkdv_kernel(BwdParams p) {
 
     const int qrow = swap_bits_2_3(l & 31);   // A-operand row of this lane
     const float c2 = p.c;
-    if (total > 0) issue(0);
-    for (int f = 0; f < total; ++f) {
+    // Tile f runs with f % 2 as a compile-time constant, so every LDS address
+    // is a per-lane base plus an immediate offset.
+    auto tile = [&](const int f, auto stage) __attribute__((always_inline)) {
+        constexpr int stg = decltype(stage)::value;
         wait_all_vector_loads();                // this wavefront's copies of tile f
-        if (w == 0) stat[(f & 1) * 64 + l] = st_next;
+        if (w == 0) stat[stg * 64 + l] = st_next;
         __syncthreads();                        // tile f visible; every wavefront is done with tile f - 1
-        if (f + 1 < total) issue(f + 1);        // into the stage of tile f - 1
+        if (f + 1 < total) issue(BwdStage<1 - stg>{});   // into the stage of tile f - 1
         const int q0 = q_first + use_qi * 32;
         if (++use_qi == nqt) use_qi = 0;
-        if (k0 >= n) continue;                  // this wavefront's keys are all past n
-        const bf16* Qs = qt + (f & 1) * TILE;
-        const bf16* Gs = gt + (f & 1) * TILE;
-        const float* St = stat + (f & 1) * 64;
+        if (k0 >= n) return;                    // this wavefront's keys are all past n
+        const bf16* Qs = qt + stg * TILE;
+        const bf16* Gs = gt + stg * TILE;
+        const float* St = stat + stg * 64;
 
         // Elementwise masks only on tiles where some pair is out (wave-uniform).
         const bool need = (q0 + 32 > p.Lq) || (k0 + 32 > n) || (p.causal && k0 + 31 > q0 + off) ||
@@ -527,6 +536,11 @@ bwd_dkdv_kernel(BwdParams p) {
                 acc2[db] = mfma_32x32x16(db1, qT[2 * db + 1], acc2[db]);
             }
         }
+    };
+    if (total > 0) issue(BwdStage<0>{});
+    for (int f = 0; f < total; f += 2) {
+        tile(f, BwdStage<0>{});
+        if (f + 1 < total) tile(f + 1, BwdStage<1>{});
     }
 
     // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
