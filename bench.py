@@ -65,12 +65,32 @@ TRIALS = 5
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources; a stored traffic figure is only reported for
-    the exact sources its counters were taken on."""
+# The sources a profiled kernel is built and launched from: its own file plus
+# the shared device and launch headers and the C ABI that sizes its launch.
+KERNEL_SOURCES = {
+    "prefill_kernel": ["fa_prefill.hip"],
+    "splitkv_kernel": ["fa_splitkv.hip"],
+    "combine_kernel": ["fa_splitkv.hip"],
+    "bwd_dkdv_split_kernel": ["fa_backward.hip"],
+    "bwd_dkdv_kernel": ["fa_backward.hip"],
+    "bwd_dq_kernel": ["fa_backward.hip"],
+    "quantize_fp8_kernel": ["fa_fp8.hip"],
+    "varlen_schedule_kernel": ["fa_varlen.hip"],
+}
+KERNEL_COMMON = ["fa_device.h", "fa_internal.h", "fa_api.hip"]
+
+
+def kernel_source_hash(kernel: str = None) -> str:
+    """Hash of the kernel sources (all of them, or those of one kernel); a
+    stored traffic figure is only reported for the exact sources its counters
+    were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_07_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*"))):
+    if kernel is None:
+        paths = sorted(glob.glob(os.path.join(csrc, "*")))
+    else:
+        paths = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[kernel] + KERNEL_COMMON)]
+    for path in paths:
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode())
             h.update(f.read())
@@ -84,7 +104,8 @@ def stored_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("kernel") not in KERNEL_SOURCES or \
+            entry.get("source_hash") != kernel_source_hash(entry["kernel"]):
         return None
     return entry.get("bytes_per_launch")
 
