@@ -623,14 +623,17 @@ bwd_dkdv_split_kernel(BwdParams p) {
     const int nqt = (kw0 < n && i_hi > q_first) ? (i_hi - q_first + 31) / 32 : 0;
     const int total = p.r * nqt;
 
-    // Only the dV wavefronts copy (two 16-byte copies per lane per tile).
-    // Their step is the shorter one, and copies issued by all eight
-    // wavefronts right after the barrier queue behind each other and delay the
-    // dK chain.
+    // Only the dK wavefronts copy (two 16-byte copies per lane per tile):
+    // the dV wavefront's step (its products, then S and P of the next tile)
+    // is the longer one, and copies issued by all eight wavefronts right after
+    // the barrier queue behind each other.  Wavefront 4 also loads the rows'
+    // statistics.
+    const bool copier = !role_dv;
+    constexpr int kStatWave = 4;
     TileCopy<D, 256> cp;
     cp.init(w & 3, l);
     const uint32_t lds_q = lds_address(qt), lds_g = lds_address(gt);
-    float st_next = 0.0f;                       // wavefront 0: L2 (lanes < 32) or delta of a query
+    float st_next = 0.0f;                       // wavefront 4: L2 (lanes < 32) or delta of a query
     // Tiles are copied, and P formed, in order f = 0, 1, 2, ...: tile f is
     // query tile f % nqt of query head f / nqt.  Running counters give the
     // tile's first query and row index with scalar adds; a division per tile,
@@ -642,12 +645,12 @@ bwd_dkdv_split_kernel(BwdParams p) {
     // Step f of the loop below runs with f % 6 as a compile-time constant
     // (the LDS stage f % 3 and the P buffer f % 2), so every LDS address is a
     // per-lane base plus an immediate offset: no address arithmetic per step.
-    auto issue = [&](auto stage) __attribute__((always_inline)) {   // the next tile into LDS stage `stage` (dV role only)
+    auto issue = [&](auto stage) __attribute__((always_inline)) {   // the next tile into LDS stage `stage` (dK role only)
         const int q0 = q_first + cp_qi * 32;
         constexpr int buf = (decltype(stage)::value % NSTG) * TILE * 2;
-        cp.issue(p.q + cp_row * D, p.Lq - q0, lds_q + buf, w);
-        cp.issue(p.dout + cp_row * D, p.Lq - q0, lds_g + buf, w);
-        if (w == 0) {
+        cp.issue(p.q + cp_row * D, p.Lq - q0, lds_q + buf, w & 3);
+        cp.issue(p.dout + cp_row * D, p.Lq - q0, lds_g + buf, w & 3);
+        if (w == kStatWave) {
             const int i = q0 + (l & 31);
             float val = 0.0f;
             if (i < p.Lq) {
@@ -727,10 +730,10 @@ bwd_dkdv_split_kernel(BwdParams p) {
     };
 
     // ---- prologue: tiles 0 and 1 on their way, P(0) ------------------------
-    if (role_dv && total > 0) issue(BwdStage<0>{});
+    if (copier && total > 0) issue(BwdStage<0>{});
     wait_all_vector_loads();                    // tile 0, its statistics, this wavefront's K / V rows
-    if (w == 0) stat[l] = st_next;
-    if (role_dv && total > 1) issue(BwdStage<1>{});
+    if (w == kStatWave) stat[l] = st_next;
+    if (copier && total > 1) issue(BwdStage<1>{});
     __syncthreads();                            // tile 0 visible
     if (role_dv && active && total > 0) form_p(BwdStage<0>{});
 
@@ -739,9 +742,9 @@ bwd_dkdv_split_kernel(BwdParams p) {
         constexpr int stg = S6 % NSTG;
         constexpr int pbf = S6 & 1;
         wait_all_vector_loads();                // this wavefront's copies of tile f + 1
-        if (w == 0 && f + 1 < total) stat[((S6 + 1) % NSTG) * 64 + l] = st_next;
+        if (w == kStatWave && f + 1 < total) stat[((S6 + 1) % NSTG) * 64 + l] = st_next;
         __syncthreads();                        // tile f + 1 and P(f) visible; step f - 1 done everywhere
-        if (role_dv && f + 2 < total) issue(BwdStage<(S6 + 2) % 6>{});   // into the stage of tile f - 1
+        if (copier && f + 2 < total) issue(BwdStage<(S6 + 2) % 6>{});   // into the stage of tile f - 1
         if (!active) return;
         const bf16* Qs = qt + stg * TILE;
         const bf16* Gs = gt + stg * TILE;
