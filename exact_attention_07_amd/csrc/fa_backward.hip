@@ -730,35 +730,50 @@ bwd_dkdv_split_kernel(BwdParams p) {
     };
 
     // ---- prologue: tiles 0 and 1 on their way, P(0) ------------------------
+    // dV role: G(f)^T fragments of the next dV product, read at the end of
+    // the previous step (tile f is visible from step f - 1 on), so their LDS
+    // latency passes during the barrier.
+    bf16x8 gT[2 * DB];
+    auto read_gT = [&](auto stage) __attribute__((always_inline)) {
+        const bf16* Gs = gt + (decltype(stage)::value % NSTG) * TILE;
+#pragma unroll
+        for (int j = 0; j < 2 * DB; ++j) gT[j] = read_transposed<D>(Gs, 16 * (j & 1), 32 * (j >> 1), l);
+    };
     if (copier && total > 0) issue(BwdStage<0>{});
     wait_all_vector_loads();                    // tile 0, its statistics, this wavefront's K / V rows
     if (w == kStatWave) stat[l] = st_next;
     if (copier && total > 1) issue(BwdStage<1>{});
     __syncthreads();                            // tile 0 visible
-    if (role_dv && active && total > 0) form_p(BwdStage<0>{});
+    if (role_dv && active && total > 0) {
+        form_p(BwdStage<0>{});
+        read_gT(BwdStage<0>{});
+    }
 
-    auto step = [&](const int f, auto stage) __attribute__((always_inline)) {
+    // One step, in the two roles' own loops (so each role's registers are live
+    // only in its own loop); both loops take one workgroup barrier per step.
+    auto step = [&](const int f, auto stage, auto role) __attribute__((always_inline)) {
         constexpr int S6 = decltype(stage)::value;   // f % 6
         constexpr int stg = S6 % NSTG;
         constexpr int pbf = S6 & 1;
         wait_all_vector_loads();                // this wavefront's copies of tile f + 1
-        if (w == kStatWave && f + 1 < total) stat[((S6 + 1) % NSTG) * 64 + l] = st_next;
+        if (decltype(role)::value == 1 && w == kStatWave && f + 1 < total) stat[((S6 + 1) % NSTG) * 64 + l] = st_next;
         __syncthreads();                        // tile f + 1 and P(f) visible; step f - 1 done everywhere
-        if (copier && f + 2 < total) issue(BwdStage<(S6 + 2) % 6>{});   // into the stage of tile f - 1
+        if (decltype(role)::value == 1 && f + 2 < total) issue(BwdStage<(S6 + 2) % 6>{});   // into the stage of tile f - 1
         if (!active) return;
         const bf16* Qs = qt + stg * TILE;
         const bf16* Gs = gt + stg * TILE;
-        if (role_dv) {
-            // dV += P(f)^T G(f), then P(f + 1).
-            bf16x8 gT[2 * DB];
-#pragma unroll
-            for (int j = 0; j < 2 * DB; ++j) gT[j] = read_transposed<D>(Gs, 16 * (j & 1), 32 * (j >> 1), l);
+        (void)Qs; (void)Gs;
+        if constexpr (decltype(role)::value == 0) {
+            // dV += P(f)^T G(f), then P(f + 1) and the G(f + 1)^T fragments.
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 acc[db] = mfma_32x32x16(pb0, gT[2 * db], acc[db]);
                 acc[db] = mfma_32x32x16(pb1, gT[2 * db + 1], acc[db]);
             }
-            if (f + 1 < total) form_p(BwdStage<(S6 + 1) % 6>{});
+            if (f + 1 < total) {
+                form_p(BwdStage<(S6 + 1) % 6>{});
+                read_gT(BwdStage<(S6 + 1) % 6>{});
+            }
         } else {
             // dP(f), dS = P(f) (dP - delta), dK += dS^T Q(f).
             const f32x16 dp = product(Gs);
@@ -785,14 +800,18 @@ bwd_dkdv_split_kernel(BwdParams p) {
             }
         }
     };
-    for (int f = 0; f < total; f += 6) {
-        step(f, BwdStage<0>{});
-        if (f + 1 < total) step(f + 1, BwdStage<1>{});
-        if (f + 2 < total) step(f + 2, BwdStage<2>{});
-        if (f + 3 < total) step(f + 3, BwdStage<3>{});
-        if (f + 4 < total) step(f + 4, BwdStage<4>{});
-        if (f + 5 < total) step(f + 5, BwdStage<5>{});
-    }
+    auto run_role = [&](auto role) __attribute__((always_inline)) {
+        for (int f = 0; f < total; f += 6) {
+            step(f, BwdStage<0>{}, role);
+            if (f + 1 < total) step(f + 1, BwdStage<1>{}, role);
+            if (f + 2 < total) step(f + 2, BwdStage<2>{}, role);
+            if (f + 3 < total) step(f + 3, BwdStage<3>{}, role);
+            if (f + 4 < total) step(f + 4, BwdStage<4>{}, role);
+            if (f + 5 < total) step(f + 5, BwdStage<5>{}, role);
+        }
+    };
+    if (role_dv) run_role(BwdStage<0>{});
+    else         run_role(BwdStage<1>{});
 
     // Accumulator entry v of lane l: key k0 + 8*(v/4) + 4*hi + (v%4), column
     // 32*db + (l % 32).  Keys past n hold zeros.
