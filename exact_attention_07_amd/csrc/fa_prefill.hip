@@ -568,7 +568,9 @@ prefill_kernel(PrefillParams p) {
     };
 
     // Matrix phase M(t) as one software pipeline over its products: the KB*KS
-    // score products of tile t+1, then the DB*KB*2 PV products of tile t.
+    // score products of tile t+1, then the DB*KB*2 PV products of tile t, each
+    // group ordered so that consecutive products go to different accumulators
+    // (the two key blocks' S^T, the DB blocks of O^T).
     // Product i is issued right after the LDS read(s) of product i + AHEAD, so
     // every operand is read AHEAD products (~32 cycles each) before its use
     // and only ~AHEAD fragments are live.  A scheduling fence after each step
@@ -585,10 +587,10 @@ prefill_kernel(PrefillParams p) {
         bf16x8 frag[NOPS];                  // PV operands (entries NQ..)
         auto read_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
-                kfrag[i] = k_operand(Ks, i / KSQ, i % KSQ);
+                kfrag[i] = k_operand(Ks, i % KB, i / KB);
             } else {
                 const int f = i - NQ;
-                const int db = f / (KB * 2), kb = (f / 2) % KB, half = f % 2;
+                const int db = f % DB, kb = (f / DB) / 2, half = (f / DB) % 2;
                 const int row0 = kb * 32 + half * 16 + vrow;
                 const int col = db * 32 + vcol;
                 const bf16* base = Vs + row0 * D + (((col >> 3) ^ vxor) * 8) + (col & 7);
@@ -615,13 +617,13 @@ prefill_kernel(PrefillParams p) {
         };
         auto mfma_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
-                const int kb = i / KSQ, ks = i % KSQ;
+                const int kb = i % KB, ks = i / KB;
                 s[kb] = score_mfma(kfrag[i], ks, ks == 0 ? zero_f32x16() : s[kb]);
                 if (i % (NQ / NP) == 0) convert_p(i / (NQ / NP));
                 if (i == NQ - 1) ell_r += corr ? 0.0f : sr[0] + sr[1];
             } else {
                 const int f = i - NQ;
-                const int db = f / (KB * 2), kb = (f / 2) % KB, half = f % 2;
+                const int db = f % DB, kb = (f / DB) / 2, half = (f / DB) % 2;
                 acc[db] = mfma_32x32x16(frag[i], pb[kb][half], acc[db]);
             }
         };
