@@ -84,17 +84,21 @@ constexpr float kTauSum = 256.0f;
 // moves O by up to 2^-8 sum_j P_j |v_j - O|: on rows that a few keys dominate
 // that reaches a few 1e-3 of an output of magnitude 2-4.  Such a row is
 // recognised when its reference moves (the row max is known exactly then):
-// its largest p is at least kPeakFrac of its running sum.  Once kSplitRows
-// rows of a workgroup are (a head whose scores spread widely), the workgroup
-// switches, for the rest of its KV loop, to split probabilities: the residual
-// p - bf16(p), itself rounded to bf16, goes through a second product with the
-// same V fragments, so every weight is exact to ~2^-16, and the normaliser
-// takes the fp32 sum of p for those tiles.  The switch is one counter in LDS
-// that every wavefront adds to and reads at its next vector phase: all
-// wavefronts of a workgroup then do the same work per tile, so the phases stay
-// balanced.
+// its largest p is at least kPeakFrac of its running sum, judged only once
+// the row has seen kJudgeKeys of its keys (or all, if it has fewer), since a
+// row whose first tile holds a few of its keys is dominated there whatever
+// the rest.  Once kSplitRows rows of a workgroup are (a head whose scores
+// spread widely), the workgroup switches, for the rest of its KV loop, to
+// split probabilities: the residual p - bf16(p), itself rounded to bf16, goes
+// through a second product with the same V fragments, so every weight is
+// exact to ~2^-16, and the normaliser adds the residuals' sum to the rounded
+// one.  The switch is one counter in LDS that every wavefront adds to and
+// reads at its next vector phase: all wavefronts of a workgroup then do the
+// same work per tile, so the phases stay balanced.  The modifier and FP8
+// kernels keep bf16 probabilities (their bars account for them).
 constexpr float kPeakFrac = 1.0f / 2.0f;
 constexpr int kSplitRows = 16;              // dominated rows that switch a workgroup to split probabilities
+constexpr int kJudgeKeys = 32;              // keys a row must have seen to be judged dominated
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -142,7 +146,9 @@ prefill_kernel(PrefillParams p) {
     static_assert(!FP8 || (D == 128 && !WINDOW), "the FP8 scores are built for D = 128 without a window");
     static_assert(MOD == kModNone || (!FP8 && !WINDOW), "score modifiers are built for the bf16 kernel without a window");
     static_assert(!VARLEN || (!FP8 && !WINDOW && MOD == kModNone), "packed batches are built for the plain bf16 kernel");
-    constexpr bool CORR = D == 128;         // residual correction of dominant probabilities
+    // Split probabilities in the bf16 kernels at D = 128 without modifiers: the
+    // modifier and FP8 instantiations keep bf16 probabilities throughout.
+    constexpr bool CORR = D == 128 && !FP8 && MOD == kModNone;
     constexpr int KSQ = FP8 ? D / 64 : KS;  // k-steps of S^T
     constexpr int NIK = FP8 ? BN * D / (NT * 16) : NI;   // 16-byte copies per thread per K tile
     static_assert(NIK >= 1, "a K tile must split evenly over the workgroup");
@@ -512,7 +518,7 @@ prefill_kernel(PrefillParams p) {
         const bool move = ref == kNegInf || !(row_sum <= kTauSum);
         if constexpr (CORR)   // counted by all wavefronts at earlier phases
             split = split || __builtin_amdgcn_readfirstlane(flag_seen) >= kSplitRows;
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
             if constexpr (MOD == kModAlibi) {
                 // The row max is of the biased scores: apply the bias here.
                 if (folded) add_alibi();
@@ -539,28 +545,42 @@ prefill_kernel(PrefillParams p) {
             se_l = (se[0] + se[1]) + (se[2] + se[3]);
             row_sum = sum_with_partner(se_l);
             if constexpr (CORR) {
-                // After the move the row's largest p is exactly 2^-kTau.
-                const bool dominated = shift && 1.0f / kTauSum >= kPeakFrac * (ell_e + row_sum);
+                // After the move the row's largest p is exactly 2^-kTau.  A row
+                // is judged once it has seen kJudgeKeys of its keys, or all of
+                // them if it has fewer (key order: its keys up to the tile's
+                // end so far); a row with a few keys so far is dominated now
+                // whatever the rest of its keys.
+                const int qpos = qrow + off;
+                const int key_hi = min(CAUSAL ? qpos : n - 1, n - 1);
+                const int key_lo = WINDOW ? max(qpos - p.window + 1, 0) : 0;
+                const int seen = min(key_hi, k0 + BN - 1) - key_lo + 1;
+                const bool judged = seen >= min(kJudgeKeys, key_hi - key_lo + 1);
+                const bool dominated = shift && judged && 1.0f / kTauSum >= kPeakFrac * (ell_e + row_sum);
                 const uint64_t dm = __builtin_amdgcn_ballot_w64(dominated && hi == 0);   // one lane per row
                 if (!split && dm != 0 && l == 0) atomicAdd(&split_rows, (int)__builtin_popcountll(dm));
             }
         }
         corr = 0;
         if constexpr (CORR) {
-            if (split) {
-                // Residuals of every chunk to LDS for the next matrix phase; the
-                // normaliser takes this tile's fp32 sum (the matrix phase then
-                // leaves out its rounded sum).
+            if (__builtin_expect(split, 0)) {
+                // Residuals of every chunk to LDS for the next matrix phase.  The
+                // normaliser gets their sum here and the rounded sum in the
+                // matrix phase: sum_j bf16(p_j) + (p_j - bf16(p_j)) = sum_j p_j.
+                float rs[2] = {0.0f, 0.0f};
 #pragma unroll
                 for (int cc = 0; cc < NCH; ++cc) {
                     const float* e = pe[cc / 2][cc % 2];
                     const bf16x8 hi8 = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+                    float r8[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        r8[j] = e[j] - (float)hi8[j];
+                        rs[j & 1] += r8[j];
+                    }
                     plo_lds[(w * NCH + cc) * 64 + l] =
-                        to_bf16x8(e[0] - (float)hi8[0], e[1] - (float)hi8[1], e[2] - (float)hi8[2],
-                                  e[3] - (float)hi8[3], e[4] - (float)hi8[4], e[5] - (float)hi8[5],
-                                  e[6] - (float)hi8[6], e[7] - (float)hi8[7]);
+                        to_bf16x8(r8[0], r8[1], r8[2], r8[3], r8[4], r8[5], r8[6], r8[7]);
                 }
-                ell_r += se_l;
+                ell_r += rs[0] + rs[1];
                 corr = 1;
             }
         }
@@ -614,13 +634,17 @@ prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 sr[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[2 * j], pv[2 * j + 1]}, ones, sr[j & 1], false);
+            // Pin the sums here, between the score products: otherwise the
+            // compiler sinks them (and a second conversion of P) past the
+            // residual branch, to the end of the phase.
+            asm volatile("" : "+v"(sr[0]), "+v"(sr[1]));
         };
         auto mfma_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
                 const int kb = i % KB, ks = i / KB;
                 s[kb] = score_mfma(kfrag[i], ks, ks == 0 ? zero_f32x16() : s[kb]);
                 if (i % (NQ / NP) == 0) convert_p(i / (NQ / NP));
-                if (i == NQ - 1) ell_r += corr ? 0.0f : sr[0] + sr[1];
+                if (i == NQ - 1) ell_r += sr[0] + sr[1];
             } else {
                 const int f = i - NQ;
                 const int db = f % DB, kb = (f / DB) / 2, half = (f / DB) % 2;
@@ -638,7 +662,7 @@ prefill_kernel(PrefillParams p) {
         }
         // Residual products of a splitting wavefront (wave-uniform): the same V
         // fragments times bf16(p - bf16(p)).
-        if (CORR && corr != 0) {
+        if (CORR && __builtin_expect(corr != 0, 0)) {
             // Side-effect marker: keeps the compiler from executing these
             // products speculatively (as a select) on the common path.
             asm volatile("" ::: "memory");
