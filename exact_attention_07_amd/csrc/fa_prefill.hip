@@ -92,10 +92,13 @@ constexpr float kTauSum = 256.0f;
 // split probabilities: the residual p - bf16(p), itself rounded to bf16, goes
 // through a second product with the same V fragments, so every weight is
 // exact to ~2^-16, and the normaliser adds the residuals' sum to the rounded
-// one.  The switch is one counter in LDS that every wavefront adds to and
-// reads at its next vector phase: all wavefronts of a workgroup then do the
-// same work per tile, so the phases stay balanced.  The modifier and FP8
-// kernels keep bf16 probabilities (their bars account for them).
+// one.  The switch is one counter in LDS that every wavefront adds to; each
+// reads it after the prologue's tile and then once per cycle of LDS stages,
+// and moves from the plain tile loop to a split one (whose matrix phase
+// follows every PV product by its residual product on the same fragment), so
+// the plain loop carries no residual code.  All wavefronts of a workgroup
+// then do the same work per tile, so the phases stay balanced.  The modifier
+// and FP8 kernels keep bf16 probabilities (their bars account for them).
 constexpr float kPeakFrac = 1.0f / 2.0f;
 constexpr int kSplitRows = 16;              // dominated rows that switch a workgroup to split probabilities
 constexpr int kJudgeKeys = 32;              // keys a row must have seen to be judged dominated
@@ -424,7 +427,6 @@ prefill_kernel(PrefillParams p) {
     // rounded values) while its score products run.
     float pe[KB][2][8];
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-    int corr = 0;                           // the next PV product takes the residual products (wave-uniform)
     bool split = false;                     // this wavefront splits its probabilities (wave-uniform, sticky)
     float ksc_next = k_scale_of(0);         // FP8: s_k of the tile softmax_tile handles next
     // Modifier constants in raw-score units.
@@ -432,12 +434,41 @@ prefill_kernel(PrefillParams p) {
                       : MOD == kModSoftcap ? p.softcap / p.scale : 0.0f;   // slope, or cap
     const float mod_b = MOD == kModSoftcap ? 2.0f * p.scale * 1.4426950408889634f / p.softcap : 0.0f;
 
+    // Residuals p - bf16(p) of every 16-key chunk of pe to LDS, for the next
+    // matrix phase's residual products; returns their sum (this lane's half
+    // of the row).  The normaliser takes it with the rounded sum of the matrix
+    // phase: sum_j bf16(p_j) + (p_j - bf16(p_j)) = sum_j p_j.
+    auto write_residuals = [&]() __attribute__((always_inline)) -> float {
+        float rs[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int cc = 0; cc < NCH; ++cc) {
+            const float* e = pe[cc / 2][cc % 2];
+            const bf16x8 hi8 = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+            float r8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                r8[j] = e[j] - (float)hi8[j];
+                rs[j & 1] += r8[j];
+            }
+            plo_lds[(w * NCH + cc) * 64 + l] = to_bf16x8(r8[0], r8[1], r8[2], r8[3], r8[4], r8[5], r8[6], r8[7]);
+        }
+        return rs[0] + rs[1];
+    };
+    float rs_first = 0.0f;                  // residual sum of the prologue's tile
+
     // Vector phase for tile t (scores in s): mask where needed, p -> pe and the
-    // fp32 row sum, and the rare reference move.
-    auto softmax_tile = [&](int t) __attribute__((always_inline)) {
+    // fp32 row sum, and the rare reference move.  MODE (split probabilities,
+    // D = 128): 0 plain; 1 plain, and the wavefront switches to split
+    // probabilities from this tile on once the workgroup's count is reached
+    // (only before a matrix phase of LDS stage 0, so each form of the tile
+    // loop runs whole stage cycles); 2 split; 3 plain, with the residuals
+    // written and their sum kept aside (the prologue's tile, whose form is
+    // decided after it).
+    auto softmax_tile = [&](int t, auto mode) __attribute__((always_inline)) {
+        constexpr int MODE = CORR ? decltype(mode)::value : 0;
         const int k0 = tile_abs(t) * BN;
-        // The workgroup's split flag, read early (used after the exponentials).
-        const int flag_seen = CORR ? split_rows : 0;
+        // The workgroup's split count, read early (used after the exponentials).
+        const int flag_seen = MODE == 1 ? split_rows : 0;
         const float ct = FP8 ? cq * ksc_next : c;   // this tile's exponent scale
         if (FP8) ksc_next = k_scale_of(t + 1);
         // ALiBi: |pos_i - pos_j| = |base - K_v| with base = qpos - k0 - 8 hi
@@ -516,8 +547,8 @@ prefill_kernel(PrefillParams p) {
         float se_l = (se[0] + se[1]) + (se[2] + se[3]);
         float row_sum = sum_with_partner(se_l);
         const bool move = ref == kNegInf || !(row_sum <= kTauSum);
-        if constexpr (CORR)   // counted by all wavefronts at earlier phases
-            split = split || __builtin_amdgcn_readfirstlane(flag_seen) >= kSplitRows;
+        if constexpr (MODE == 1)   // counted by all wavefronts at earlier phases
+            split = __builtin_amdgcn_readfirstlane(flag_seen) >= kSplitRows;
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
             if constexpr (MOD == kModAlibi) {
                 // The row max is of the biased scores: apply the bias here.
@@ -557,32 +588,12 @@ prefill_kernel(PrefillParams p) {
                 const bool judged = seen >= min(kJudgeKeys, key_hi - key_lo + 1);
                 const bool dominated = shift && judged && 1.0f / kTauSum >= kPeakFrac * (ell_e + row_sum);
                 const uint64_t dm = __builtin_amdgcn_ballot_w64(dominated && hi == 0);   // one lane per row
-                if (!split && dm != 0 && l == 0) atomicAdd(&split_rows, (int)__builtin_popcountll(dm));
+                if (MODE != 2 && dm != 0 && l == 0) atomicAdd(&split_rows, (int)__builtin_popcountll(dm));
             }
         }
-        corr = 0;
-        if constexpr (CORR) {
-            if (__builtin_expect(split, 0)) {
-                // Residuals of every chunk to LDS for the next matrix phase.  The
-                // normaliser gets their sum here and the rounded sum in the
-                // matrix phase: sum_j bf16(p_j) + (p_j - bf16(p_j)) = sum_j p_j.
-                float rs[2] = {0.0f, 0.0f};
-#pragma unroll
-                for (int cc = 0; cc < NCH; ++cc) {
-                    const float* e = pe[cc / 2][cc % 2];
-                    const bf16x8 hi8 = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-                    float r8[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        r8[j] = e[j] - (float)hi8[j];
-                        rs[j & 1] += r8[j];
-                    }
-                    plo_lds[(w * NCH + cc) * 64 + l] =
-                        to_bf16x8(r8[0], r8[1], r8[2], r8[3], r8[4], r8[5], r8[6], r8[7]);
-                }
-                ell_r += rs[0] + rs[1];
-                corr = 1;
-            }
+        if constexpr (MODE != 0) {
+            if (MODE == 3) rs_first = write_residuals();
+            else if (MODE == 2 || __builtin_expect(split, 0)) ell_r += write_residuals();
         }
         ell_e += row_sum;
     };
@@ -595,16 +606,23 @@ prefill_kernel(PrefillParams p) {
     // every operand is read AHEAD products (~32 cycles each) before its use
     // and only ~AHEAD fragments are live.  A scheduling fence after each step
     // keeps this order.
-    auto matrix_phase = [&](auto phase) __attribute__((always_inline)) {
+    // The split form (SPL, a splitting wavefront's phase) follows each PV
+    // product by its residual product, with the same V fragment and the same
+    // accumulator (a back-to-back accumulation); the residual operand of a
+    // 16-key chunk is read from LDS with the chunk's first V fragment.
+    auto matrix_phase = [&](auto phase, auto spl) __attribute__((always_inline)) {
         constexpr int PH = decltype(phase)::value;      // t % NB
+        constexpr bool SPL = decltype(spl)::value;
         const bf16* Ks = smem + ((PH + 1) % NB) * TILE;
         const bf16* Vs = smem + (NB + PH) * TILE;
         constexpr int NQ = KB * KSQ;        // score products
         constexpr int NF = DB * KB * 2;     // PV products (one V fragment each)
         constexpr int NOPS = NQ + NF;
         constexpr int AHEAD = 6;
+        constexpr int NP = KB * 2;          // bf16x8 operands of P^T (16-key chunks)
         SA kfrag[NQ];                       // score operands
         bf16x8 frag[NOPS];                  // PV operands (entries NQ..)
+        bf16x8 plo[NP];                     // residual operands (SPL)
         auto read_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
                 kfrag[i] = k_operand(Ks, i % KB, i / KB);
@@ -618,11 +636,11 @@ prefill_kernel(PrefillParams p) {
                 const bf16x4 up = lds_read_transposed(base + 4 * D);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { frag[i][e] = lo[e]; frag[i][4 + e] = up[e]; }
+                if (SPL && db == 0) plo[f / DB] = plo_lds[(w * NP + f / DB) * 64 + l];
             }
         };
         // P -> bf16 operand and the rounded row sum, spread over the score
         // products (which do not need them); the PV products come after.
-        constexpr int NP = KB * 2;           // bf16x8 operands of P^T
         static_assert(NQ % NP == 0, "conversions per score product");
         bf16x8 pb[KB][2];
         float sr[2] = {0.0f, 0.0f};
@@ -635,8 +653,8 @@ prefill_kernel(PrefillParams p) {
             for (int j = 0; j < 4; ++j)
                 sr[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[2 * j], pv[2 * j + 1]}, ones, sr[j & 1], false);
             // Pin the sums here, between the score products: otherwise the
-            // compiler sinks them (and a second conversion of P) past the
-            // residual branch, to the end of the phase.
+            // compiler sinks them (and a second conversion of P) to the end
+            // of the phase.
             asm volatile("" : "+v"(sr[0]), "+v"(sr[1]));
         };
         auto mfma_op = [&](int i) __attribute__((always_inline)) {
@@ -649,8 +667,14 @@ prefill_kernel(PrefillParams p) {
                 const int f = i - NQ;
                 const int db = f % DB, kb = (f / DB) / 2, half = (f / DB) % 2;
                 acc[db] = mfma_32x32x16(frag[i], pb[kb][half], acc[db]);
+                if constexpr (SPL) acc[db] = mfma_32x32x16(frag[i], plo[f / DB], acc[db]);
             }
         };
+        if constexpr (SPL) {
+            // Side-effect marker: keeps the compiler from merging the two forms
+            // of the phase (executing the residual products as selects).
+            asm volatile("" ::: "memory");
+        }
 #pragma unroll
         for (int i = 0; i < AHEAD; ++i) read_op(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -659,32 +683,6 @@ prefill_kernel(PrefillParams p) {
             mfma_op(i);
             if (i + AHEAD < NOPS) read_op(i + AHEAD);
             __builtin_amdgcn_sched_barrier(0);
-        }
-        // Residual products of a splitting wavefront (wave-uniform): the same V
-        // fragments times bf16(p - bf16(p)).
-        if (CORR && __builtin_expect(corr != 0, 0)) {
-            // Side-effect marker: keeps the compiler from executing these
-            // products speculatively (as a select) on the common path.
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int c = 0; c < NP; ++c) {
-                {
-                    const int kb = c / 2, half = c % 2;
-                    const bf16x8 lo = plo_lds[(w * NP + c) * 64 + l];
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int row0 = kb * 32 + half * 16 + vrow;
-                        const int col = db * 32 + vcol;
-                        const bf16* base = Vs + row0 * D + (((col >> 3) ^ vxor) * 8) + (col & 7);
-                        const bf16x4 v0 = lds_read_transposed(base);
-                        const bf16x4 v1 = lds_read_transposed(base + 4 * D);
-                        bf16x8 fr;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) { fr[e] = v0[e]; fr[4 + e] = v1[e]; }
-                        acc[db] = mfma_32x32x16(fr, lo, acc[db]);
-                    }
-                }
-            }
         }
     };
 
@@ -699,14 +697,15 @@ prefill_kernel(PrefillParams p) {
     wait_vector_loads_until<2 * NIK + 2 * NI>();
     __syncthreads();
     score_tile(0);
-    softmax_tile(0);
+    softmax_tile(0, Const<3>{});
     wait_vector_loads_until<NIK + NI>();    // K(1) and V(0), the first matrix phase's operands
     __syncthreads();                        // ... visible; K(0) read by every wavefront before M(0) refills its buffer
     if (grp == 1) __syncthreads();          // the second group runs one phase behind
 
     // One tile: matrix phase M(t), barrier, vector phase V(t), barrier.
     // PH = t % NB is a compile-time constant, so every LDS offset is one.
-    auto tile_step = [&](int t, auto phase) __attribute__((always_inline)) {
+    // MODE as in softmax_tile; the matrix phase takes the split form in mode 2.
+    auto tile_step = [&](int t, auto phase, auto mode) __attribute__((always_inline)) {
         // ---- matrix phase M(t) ----
         __builtin_amdgcn_s_setprio(1);
         copy_k(t + NB);                     // into the buffer of K(t)
@@ -714,18 +713,38 @@ prefill_kernel(PrefillParams p) {
         // The score product runs for the last tile too (on the zero-filled
         // buffer past the end; the result is not used), which keeps the
         // phase one basic block.
-        matrix_phase(phase);
+        matrix_phase(phase, Const<decltype(mode)::value == 2>{});
         __builtin_amdgcn_s_setprio(0);
         wait_vector_loads_until<NIK + NI>();   // the copies of M(t-1) have landed
         __syncthreads();
         // ---- vector phase V(t) ----
-        if (t + 1 < ntiles) softmax_tile(t + 1);
+        if (t + 1 < ntiles) softmax_tile(t + 1, mode);
         __syncthreads();
     };
-    for (int t = 0; t < ntiles; t += NB) {
-        tile_step(t, Const<0>{});
-        if (t + 1 < ntiles) tile_step(t + 1, Const<1>{});
-        if (t + 2 < ntiles) tile_step(t + 2, Const<2>{});
+    // Split probabilities: the plain loop runs until this wavefront switches
+    // (at the end of a stage cycle), then the split loop runs the rest.  Both
+    // take the same barriers per tile, so wavefronts in either loop stay in step.
+    int t = 0;
+    if constexpr (CORR) {
+        // The counts of the prologue's tile are complete: a workgroup whose
+        // rows are dominated from the start splits from its first product.
+        split = __builtin_amdgcn_readfirstlane(split_rows) >= kSplitRows;
+        ell_r += split ? rs_first : 0.0f;
+        if (!split) for (; t < ntiles; t += NB) {
+            tile_step(t, Const<0>{}, Const<0>{});
+            if (t + 1 < ntiles) tile_step(t + 1, Const<1>{}, Const<0>{});
+            if (t + 2 < ntiles) tile_step(t + 2, Const<2>{}, Const<1>{});
+            if (__builtin_expect(split, 0)) {
+                t += NB;
+                break;
+            }
+        }
+    }
+    for (; t < ntiles; t += NB) {
+        constexpr int M = CORR ? 2 : 0;
+        tile_step(t, Const<0>{}, Const<M>{});
+        if (t + 1 < ntiles) tile_step(t + 1, Const<1>{}, Const<M>{});
+        if (t + 2 < ntiles) tile_step(t + 2, Const<2>{}, Const<M>{});
     }
     if (grp == 0) __syncthreads();          // match the second group's extra barrier
     wait_all_vector_loads();                // copies past the last tile (zero-range) drained
