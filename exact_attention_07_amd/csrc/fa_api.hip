@@ -505,7 +505,7 @@ int fa_quantize_fp8(const void* x, void* x8, float* scales, int heads, int L, in
     p.scales = scales;
     p.signs = signs;
     p.heads = heads; p.L = L; p.block_rows = block_rows; p.nblk = (int)nblk;
-    hipError_t e = fa::launch_quantize_fp8(D, p, reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = fa::launch_quantize_fp8(D, p, cu_count(), reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
     return FA_OK;
 }
