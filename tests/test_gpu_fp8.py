@@ -81,6 +81,29 @@ def test_quantizer_matches_oracle(dev, case):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
 
 
+@pytest.mark.parametrize("D,R", [(128, 256), (128, 64), (64, 256)])
+def test_quantizer_several_blocks_per_workgroup(dev, D, R):
+    # The quantizer's workgroups take every grid-th block, each block's copy
+    # in flight during the previous one and its codes stored during the next:
+    # enough blocks that every workgroup runs at least three, the last block
+    # of each head partial, bit for bit against the oracle.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slices = -(-R // (64 // (D // 64)))
+    grid = cus * (8 // min(slices, 8))
+    H = 16
+    nblk = -(-3 * grid // H) + 1                 # blocks per head
+    L = nblk * R - R // 3                        # the last block of each head partial
+    x = rows(2351 + D + R, (1, H, L, D), 1)
+    sg = signs_of(31 + D, D)
+    codes, scales = binding.quantize_fp8(x.to(dev), R, sg.to(dev))
+    torch.cuda.synchronize()
+    print(f"[fp8] quantizer D={D} block_rows={R}: {H * nblk} blocks on a grid of {grid}", flush=True)
+    rc, rs, _ = oracle.fp8.quantize_rows(x, R, sg.numpy())
+    assert np.array_equal(scales.cpu().numpy().astype(np.float64), rs), "block scales differ"
+    bad = np.argwhere(codes.cpu().numpy() != rc)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
+
+
 FWD_CASES = [
     # B, Hq, Hkv, Lq, Lk, causal, kv_lens, transform
     (1, 2, 2, 64, 64, False, None, False),
