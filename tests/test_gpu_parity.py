@@ -21,7 +21,7 @@ import torch
 import oracle
 from exact_attention_07_amd import binding, workloads as W
 
-from tests.parity import compare, compare_all_rows  # noqa: E402
+from tests.parity import compare, compare_all_rows, variant_spread  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -219,6 +219,31 @@ def test_tile_sum_alone_moves_reference(dev, D):
     o, lse = run(case, dev)
     ref_o, ref_lse = full_reference(case)
     report(f"tile-sum move D{D}", compare(o, lse, ref_o, ref_lse))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dominant_keys_appear_mid_sequence(dev, causal):
+    # Two "needle" keys (positions 300 and 700) aligned with every query: from
+    # their tiles on, the rows they reach are dominated by them (weights near
+    # 0.4 / 0.6 after the second).  At D = 128 the workgroups that meet them
+    # mid-loop move from the plain tile loop to the split-probability one at
+    # the next cycle of LDS stages, so the first needle's tile (and the next)
+    # keeps bf16 probabilities: the variant bar (parity.py), whose bound
+    # covers bf16 probabilities, applies.  A mistake in the move between the
+    # loops (a wrong stage, a lost tile) would break it by far.
+    g = torch.Generator().manual_seed(33)
+    B, Hq, Hkv, L, D = 1, 4, 2, 1024, 128
+    q = torch.randn(B, Hq, L, D, generator=g) * 0.05
+    k = torch.randn(B, Hkv, L, D, generator=g) * 0.05
+    v = torch.randn(B, Hkv, L, D, generator=g)
+    q[..., 0] = 1.0
+    k[..., 300, 0] = 10.0
+    k[..., 700, 0] = 10.5
+    case = W.Inputs(q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), None, 1.0, causal)
+    o, lse = run(case, dev)
+    ref_o, ref_lse = full_reference(case)
+    report(f"needles mid-sequence causal={causal}",
+           compare(o, lse, ref_o, ref_lse, spread=variant_spread(case)))
 
 
 def test_causal_row_zero_is_value_row_zero_exactly(dev):
