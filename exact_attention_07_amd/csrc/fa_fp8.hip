@@ -41,11 +41,9 @@ namespace fa {
 
 namespace {
 
-// Lane-pair exchange of a double through two quad-permute DPP moves (lanes
-// xor 1 or xor 2 within each group of four).
-template <int XOR>
-__device__ __forceinline__ double dpp_xor(double v) {
-    constexpr int ctrl = XOR == 1 ? 0xB1 : 0x4E;    // quad_perm [1,0,3,2] / [2,3,0,1]
+// The double held by lane l ^ 1, through two quad-permute DPP moves.
+__device__ __forceinline__ double lane_pair_swap(double v) {
+    constexpr int ctrl = 0xB1;              // quad_perm [1,0,3,2]
     // Every lane reads a valid partner, so no lane keeps an old value: a plain
     // DPP move (no initialisation of the destination).
     const long long b = __builtin_bit_cast(long long, v);
@@ -121,7 +119,7 @@ __device__ __forceinline__ void transform_row(const QuantParams& p, int h, const
         // bit set keeps partner - own.
         const double s1 = h ? -1.0 : 1.0;
 #pragma unroll
-        for (int e = 0; e < 64; ++e) x[e] = __builtin_fma(x[e], s1, dpp_xor<1>(x[e]));
+        for (int e = 0; e < 64; ++e) x[e] = __builtin_fma(x[e], s1, lane_pair_swap(x[e]));
     }
 #pragma unroll
     for (int e = 0; e < 64; ++e) out[e] = (float)x[e];
