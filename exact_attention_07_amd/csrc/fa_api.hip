@@ -518,7 +518,6 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
     const Shape s{B, Hq, Hkv, Lq, Lk, D};
     int st = validate(q8, k8, v, o, lse, s, causal, scale, kv_lens);
     if (st != FA_OK) return st;
-    if (D != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward is built for D=128 (got D=%d)", D);
     if (!q_scales || (Lk > 0 && !k_scales)) return fail(FA_ERR_INVALID_ARG, "q_scales and k_scales must not be NULL");
     if (!aligned(q_scales, 4) || !aligned(k_scales, 4))
         return fail(FA_ERR_INVALID_ARG, "q_scales and k_scales must be 4-byte aligned");
@@ -542,7 +541,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
     p.c = scale * 1.4426950408889634f;
     const long long total = (long long)B * Hq * p.n_qblocks;
     if (!grid_fits(total, 512)) return fail(FA_ERR_INVALID_ARG, "grid too large");
-    hipError_t e = fa::launch_prefill_fp8(causal != 0, p, reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = fa::launch_prefill_fp8(D, causal != 0, p, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
     return FA_OK;
 }

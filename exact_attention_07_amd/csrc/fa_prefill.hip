@@ -111,9 +111,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // lane holds 32 bytes of its K row (A) or Q row (B); the instruction pairs
 // byte e of lane half hi in A with the same in B, so giving both the bytes
 // 64 ks + 32 hi + e of a row makes the product a dot product over D.  K rows
-// of 128 bytes sit in LDS in 16-byte chunks XOR-swizzled by (row / 2) % 8,
-// so 16 lanes reading one chunk column of 16 rows hit 16 distinct bank
-// groups.  V and P stay bf16 (the PV product is the bf16 one).
+// of D bytes sit in LDS in 16-byte chunks XOR-swizzled by k8_swizzle, so 16
+// lanes reading one chunk column of 16 rows hit 16 distinct bank groups (of
+// 16 bytes: group (D/16) row + chunk, mod 16).  V and P stay bf16 (the PV
+// product is the bf16 one).
+template <int D>
+__device__ __forceinline__ int k8_swizzle(int row) {
+    return D == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
 template <bool FP8>
 struct ScoreOperand { typedef bf16x8 type; };
 template <>
@@ -146,14 +151,18 @@ prefill_kernel(PrefillParams p) {
     static_assert(BM == kPrefillRows, "host and kernel disagree on the query block");
     static_assert(NI >= 1 && (BN * CH) % NT == 0, "a tile must split evenly over the workgroup");
     static_assert(CAUSAL || !WINDOW, "the window is causal");
-    static_assert(!FP8 || (D == 128 && !WINDOW), "the FP8 scores are built for D = 128 without a window");
+    static_assert(!FP8 || !WINDOW, "the FP8 scores are built without a window");
     static_assert(MOD == kModNone || (!FP8 && !WINDOW), "score modifiers are built for the bf16 kernel without a window");
     static_assert(!VARLEN || (!FP8 && !WINDOW && MOD == kModNone), "packed batches are built for the plain bf16 kernel");
     // Split probabilities in the bf16 kernels at D = 128 without modifiers: the
     // modifier and FP8 instantiations keep bf16 probabilities throughout.
     constexpr bool CORR = D == 128 && !FP8 && MOD == kModNone;
     constexpr int KSQ = FP8 ? D / 64 : KS;  // k-steps of S^T
-    constexpr int NIK = FP8 ? BN * D / (NT * 16) : NI;   // 16-byte copies per thread per K tile
+    // 16-byte copies per thread per K tile.  An E4M3 tile at D = 64 (4 KB) is
+    // half a copy per thread: the copies of its second half of positions fall
+    // on rows past the tile, outside the descriptor's range (nothing is
+    // read), into the unused second half of the stage buffer.
+    constexpr int NIK = FP8 ? (BN * D + NT * 16 - 1) / (NT * 16) : NI;
     static_assert(NIK >= 1, "a K tile must split evenly over the workgroup");
     typedef typename ScoreOperand<FP8>::type SA;
 
@@ -343,7 +352,7 @@ prefill_kernel(PrefillParams p) {
         for (int i = 0; i < NIK; ++i) {     // E4M3 rows of D bytes: D / 16 chunks
             const int P = (w * NIK + i) * 64 + l;
             const int row = P / (D / 16);
-            koff[i] = (uint32_t)(row * D + (((P % (D / 16)) ^ ((row >> 1) & 7)) * 16));
+            koff[i] = (uint32_t)(row * D + (((P % (D / 16)) ^ k8_swizzle<D>(row)) * 16));
         }
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)smem);
@@ -361,7 +370,7 @@ prefill_kernel(PrefillParams p) {
     auto copy_k = [&](int t) __attribute__((always_inline)) {
         if constexpr (FP8) {
             const int ta = tb + t;
-            const int rows = n - ta * BN;
+            const int rows = min(n - ta * BN, BN);   // the tile's rows only (see NIK)
             const i32x4 d = make_desc(p.k8 + kvoff + (size_t)(rows > 0 ? ta : 0) * BN * D,
                                       (uint32_t)(rows > 0 ? rows : 0) * D);
 #pragma unroll
@@ -387,7 +396,7 @@ prefill_kernel(PrefillParams p) {
     auto k_operand = [&](const bf16* Ks, int kb, int ks) __attribute__((always_inline)) -> SA {
         if constexpr (FP8) {
             const uint8_t* row = reinterpret_cast<const uint8_t*>(Ks) + (kb * 32 + krow) * D;
-            const int x8 = (krow >> 1) & 7;
+            const int x8 = k8_swizzle<D>(krow);   // rows kb*32 + krow share it
             const int c0 = 4 * ks + 2 * hi;
             const i32x4 lo = *reinterpret_cast<const i32x4*>(row + ((c0 ^ x8) * 16));
             const i32x4 up = *reinterpret_cast<const i32x4*>(row + (((c0 + 1) ^ x8) * 16));
@@ -640,8 +649,10 @@ prefill_kernel(PrefillParams p) {
             }
         };
         // P -> bf16 operand and the rounded row sum, spread over the score
-        // products (which do not need them); the PV products come after.
-        static_assert(NQ % NP == 0, "conversions per score product");
+        // products (which do not need them): conversion q follows score
+        // product q NQ / NP (several per product when there are fewer score
+        // products than operands, as with E4M3 scores at D = 64); the PV
+        // products come after.
         bf16x8 pb[KB][2];
         float sr[2] = {0.0f, 0.0f};
         auto convert_p = [&](int q) __attribute__((always_inline)) {
@@ -661,7 +672,9 @@ prefill_kernel(PrefillParams p) {
             if (i < NQ) {
                 const int kb = i % KB, ks = i / KB;
                 s[kb] = score_mfma(kfrag[i], ks, ks == 0 ? zero_f32x16() : s[kb]);
-                if (i % (NQ / NP) == 0) convert_p(i / (NQ / NP));
+#pragma unroll
+                for (int q = 0; q < NP; ++q)
+                    if (q * NQ / NP == i) convert_p(q);
                 if (i == NQ - 1) ell_r += sr[0] + sr[1];
             } else {
                 const int f = i - NQ;
@@ -778,11 +791,16 @@ void launch_prefill_d(bool causal, bool window, const PrefillParams& p, dim3 gri
     else             hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, block, 0, stream, p);
 }
 
-hipError_t launch_prefill_fp8(bool causal, const PrefillParams& p, hipStream_t stream) {
+hipError_t launch_prefill_fp8(int D, bool causal, const PrefillParams& p, hipStream_t stream) {
     const long long total = (long long)p.B * p.Hq * p.n_qblocks;
     const dim3 grid((unsigned)total), block(512);
-    if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, false, true>), grid, block, 0, stream, p);
-    else        hipLaunchKernelGGL((prefill_kernel<128, false, false, true>), grid, block, 0, stream, p);
+    if (D == 64) {
+        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true, false, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<64, false, false, true>), grid, block, 0, stream, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, false, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((prefill_kernel<128, false, false, true>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -245,7 +245,7 @@ int fa_quantize_fp8(const void* x, void* x8, float* scales, int heads, int L, in
  *   q8 : uint8 [B, Hq, Lq, D] codes, with q_scales fp32 [B, Hq, ceil(Lq / 256)]
  *   k8 : uint8 [B, Hkv, Lk, D] codes, with k_scales fp32 [B, Hkv, ceil(Lk / 64)]
  *   v, o, lse, kv_lens, causal, stream: as for fa_fwd (no window)
- * D must be 128 (FA_ERR_UNSUPPORTED otherwise); other errors as for fa_fwd.
+ * D = 64 or 128 (FA_ERR_UNSUPPORTED otherwise); other errors as for fa_fwd.
  */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,
                const float* q_scales, const float* k_scales,

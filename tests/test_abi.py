@@ -229,7 +229,7 @@ def call_fp8(lib, q8=P, k8=P, v=P, o=P, lse=P, qs=P, ks=P, B=1, Hq=2, Hkv=1, Lq=
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=64), binding.FA_ERR_UNSUPPORTED),
+    (dict(D=32), binding.FA_ERR_UNSUPPORTED),
     (dict(D=96), binding.FA_ERR_UNSUPPORTED),
     (dict(qs=None), binding.FA_ERR_INVALID_ARG),
     (dict(ks=None), binding.FA_ERR_INVALID_ARG),

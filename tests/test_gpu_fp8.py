@@ -116,11 +116,11 @@ FWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"_{c[6] is not None}_{c[7]}")
-def test_fp8_forward_matches_oracle(dev, case):
+def test_fp8_forward_matches_oracle(dev, case, D):
     B, Hq, Hkv, Lq, Lk, causal, lens, tr = case
-    D = 128
-    c = W.random_case(1200 + Lq + Lk, B, Hq, Hkv, Lq, Lk, D, causal, lens)
+    c = W.random_case(1200 + Lq + Lk + (D == 64), B, Hq, Hkv, Lq, Lk, D, causal, lens)
     sg = signs_of(11, D) if tr else None
     kl = None if c.kv_lens is None else c.kv_lens.to(dev)
     o, lse = binding.attention_fp8(c.q.to(dev), c.k.to(dev), c.v.to(dev), causal=causal, scale=c.scale,
@@ -129,14 +129,15 @@ def test_fp8_forward_matches_oracle(dev, case):
     ro, rl, *_ = oracle.fp8.fp8_attention_forward(c.q, c.k, c.v, c.scale, causal, c.kv_lens,
                                                   None if sg is None else sg.numpy())
     m = compare(o, lse, ro, rl)
-    print(f"[parity] fp8 {case}: {m}", flush=True)
+    print(f"[parity] fp8 D={D} {case}: {m}", flush=True)
 
 
-def test_fp8_zero_length_and_nan_padding(dev):
+@pytest.mark.parametrize("D", [128, 64])
+def test_fp8_zero_length_and_nan_padding(dev, D):
     # Zero-length sequences give O = 0 and LSE = -inf; NaN in V rows past a
     # sequence's length is never read.  (K is quantized whole, padding rows
     # included, on both sides.)
-    B, H, L, D = 3, 2, 96, 128
+    B, H, L = 3, 2, 96
     c = W.random_case(1300, B, H, H, L, L, D, True, [96, 0, 41])
     v = c.v.clone()
     v[2, :, 41:] = float("nan")
