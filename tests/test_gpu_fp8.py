@@ -198,3 +198,26 @@ def test_fp8_full_size_sampled_rows(dev, name):
         rr = sample_rows(w.Lq, 1500 + b * 16 + h)
         ro, rl = oracle.attention_rows(qv, kv, inp.v[b:b + 1, g:g + 1], eff, True, None, 0, 0, rows=rr)
         compare(o[b, h][rr], lse[b, h][rr], ro, rl)
+
+
+def test_fp8_d64_long_causal_sampled_rows(dev):
+    # D = 64 at a long causal shape (16 query blocks, 64 key tiles per
+    # block at the end): codes of the checked heads bit-exact, sampled rows
+    # (every query block and wavefront slot) against the oracle.
+    B, H, L, D = 2, 4, 4096, 64
+    c = W.random_case(1600, B, H, H, L, L, D, True, None)
+    sg = signs_of(17, D)
+    q8, qs = binding.quantize_fp8(c.q.to(dev), binding.FP8_Q_BLOCK, sg.to(dev))
+    k8, ks = binding.quantize_fp8(c.k.to(dev), binding.FP8_K_BLOCK, sg.to(dev))
+    eff = c.scale / D
+    o, lse = binding.fa_fwd_fp8(q8, k8, c.v.to(dev), qs, ks, causal=True, scale=eff)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    for (b, h) in ((0, 0), (1, 3)):
+        rc, _, qv = oracle.fp8.quantize_rows(c.q[b:b + 1, h:h + 1], binding.FP8_Q_BLOCK, sg.numpy())
+        kc, _, kv = oracle.fp8.quantize_rows(c.k[b:b + 1, h:h + 1], binding.FP8_K_BLOCK, sg.numpy())
+        assert np.array_equal(q8[b, h].cpu().numpy(), rc[0, 0]) and np.array_equal(k8[b, h].cpu().numpy(), kc[0, 0])
+        rr = sample_rows(L, 1610 + b * 8 + h)
+        ro, rl = oracle.attention_rows(qv, kv, c.v[b:b + 1, h:h + 1], eff, True, None, 0, 0, rows=rr)
+        m = compare(o[b, h][rr], lse[b, h][rr], ro, rl)
+        print(f"[parity] fp8 D=64 long causal (b={b}, h={h}): {m}", flush=True)
