@@ -91,8 +91,8 @@ constexpr float kTauSum = 256.0f;
 // spread widely), the workgroup switches, for the rest of its KV loop, to
 // split probabilities: the residual p - bf16(p), itself rounded to bf16, goes
 // through a second product with the same V fragments, so every weight is
-// exact to ~2^-16, and the normaliser adds the residuals' sum to the rounded
-// one.  The switch is one counter in LDS that every wavefront adds to; each
+// exact to ~2^-16, and the tile's normaliser is the fp32 sum of p (which its
+// weights then match to ~2^-18).  The switch is one counter in LDS that every wavefront adds to; each
 // reads it after the prologue's tile and then once per cycle of LDS stages,
 // and moves from the plain tile loop to a split one (whose matrix phase
 // follows every PV product by its residual product on the same fragment), so
@@ -427,7 +427,7 @@ prefill_kernel(PrefillParams p) {
     const float c = p.c;
     float ref = kNegInf;                    // reference r = (running max) * c; -inf while the row is empty
     float ell_e = 0.0f;                     // the row's sum of p (both lanes of the row hold it)
-    float ell_r = 0.0f;                     // this lane's half of the row's sum of bf16(p)
+    float ell_r = 0.0f;                     // this lane's half of the normaliser: sum of bf16(p) (split tiles: of p)
     f32x16 acc[DB];                         // O^T accumulator: rows d, column = this lane's query
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = zero_f32x16();
@@ -435,6 +435,7 @@ prefill_kernel(PrefillParams p) {
     // the matrix phase converts it to the bf16 P^T operand (and sums the
     // rounded values) while its score products run.
     float pe[KB][2][8];
+    bf16x8 pbs[KB][2];                      // split tiles: bf16(p), converted in the vector phase
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     bool split = false;                     // this wavefront splits its probabilities (wave-uniform, sticky)
     float ksc_next = k_scale_of(0);         // FP8: s_k of the tile softmax_tile handles next
@@ -444,20 +445,26 @@ prefill_kernel(PrefillParams p) {
     const float mod_b = MOD == kModSoftcap ? 2.0f * p.scale * 1.4426950408889634f / p.softcap : 0.0f;
 
     // Residuals p - bf16(p) of every 16-key chunk of pe to LDS, for the next
-    // matrix phase's residual products; returns their sum (this lane's half
-    // of the row).  The normaliser takes it with the rounded sum of the matrix
-    // phase: sum_j bf16(p_j) + (p_j - bf16(p_j)) = sum_j p_j.
-    auto write_residuals = [&]() __attribute__((always_inline)) -> float {
+    // matrix phase's residual products.  Inside the split loop the rounded
+    // halves stay in registers (pbs, `keep`) as that phase's P^T operands,
+    // and the tile's normaliser is the fp32 sum of p: its weights
+    // bf16(p) + bf16(p - bf16(p)) are within 2^-18 of p, relative.  A tile
+    // that enters the split loop (the prologue's, or the one after the
+    // switch) keeps the plain tiles' form instead -- its matrix phase converts
+    // P^T and sums the rounded values -- and adds its residuals' sum (`sum`),
+    // so no split operand stays live through the plain loop.
+    auto write_residuals = [&](auto keep, auto sum) __attribute__((always_inline)) -> float {
         float rs[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int cc = 0; cc < NCH; ++cc) {
             const float* e = pe[cc / 2][cc % 2];
             const bf16x8 hi8 = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+            if constexpr (decltype(keep)::value) pbs[cc / 2][cc % 2] = hi8;
             float r8[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 r8[j] = e[j] - (float)hi8[j];
-                rs[j & 1] += r8[j];
+                if constexpr (decltype(sum)::value) rs[j & 1] += r8[j];
             }
             plo_lds[(w * NCH + cc) * 64 + l] = to_bf16x8(r8[0], r8[1], r8[2], r8[3], r8[4], r8[5], r8[6], r8[7]);
         }
@@ -601,8 +608,14 @@ prefill_kernel(PrefillParams p) {
             }
         }
         if constexpr (MODE != 0) {
-            if (MODE == 3) rs_first = write_residuals();
-            else if (MODE == 2 || __builtin_expect(split, 0)) ell_r += write_residuals();
+            if (MODE == 3) {
+                rs_first = write_residuals(Const<false>{}, Const<true>{});
+            } else if (MODE == 2) {
+                write_residuals(Const<true>{}, Const<false>{});
+                ell_r += se_l;              // the split tile's normaliser: the fp32 sum
+            } else if (__builtin_expect(split, 0)) {
+                ell_r += write_residuals(Const<false>{}, Const<true>{});
+            }
         }
         ell_e += row_sum;
     };
@@ -619,9 +632,13 @@ prefill_kernel(PrefillParams p) {
     // product by its residual product, with the same V fragment and the same
     // accumulator (a back-to-back accumulation); the residual operand of a
     // 16-key chunk is read from LDS with the chunk's first V fragment.
-    auto matrix_phase = [&](auto phase, auto spl) __attribute__((always_inline)) {
+    auto matrix_phase = [&](auto phase, auto form) __attribute__((always_inline)) {
         constexpr int PH = decltype(phase)::value;      // t % NB
-        constexpr bool SPL = decltype(spl)::value;
+        // FORM 0: plain; 1: split, P^T converted here from pe with its
+        // rounded sums (the tile entering the split loop); 2: split, P^T
+        // from the vector phase (pbs), normalised by the fp32 sum.
+        constexpr int FORM = decltype(form)::value;
+        constexpr bool SPL = FORM != 0;
         const bf16* Ks = smem + ((PH + 1) % NB) * TILE;
         const bf16* Vs = smem + (NB + PH) * TILE;
         constexpr int NQ = KB * KSQ;        // score products
@@ -658,15 +675,21 @@ prefill_kernel(PrefillParams p) {
         auto convert_p = [&](int q) __attribute__((always_inline)) {
             const int kb = q / 2, half = q % 2;
             const float* e = pe[kb][half];
-            const bf16x8 pv = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-            pb[kb][half] = pv;
+            if constexpr (FORM == 2) {
+                // A split tile's operand was converted in the vector phase,
+                // and its normaliser is its fp32 sum (no rounded sums).
+                pb[kb][half] = pbs[kb][half];
+            } else {
+                const bf16x8 pv = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+                pb[kb][half] = pv;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                sr[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[2 * j], pv[2 * j + 1]}, ones, sr[j & 1], false);
-            // Pin the sums here, between the score products: otherwise the
-            // compiler sinks them (and a second conversion of P) to the end
-            // of the phase.
-            asm volatile("" : "+v"(sr[0]), "+v"(sr[1]));
+                for (int j = 0; j < 4; ++j)
+                    sr[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[2 * j], pv[2 * j + 1]}, ones, sr[j & 1], false);
+                // Pin the sums here, between the score products: otherwise the
+                // compiler sinks them (and a second conversion of P) to the end
+                // of the phase.
+                asm volatile("" : "+v"(sr[0]), "+v"(sr[1]));
+            }
         };
         auto mfma_op = [&](int i) __attribute__((always_inline)) {
             if (i < NQ) {
@@ -675,7 +698,7 @@ prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int q = 0; q < NP; ++q)
                     if (q * NQ / NP == i) convert_p(q);
-                if (i == NQ - 1) ell_r += sr[0] + sr[1];
+                if (FORM != 2 && i == NQ - 1) ell_r += sr[0] + sr[1];
             } else {
                 const int f = i - NQ;
                 const int db = f % DB, kb = (f / DB) / 2, half = (f / DB) % 2;
@@ -718,7 +741,7 @@ prefill_kernel(PrefillParams p) {
     // One tile: matrix phase M(t), barrier, vector phase V(t), barrier.
     // PH = t % NB is a compile-time constant, so every LDS offset is one.
     // MODE as in softmax_tile; the matrix phase takes the split form in mode 2.
-    auto tile_step = [&](int t, auto phase, auto mode) __attribute__((always_inline)) {
+    auto tile_step = [&](int t, auto phase, auto mode, auto form) __attribute__((always_inline)) {
         // ---- matrix phase M(t) ----
         __builtin_amdgcn_s_setprio(1);
         copy_k(t + NB);                     // into the buffer of K(t)
@@ -726,7 +749,7 @@ prefill_kernel(PrefillParams p) {
         // The score product runs for the last tile too (on the zero-filled
         // buffer past the end; the result is not used), which keeps the
         // phase one basic block.
-        matrix_phase(phase, Const<decltype(mode)::value == 2>{});
+        matrix_phase(phase, form);
         __builtin_amdgcn_s_setprio(0);
         wait_vector_loads_until<NIK + NI>();   // the copies of M(t-1) have landed
         __syncthreads();
@@ -744,20 +767,29 @@ prefill_kernel(PrefillParams p) {
         split = __builtin_amdgcn_readfirstlane(split_rows) >= kSplitRows;
         ell_r += split ? rs_first : 0.0f;
         if (!split) for (; t < ntiles; t += NB) {
-            tile_step(t, Const<0>{}, Const<0>{});
-            if (t + 1 < ntiles) tile_step(t + 1, Const<1>{}, Const<0>{});
-            if (t + 2 < ntiles) tile_step(t + 2, Const<2>{}, Const<1>{});
+            tile_step(t, Const<0>{}, Const<0>{}, Const<0>{});
+            if (t + 1 < ntiles) tile_step(t + 1, Const<1>{}, Const<0>{}, Const<0>{});
+            if (t + 2 < ntiles) tile_step(t + 2, Const<2>{}, Const<1>{}, Const<0>{});
             if (__builtin_expect(split, 0)) {
                 t += NB;
                 break;
             }
         }
+        // The split loop's first stage cycle: its first matrix phase converts
+        // the entering tile's P^T itself (form 1); later ones take the vector
+        // phase's operands (form 2).
+        if (t < ntiles) {
+            tile_step(t, Const<0>{}, Const<2>{}, Const<1>{});
+            if (t + 1 < ntiles) tile_step(t + 1, Const<1>{}, Const<2>{}, Const<2>{});
+            if (t + 2 < ntiles) tile_step(t + 2, Const<2>{}, Const<2>{}, Const<2>{});
+            t += NB;
+        }
     }
     for (; t < ntiles; t += NB) {
         constexpr int M = CORR ? 2 : 0;
-        tile_step(t, Const<0>{}, Const<M>{});
-        if (t + 1 < ntiles) tile_step(t + 1, Const<1>{}, Const<M>{});
-        if (t + 2 < ntiles) tile_step(t + 2, Const<2>{}, Const<M>{});
+        tile_step(t, Const<0>{}, Const<M>{}, Const<M>{});
+        if (t + 1 < ntiles) tile_step(t + 1, Const<1>{}, Const<M>{}, Const<M>{});
+        if (t + 2 < ntiles) tile_step(t + 2, Const<2>{}, Const<M>{}, Const<M>{});
     }
     if (grp == 0) __syncthreads();          // match the second group's extra barrier
     wait_all_vector_loads();                // copies past the last tile (zero-range) drained
