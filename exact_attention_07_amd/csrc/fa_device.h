@@ -110,6 +110,7 @@ __device__ __forceinline__ void load16_to_lds(rsrc_t r, uint32_t byte_offset, bf
 // Buffer descriptor as four scalar dwords, for the inline-assembly copy below:
 // base address (wave-uniform), stride 0, range in bytes, raw-buffer format.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes) {
     const uint64_t a = (uint64_t)(uintptr_t)base;
     i32x4 d;

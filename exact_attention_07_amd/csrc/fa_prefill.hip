@@ -798,8 +798,18 @@ prefill_kernel(PrefillParams p) {
     const float le = ell_e;
     const float lr = sum_with_partner(ell_r);
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-    if (qrow < Lq) {
-        bf16* Op = p.o + qoff + (size_t)qrow * D;
+    // O goes out through LDS so that each store instruction writes whole rows:
+    // a lane's accumulator holds 8-byte pieces of its row spread over the
+    // row, so direct stores would touch 32 rows per instruction.  Each
+    // wavefront stages its 32 rows (row-major, 16-byte chunks XOR-swizzled by
+    // the row so the 32 rows of one write hit distinct banks) in the now idle
+    // K/V buffers, then stores 64 / (D / 8) full rows per instruction through
+    // a descriptor over its valid rows.
+    __syncthreads();                        // every wavefront's copies into the buffers have landed
+    constexpr int CPR = D / 8;              // 16-byte chunks per row of O
+    bf16* ost = smem + w * 32 * D;
+    {
+        const int r = l & 31;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -807,12 +817,26 @@ prefill_kernel(PrefillParams p) {
                 bf16x4 ov;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) ov[j] = (bf16)(acc[db][4 * gq + j] * inv);
-                *reinterpret_cast<bf16x4*>(Op + db * 32 + 8 * gq + 4 * hi) = ov;
+                const int chunk = (4 * db + gq) ^ (r & (CPR - 1));
+                *reinterpret_cast<bf16x4*>(ost + r * D + chunk * 8 + 4 * hi) = ov;
             }
-        if (p.lse && hi == 0)
-            p.lse[lse_off + qrow] =
-                le > 0.0f ? (ref + log2_fast(le)) * kLn2 : kNegInf;
     }
+    __syncthreads();
+    {
+        constexpr int RPI = 64 / CPR;       // rows per store instruction
+        const int cl = l % CPR, rl = l / CPR;
+        const int vrows = min(max(Lq - qw0, 0), 32);
+        const rsrc_t obuf = make_rsrc(p.o + qoff + (size_t)min(qw0, Lq) * D, (uint32_t)vrows * D * 2);
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int r = i * RPI + rl;
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(ost + r * D + ((cl ^ (r & (CPR - 1))) * 8));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), obuf,
+                                                   (uint32_t)(r * D + cl * 8) * 2, 0, 0);
+        }
+    }
+    if (p.lse && hi == 0 && qrow < Lq)
+        p.lse[lse_off + qrow] = le > 0.0f ? (ref + log2_fast(le)) * kLn2 : kNegInf;
 }
 
 template <int D>
