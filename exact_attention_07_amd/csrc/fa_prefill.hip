@@ -518,14 +518,20 @@ prefill_kernel(PrefillParams p) {
         const bool need = (k0 + BN > n) || (CAUSAL && (k0 + BN - 1 > qw0 + off)) ||
                           (WINDOW && (qw0 + 31 + off - k0 >= p.window));
         if (need) {
+            // Element (kb, v) holds key base + idx with idx a compile-time
+            // constant, so every condition is one compare of idx against a
+            // per-lane limit: key < n and (causal) key <= qpos give
+            // idx <= lim; (window) qpos - key < w gives idx >= lo.
             const int qpos = qrow + off;
+            const int base = k0 + 8 * hi;
+            const int lim = CAUSAL ? min(n - 1, qpos) - base : n - 1 - base;
+            const int lo = WINDOW ? qpos - p.window + 1 - base : 0;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int key = k0 + kb * 32 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                    const bool ok = (key < n) & (!CAUSAL | (key <= qpos)) &
-                                    (!WINDOW | (qpos - key < p.window));
+                    const int idx = kb * 32 + 16 * (v >> 3) + (v & 7);
+                    const bool ok = WINDOW ? (idx <= lim) & (idx >= lo) : idx <= lim;
                     s[kb][v] = ok ? s[kb][v] : kNegInf;   // a select, no branch
                 }
         }
@@ -539,7 +545,6 @@ prefill_kernel(PrefillParams p) {
             // Folded ALiBi: s ct - r - a ct sgn (base - K_v) = fma(s, ct, fma(c1, K_v, b0)).
             const float c1 = folded ? (float)sgn * mod_a * ct : 0.0f;
             const float b0 = folded ? __builtin_fmaf(-c1, base, -r) : -r;
-            se[0] = se[1] = se[2] = se[3] = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -549,7 +554,10 @@ prefill_kernel(PrefillParams p) {
                         const float kv = (float)(kb * 32 + 16 * half + j);
                         const float t = (MOD == kModAlibi) ? __builtin_fmaf(c1, kv, b0) : -r;
                         pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], ct, t));
-                        se[j & 3] += pe[kb][half][j];
+                        // The first four terms start the partial sums (p >= 0, so
+                        // 0 + p would be p: no add needed).
+                        if (kb == 0 && half == 0 && j < 4) se[j] = pe[kb][half][j];
+                        else se[j & 3] += pe[kb][half][j];
                     }
         };
         exponentials();
