@@ -172,6 +172,7 @@ prefill_kernel(PrefillParams p) {
     // a wavefront's vector phase and read in its next matrix phase.
     constexpr int NCH = KB * 2;                     // 16-key chunks per tile
     __shared__ __attribute__((aligned(16))) bf16x8 plo_lds[D == 128 ? NW * NCH * 64 : 1];
+    __shared__ __attribute__((aligned(16))) bf16 qst[(!FP8 && D == 64) ? 256 * 64 : 8];   // Q staging at D = 64
     __shared__ int split_rows;              // rows of the workgroup found dominated by a few keys
 
     const int tid = threadIdx.x;
@@ -319,12 +320,39 @@ prefill_kernel(PrefillParams p) {
             const i32x4 up = __builtin_bit_cast(i32x4, load16(qbuf, at + 16));
             qf[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
         }
-    } else {
-        const rsrc_t qbuf = make_rsrc(p.q + qoff, (uint32_t)Lq * D * 2);   // rows >= Lq read as zero
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[ks] = load16(qbuf, (uint32_t)(qrow * D + ks * 16 + hi * 8) * 2);
     }
+    // bf16 kernels: each wavefront copies its 32 rows of Q straight into LDS
+    // as whole rows (1 KB of consecutive rows per copy instruction; rows past
+    // Lq arrive as zeros), 16-byte chunks XOR-swizzled by the row so the
+    // fragment reads below hit distinct banks, and reads its B-operand
+    // fragments back once they have landed (wavefront-local, in the
+    // prologue).  Staging: at D = 128 the residual buffer (wavefronts 0-3)
+    // and V buffers 1-2 (wavefronts 4-7; V(1) is copied after the prologue's
+    // barrier), at D = 64 a buffer of its own.
+    constexpr int NQC = 32 * D * 2 / 1024;  // copies per lane
+    bf16* qs_w = D == 128 ? (w < 4 ? reinterpret_cast<bf16*>(plo_lds) + w * 32 * D
+                                   : smem + (NB + 1) * TILE + (w - 4) * 32 * D)
+                          : qst + w * 32 * D;
+    auto q_swz = [](int row) { return row & (CH - 1); };
+    if constexpr (!FP8) {
+        const int vq = min(max(Lq - qw0, 0), 32);
+        const i32x4 qd = make_desc(p.q + qoff + (size_t)min(qw0, Lq) * D, (uint32_t)vq * D * 2);
+        const uint32_t qs_addr = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)qs_w);
+#pragma unroll
+        for (int i = 0; i < NQC; ++i) {
+            const int P = i * 64 + l;
+            const int row = P / CH;
+            copy16_to_lds_async(qd, (uint32_t)(row * D + ((P % CH) ^ q_swz(row)) * 8) * 2, qs_addr + i * 1024);
+        }
+    }
+    auto read_q = [&]() __attribute__((always_inline)) {
+        if constexpr (!FP8) {
+            const int row = l & 31;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ks] = *reinterpret_cast<const bf16x8*>(qs_w + row * D + (((2 * ks + hi) ^ q_swz(row)) * 8));
+        }
+    };
     // FP8: exponent scale of tile t = c s_q s_k(t); s_k is read one tile ahead.
     const float cq = FP8 ? p.c * p.q_scale[(size_t)(b * p.Hq + h) * p.n_qblocks + qblk] : p.c;
     const int nks = (p.Lk + kFp8KBlock - 1) / kFp8KBlock;
@@ -731,15 +759,22 @@ prefill_kernel(PrefillParams p) {
     };
 
     // ---- prologue: K(0..2), V(0..1) resident; S(0) -> P(0) -------------------
+    // V(1) waits for the prologue's barrier where its buffer stages Q.
+    constexpr bool LATE_V1 = !FP8 && D == 128;
     copy_k(0);
     copy_k(1);
     copy_v(0);
     copy_k(2);
-    copy_v(1);
-    // Q and K(0) only: the other four tiles stream in while S(0) and P(0) are
-    // computed (vmcnt counts in issue order).
-    wait_vector_loads_until<2 * NIK + 2 * NI>();
-    __syncthreads();
+    if (!LATE_V1) copy_v(1);
+    // Q and K(0) only: the other tiles stream in while S(0) and P(0) are
+    // computed (vmcnt counts in issue order, the Q copies first).
+    wait_vector_loads_until<2 * NIK + (LATE_V1 ? 1 : 2) * NI>();
+    if constexpr (!FP8) {
+        asm volatile("" ::: "memory");      // the staged rows are read only after the wait
+        read_q();
+    }
+    __syncthreads();                        // K(0) visible; every wavefront's Q read from its staging
+    if (LATE_V1) copy_v(1);
     score_tile(0);
     softmax_tile(0, Const<3>{});
     wait_vector_loads_until<NIK + NI>();    // K(1) and V(0), the first matrix phase's operands
@@ -832,7 +867,11 @@ prefill_kernel(PrefillParams p) {
     __syncthreads();
     {
         constexpr int RPI = 64 / CPR;       // rows per store instruction
-        const int cl = l % CPR, rl = l / CPR;
+        // The offsets below equal those of the Q copies; a fresh lane index
+        // keeps the compiler from holding those through the tile loop.
+        int lane = l;
+        asm volatile("" : "+v"(lane));
+        const int cl = lane % CPR, rl = lane / CPR;
         const int vrows = min(max(Lq - qw0, 0), 32);
         const rsrc_t obuf = make_rsrc(p.o + qoff + (size_t)min(qw0, Lq) * D, (uint32_t)vrows * D * 2);
 #pragma unroll
