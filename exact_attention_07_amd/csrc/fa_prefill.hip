@@ -333,7 +333,11 @@ prefill_kernel(PrefillParams p) {
     bf16* qs_w = D == 128 ? (w < 4 ? reinterpret_cast<bf16*>(plo_lds) + w * 32 * D
                                    : smem + (NB + 1) * TILE + (w - 4) * 32 * D)
                           : qst + w * 32 * D;
-    auto q_swz = [](int row) { return row & (CH - 1); };
+    // Chunk swizzle of a staged row: with 256-byte rows (D = 128) the row's
+    // low bits; with 128-byte rows two rows share the 64 banks, so bits 1-3.
+    // The 16 rows of one 16-lane group of a fragment read then hit 16
+    // distinct 16-byte bank groups.
+    auto q_swz = [](int row) { return D == 128 ? row & 15 : (row >> 1) & 7; };
     if constexpr (!FP8) {
         const int vq = min(max(Lq - qw0, 0), 32);
         const i32x4 qd = make_desc(p.q + qoff + (size_t)min(qw0, Lq) * D, (uint32_t)vq * D * 2);
@@ -844,10 +848,12 @@ prefill_kernel(PrefillParams p) {
     // O goes out through LDS so that each store instruction writes whole rows:
     // a lane's accumulator holds 8-byte pieces of its row spread over the
     // row, so direct stores would touch 32 rows per instruction.  Each
-    // wavefront stages its 32 rows (row-major, 16-byte chunks XOR-swizzled by
-    // the row so the 32 rows of one write hit distinct banks) in the now idle
-    // K/V buffers, then stores 64 / (D / 8) full rows per instruction through
-    // a descriptor over its valid rows.
+    // wavefront stages its 32 rows in the now idle K/V buffers, row-major with
+    // 16-byte chunks XOR-swizzled by the row (q_swz) and, for rows 16-31, the
+    // two 8-byte halves of a chunk swapped, so the 32 lanes of one half of a
+    // write (one 8-byte piece of each of 32 rows) hit 64 distinct banks.  It
+    // then stores 64 / (D / 8) full rows per instruction through a descriptor
+    // over its valid rows (the halves swapped back in registers).
     __syncthreads();                        // every wavefront's copies into the buffers have landed
     constexpr int CPR = D / 8;              // 16-byte chunks per row of O
     bf16* ost = smem + w * 32 * D;
@@ -860,8 +866,8 @@ prefill_kernel(PrefillParams p) {
                 bf16x4 ov;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) ov[j] = (bf16)(acc[db][4 * gq + j] * inv);
-                const int chunk = (4 * db + gq) ^ (r & (CPR - 1));
-                *reinterpret_cast<bf16x4*>(ost + r * D + chunk * 8 + 4 * hi) = ov;
+                const int chunk = (4 * db + gq) ^ q_swz(r);
+                *reinterpret_cast<bf16x4*>(ost + r * D + chunk * 8 + 4 * (hi ^ (r >> 4))) = ov;
             }
     }
     __syncthreads();
@@ -876,8 +882,9 @@ prefill_kernel(PrefillParams p) {
         const rsrc_t obuf = make_rsrc(p.o + qoff + (size_t)min(qw0, Lq) * D, (uint32_t)vrows * D * 2);
 #pragma unroll
         for (int i = 0; i < 32 / RPI; ++i) {
-            const int r = i * RPI + rl;
-            const bf16x8 v = *reinterpret_cast<const bf16x8*>(ost + r * D + ((cl ^ (r & (CPR - 1))) * 8));
+            const int r = i * RPI + rl;     // rows of instruction i all below 16 or all from 16
+            bf16x8 v = *reinterpret_cast<const bf16x8*>(ost + r * D + ((cl ^ q_swz(r)) * 8));
+            if (i * RPI >= 16) v = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), obuf,
                                                    (uint32_t)(r * D + cl * 8) * 2, 0, 0);
         }
