@@ -536,14 +536,16 @@ prefill_kernel(PrefillParams p) {
         if constexpr (MOD == kModAlibi) {
             if (sgn == 0) add_alibi();
         } else if constexpr (MOD == kModSoftcap) {
+            // s becomes u = 1 / (1 + 2^(s mod_b)); the capped score is
+            // mod_a (1 - 2u), whose last fma merges into the exponent's.
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float e = exp2_fast(s[kb][v] * mod_b);
-                    s[kb][v] = __builtin_fmaf(-2.0f * mod_a, __builtin_amdgcn_rcpf(1.0f + e), mod_a);
-                }
+                for (int v = 0; v < 16; ++v)
+                    s[kb][v] = __builtin_amdgcn_rcpf(1.0f + exp2_fast(s[kb][v] * mod_b));
         }
+        // A masked element's value: -inf, or for the cap u = +inf (capped score -inf).
+        constexpr float kMasked = MOD == kModSoftcap ? kPosInf : kNegInf;
         // Elementwise masks only where some pair of this wavefront's rows and
         // the tile is out: past n, above the diagonal, or (window) at least w
         // positions before the wavefront's last row.
@@ -564,7 +566,7 @@ prefill_kernel(PrefillParams p) {
                 for (int v = 0; v < 16; ++v) {
                     const int idx = kb * 32 + 16 * (v >> 3) + (v & 7);
                     const bool ok = WINDOW ? (idx <= lim) & (idx >= lo) : idx <= lim;
-                    s[kb][v] = ok ? s[kb][v] : kNegInf;   // a select, no branch
+                    s[kb][v] = ok ? s[kb][v] : kMasked;   // a select, no branch
                 }
         }
         // p = 2^(s c - r), the tile's sums and P -> bf16, against the current
@@ -577,6 +579,9 @@ prefill_kernel(PrefillParams p) {
             // Folded ALiBi: s ct - r - a ct sgn (base - K_v) = fma(s, ct, fma(c1, K_v, b0)).
             const float c1 = folded ? (float)sgn * mod_a * ct : 0.0f;
             const float b0 = folded ? __builtin_fmaf(-c1, base, -r) : -r;
+            // Soft-cap: mod_a (1 - 2u) ct - r = fma(u, -2 mod_a ct, mod_a ct - r).
+            const float sa = MOD == kModSoftcap ? -2.0f * mod_a * ct : ct;
+            const float sb = MOD == kModSoftcap ? __builtin_fmaf(mod_a, ct, -r) : b0;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -584,8 +589,8 @@ prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const float kv = (float)(kb * 32 + 16 * half + j);
-                        const float t = (MOD == kModAlibi) ? __builtin_fmaf(c1, kv, b0) : -r;
-                        pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], ct, t));
+                        const float t = (MOD == kModAlibi) ? __builtin_fmaf(c1, kv, b0) : sb;
+                        pe[kb][half][j] = exp2_fast(__builtin_fmaf(s[kb][8 * half + j], sa, t));
                         // The first four terms start the partial sums (p >= 0, so
                         // 0 + p would be p: no add needed).
                         if (kb == 0 && half == 0 && j < 4) se[j] = pe[kb][half][j];
@@ -611,13 +616,26 @@ prefill_kernel(PrefillParams p) {
                 if (folded) add_alibi();
                 folded = false;
             }
-            float m8[8];
+            float mx;
+            if constexpr (MOD == kModSoftcap) {
+                // The capped score falls as u rises: its max is at the least u
+                // (+inf, a row with no valid key so far, gives -inf).
+                float m8[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(s[0][j], s[0][j + 8]), fmaxf(s[1][j], s[1][j + 8]));
+                for (int j = 0; j < 8; ++j) m8[j] = fminf(fminf(s[0][j], s[0][j + 8]), fminf(s[1][j], s[1][j + 8]));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
-            float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
-            mx = max_with_partner(mx);
+                for (int j = 0; j < 4; ++j) m8[j] = fminf(m8[j], m8[j + 4]);
+                const float umin = -max_with_partner(-fminf(fminf(m8[0], m8[1]), fminf(m8[2], m8[3])));
+                mx = __builtin_fmaf(-2.0f * mod_a, umin, mod_a);
+            } else {
+                float m8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m8[j] = fmaxf(fmaxf(s[0][j], s[0][j + 8]), fmaxf(s[1][j], s[1][j + 8]));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m8[j] = fmaxf(m8[j], m8[j + 4]);
+                mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+                mx = max_with_partner(mx);
+            }
             const bool shift = move && mx != kNegInf;   // a row with no valid key so far keeps -inf
             const float r_new = shift ? mx * ct + kTau : ref;  // kTau of headroom above the max
             const float alpha = shift ? exp2_fast(ref - r_new) : 1.0f;   // 0 from an empty row
