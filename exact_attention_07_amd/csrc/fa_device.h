@@ -23,7 +23,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kPosInf = __builtin_inff();
 constexpr float kLn2 = 0.693147180559945309417232121458176568f;
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {

@@ -133,6 +133,7 @@ struct ScoreOperand<true> { typedef i32x8 type; };
 // (an exponential and a reciprocal per score; 2^(large) = inf gives 1, and
 // 2^(-large) = 0 gives -1).
 constexpr int kModNone = 0, kModAlibi = 1, kModSoftcap = 2;
+constexpr float kPosInf = __builtin_inff();
 
 template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false, int MOD = kModNone, bool VARLEN = false>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
