@@ -120,6 +120,17 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
 
+// Queries base + idx that key `key` may pair with, as a range of idx:
+// i < Lq; (causal) key <= i + off; (window) i + off - key < w; none when the
+// key is past n.
+__device__ __forceinline__ void query_range(int base, int key, int n, int off, const BwdParams& p,
+                                            int& lo, int& hi_lim) {
+    lo = p.causal ? key - off - base : INT_MIN;
+    hi_lim = p.Lq - 1 - base;
+    if (p.window > 0) hi_lim = min(hi_lim, key + p.window - 1 - off - base);
+    if (key >= n) hi_lim = -1;
+}
+
 // A-operand fragment: row `row` of a swizzled tile, 16-byte chunk `chunk`.
 template <int D>
 __device__ __forceinline__ bf16x8 read_row_chunk(const bf16* tile, int row, int chunk) {
@@ -290,12 +301,24 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(s[v], c2, -lse2);
         if (need) {
+            // Element v holds key base + idx with idx a compile-time constant:
+            // key < n and (causal) key <= qpos give idx <= lim, (window)
+            // qpos - key < w gives idx >= lo; a row past Lq has lim = -1.
+            const int base = k0 + 8 * hi;
+            const int lim = row_ok ? (p.causal ? min(n - 1, qpos) : n - 1) - base : -1;
+            if (p.window > 0) {
+                const int lo = qpos - p.window + 1 - base;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = k0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                const bool ok = row_ok & (key < n) & (!p.causal | (key <= qpos)) &
-                                ((p.window == 0) | (qpos - key < p.window));
-                x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+                for (int v = 0; v < 16; ++v) {
+                    const int idx = 16 * (v >> 3) + (v & 7);
+                    x[v] = (idx <= lim) & (idx >= lo) ? x[v] : kNegInf;   // 2^-inf = 0
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int idx = 16 * (v >> 3) + (v & 7);
+                    x[v] = idx <= lim ? x[v] : kNegInf;
+                }
             }
         }
         float ds[16];
@@ -497,13 +520,14 @@ bwd_dkdv_kernel(BwdParams p) {
                     }
                 }
             if (need) {
+                // Element v holds query base + idx (idx a compile-time
+                // constant): one range [lo, hi_lim] of idx per lane.
+                int lo, hi_lim;
+                query_range(q0 + 8 * hi, key, n, off, p, lo, hi_lim);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                    const int qpos = i + off;
-                    const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
-                                    ((p.window == 0) | (qpos - key < p.window));
-                    x[v] = ok ? x[v] : kNegInf;   // 2^-inf = 0
+                    const int idx = 16 * (v >> 3) + (v & 7);
+                    x[v] = (idx >= lo) & (idx <= hi_lim) ? x[v] : kNegInf;   // 2^-inf = 0
                 }
             }
             float pr[16];
@@ -711,13 +735,12 @@ bwd_dkdv_split_kernel(BwdParams p) {
         const bool need = (q0 + 32 > p.Lq) || (k0 + 32 > n) || (p.causal && k0 + 31 > q0 + off) ||
                           (p.window > 0 && q0 + 31 + off - k0 >= p.window);
         if (need) {
+            int lo, hi_lim;                     // as in the D = 64 kernel
+            query_range(q0 + 8 * hi, key, n, off, p, lo, hi_lim);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int i = q0 + 16 * (v >> 3) + 8 * hi + (v & 7);
-                const int qpos = i + off;
-                const bool ok = (i < p.Lq) & (key < n) & (!p.causal | (key <= qpos)) &
-                                ((p.window == 0) | (qpos - key < p.window));
-                pr[v] = ok ? pr[v] : kNegInf;   // 2^-inf = 0
+                const int idx = 16 * (v >> 3) + (v & 7);
+                pr[v] = (idx >= lo) & (idx <= hi_lim) ? pr[v] : kNegInf;   // 2^-inf = 0
             }
         }
 #pragma unroll
