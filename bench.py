@@ -13,7 +13,8 @@ workload served from a shuffled paged cache with 16-token pages; the
 backward of the causal 4K and 1K prefill workloads, one fa_bwd call per
 step; the causal 4K and GQA 16K forward with FP8 scores, one fa_fwd_fp8 call
 per step on Q and K quantized beforehand, the quantization timed separately
-and added for the end-to-end figure; the causal 4K forward with ALiBi biases
+and added for the end-to-end figure, and the other end-to-end form timed
+too: K quantized, then fa_fwd_fp8_q quantizing Q inside the forward; the causal 4K forward with ALiBi biases
 and the 1K prefill with soft-capped scores, one fa_fwd_mod call per step;
 the causal GQA forward over 16 packed sequences of 128-8192 tokens, one
 fa_fwd_varlen call per step with the longest-tile-first schedule computed
@@ -191,6 +192,14 @@ def time_workload(w, steps, warmup, dev, trials=True, warm_ms=0.0):
         def quantize():                     # one ctypes call each, arguments marshalled once
             lib.fa_quantize_fp8(*qargs)
             lib.fa_quantize_fp8(*kargs)
+
+        # The other end-to-end form: K quantized, Q quantized inside the
+        # forward (fa_fwd_fp8_q, bit for bit the same result).
+        fused_q = binding.PreparedFp8QCall(q, k8, v, ks, sg, causal=w.causal, scale=w.scale / w.D, kv_lens=kl)
+
+        def quantize_k_fused():
+            lib.fa_quantize_fp8(*kargs)
+            fused_q()
     elif w.page_size:
         # Only the paged copy of K and V is resident for a paged workload.
         kc, vc, table = (t.to(dev) for t in inp.meta["paged"])
@@ -239,6 +248,14 @@ def time_workload(w, steps, warmup, dev, trials=True, warm_ms=0.0):
         e2e = ms + rec["quantize_ms"]
         rec["end_to_end_ms"] = e2e
         rec["end_to_end_tflops"] = flops / (e2e * 1e-3) / 1e12
+        quantize_k_fused()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            quantize_k_fused()
+        end.record()
+        torch.cuda.synchronize()
+        rec["fused_q_end_to_end_ms"] = start.elapsed_time(end) / steps
     else:
         rec.update(bound="mfma", frac=rec["tflops"] / PEAK_BF16_TFLOPS)
     if w.varlen is not None:
@@ -423,6 +440,8 @@ def main():
                   + (f" (trials: median {tr['median_ms'] * 1e3:.1f}, min {tr['min_ms'] * 1e3:.1f} us)" if tr else "")
                   + f", {r['tflops']:.1f} TFLOP/s, {r['gbs']:.0f} GB/s, {100 * r['frac']:.1f}% of peak"
                   + (f", quantizing Q and K {r['quantize_ms'] * 1e3:.1f} us" if "quantize_ms" in r else "")
+                  + (f", K quantized and Q in the kernel (fa_fwd_fp8_q) {r['fused_q_end_to_end_ms'] * 1e3:.1f} us"
+                     if "fused_q_end_to_end_ms" in r else "")
                   + (f", schedule {r['schedule_ms'] * 1e3:.1f} us" if "schedule_ms" in r else "")
                   + (f", unsorted order median {r['unsorted_trials']['median_ms'] * 1e3:.1f} us"
                      if "unsorted_trials" in r else ""), flush=True)

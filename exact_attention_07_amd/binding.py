@@ -22,7 +22,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 # Every entry point declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_fwd_splits", "fa_fwd_noalloc", "fa_noalloc_scratch_bytes",
             "fa_fwd_window", "fa_fwd_paged", "fa_bwd",
-            "fa_fwd_mod", "fa_quantize_fp8", "fa_fwd_fp8",
+            "fa_fwd_mod", "fa_quantize_fp8", "fa_fwd_fp8", "fa_fwd_fp8_q",
             "fa_fwd_varlen", "fa_varlen_schedule", "fa_varlen_schedule_ints",
             "fa_workspace_bytes", "fa_status_string", "fa_last_error")
 
@@ -78,6 +78,9 @@ def load_library(path: Optional[str] = None):
     # q8, k8, v, o, lse, q_scales, k_scales, B, Hq, Hkv, Lq, Lk, D, causal, scale, kv_lens, stream
     lib.fa_fwd_fp8.argtypes = [vp] * 7 + [i32] * 7 + [f32, vp, vp]
     lib.fa_fwd_fp8.restype = i32
+    # q, signs, k8, v, o, lse, k_scales, B, Hq, Hkv, Lq, Lk, D, causal, scale, kv_lens, stream
+    lib.fa_fwd_fp8_q.argtypes = [vp] * 7 + [i32] * 7 + [f32, vp, vp]
+    lib.fa_fwd_fp8_q.restype = i32
     # q, k, v, o, lse, cu_q, cu_k, schedule, B, Hq, Hkv, total_q, total_k, D, causal, scale, stream
     lib.fa_fwd_varlen.argtypes = [vp] * 8 + [i32] * 7 + [f32, vp]
     lib.fa_fwd_varlen.restype = i32
@@ -427,6 +430,69 @@ class PreparedFp8Call:
         self._keep = (q8, k8, v, q_scales, k_scales, kv_lens)
         self._fn = load_library().fa_fwd_fp8
         self._args = (_ptr(q8), _ptr(k8), _ptr(v), _ptr(o), _ptr(lse), _ptr(q_scales), _ptr(k_scales),
+                      B, Hq, Hkv, Lq, Lk, D, int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), s)
+        self()
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != FA_OK:
+            _check(status)
+        return self.o, self.lse
+
+
+def _prepare_fp8_q(q, k8, v, k_scales, signs, o, lse, kv_lens, want_lse):
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous 4-D bfloat16 GPU tensor [B, Hq, Lq, D]")
+    if k8.dtype != torch.uint8 or k8.dim() != 4 or not k8.is_contiguous() or k8.device != q.device:
+        raise ValueError("k8 must be a contiguous 4-D uint8 device tensor of E4M3 codes")
+    if v.dtype != torch.bfloat16 or not v.is_contiguous() or v.device != q.device:
+        raise ValueError("v must be a contiguous bf16 device tensor")
+    B, Hq, Lq, D = q.shape
+    _, Hkv, Lk, _ = k8.shape
+    if tuple(v.shape) != tuple(k8.shape) or k8.shape[0] != B or k8.shape[3] != D:
+        raise ValueError("k8 and v must be [B, Hkv, Lk, D] with the batch and D of q")
+    shape = (B, Hkv, -(-Lk // FP8_K_BLOCK))
+    if (k_scales.dtype != torch.float32 or tuple(k_scales.shape) != shape or not k_scales.is_contiguous()
+            or k_scales.device != q.device):
+        raise ValueError(f"k_scales must be a contiguous fp32 device tensor of shape {shape}")
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != D
+                              or signs.device != q.device or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous fp32 device tensor of D entries")
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.device != q.device):
+        raise ValueError("kv_lens must be an int32 device tensor")
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device=q.device)
+    return o, lse, (B, Hq, Hkv, Lq, Lk, D)
+
+
+def fa_fwd_fp8_q(q, k8, v, k_scales, signs=None, o=None, lse=None, *, causal=False, scale=None,
+                 kv_lens=None, stream=None, want_lse=True):
+    """Attention with FP8 scores and Q quantized in the kernel through
+    ``fa_fwd_fp8_q``: q is bf16; k8 and k_scales come from ``quantize_fp8``
+    with 64-row blocks and the same ``signs``.  Equal bit for bit to
+    ``quantize_fp8(q, 256, signs)`` followed by ``fa_fwd_fp8``.  Returns (o, lse)."""
+    o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare_fp8_q(q, k8, v, k_scales, signs, o, lse, kv_lens, want_lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    _check(load_library().fa_fwd_fp8_q(_ptr(q), _ptr(signs), _ptr(k8), _ptr(v), _ptr(o), _ptr(lse),
+                                        _ptr(k_scales), B, Hq, Hkv, Lq, Lk, D, int(bool(causal)), scale,
+                                        _ptr(kv_lens), s))
+    return o, lse
+
+
+class PreparedFp8QCall:
+    """fa_fwd_fp8_q with its arguments checked and marshalled once (see PreparedCall)."""
+
+    def __init__(self, q, k8, v, k_scales, signs=None, *, causal=False, scale=None, kv_lens=None,
+                 stream=None):
+        o, lse, (B, Hq, Hkv, Lq, Lk, D) = _prepare_fp8_q(q, k8, v, k_scales, signs, None, None, kv_lens, True)
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        self.o, self.lse = o, lse
+        self._keep = (q, k8, v, k_scales, signs, kv_lens)
+        self._fn = load_library().fa_fwd_fp8_q
+        self._args = (_ptr(q), _ptr(signs), _ptr(k8), _ptr(v), _ptr(o), _ptr(lse), _ptr(k_scales),
                       B, Hq, Hkv, Lq, Lk, D, int(bool(causal)), ctypes.c_float(scale), _ptr(kv_lens), s)
         self()
 

@@ -546,6 +546,41 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
     return FA_OK;
 }
 
+int fa_fwd_fp8_q(const void* q, const float* signs, const void* k8, const void* v, void* o, float* lse,
+                 const float* k_scales, int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
+                 const int* kv_lens, void* stream) {
+    g_last_error[0] = '\0';
+    const Shape s{B, Hq, Hkv, Lq, Lk, D};
+    int st = validate(q, k8, v, o, lse, s, causal, scale, kv_lens);
+    if (st != FA_OK) return st;
+    if (Lk > 0 && !k_scales) return fail(FA_ERR_INVALID_ARG, "k_scales must not be NULL");
+    if (!aligned(k_scales, 4)) return fail(FA_ERR_INVALID_ARG, "k_scales must be 4-byte aligned");
+    if (!aligned(signs, 16)) return fail(FA_ERR_INVALID_ARG, "signs must be 16-byte aligned");
+    fa::PrefillParams p;
+    p.q = static_cast<const __bf16*>(q);
+    p.k = nullptr;
+    p.v = static_cast<const __bf16*>(v);
+    p.o = static_cast<__bf16*>(o);
+    p.lse = lse; p.kv_lens = kv_lens;
+    p.k8 = static_cast<const uint8_t*>(k8);
+    p.k_scale = k_scales;
+    p.q_signs = signs;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk;
+    p.r = Hq / Hkv;
+    p.n_qblocks = (Lq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+    const int units = B * Hkv;
+    p.xcd_units = (units % 8 == 0) ? units / 8 : 0;
+    p.xcd_spread = xcd_spread(Hq / Hkv, p.n_qblocks);
+    p.window = 0;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    const long long total = (long long)B * Hq * p.n_qblocks;
+    if (!grid_fits(total, 512)) return fail(FA_ERR_INVALID_ARG, "grid too large");
+    hipError_t e = fa::launch_prefill_fp8(D, causal != 0, p, reinterpret_cast<hipStream_t>(stream), true);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
 size_t fa_varlen_schedule_ints(int B) {
     return (B > 0 && B <= kMaxVarlenBatch) ? 2 * (size_t)B + 1 : 0;
 }

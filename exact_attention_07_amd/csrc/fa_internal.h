@@ -38,6 +38,9 @@ struct PrefillParams {
     const uint8_t* k8 = nullptr;
     const float* q_scale = nullptr;
     const float* k_scale = nullptr;
+    // FP8 with Q quantized in the kernel: Q in bf16 (q) and the D sign flips
+    // of the Hadamard transform (or null for none).
+    const float* q_signs = nullptr;
     // Score modifiers (the modifier instantiations only): ALiBi slopes [Hq]
     // and the soft-cap of the scaled scores.
     const float* alibi_slopes = nullptr;
@@ -127,7 +130,8 @@ struct BwdParams {
 // Each launcher enqueues its kernel(s) on `stream` and returns the launch status.
 hipError_t launch_prefill(int D, bool causal, const PrefillParams& p, hipStream_t stream);
 // The prefill with E4M3 Q and K (D = 128): p.q8, p.k8 and the scales replace p.q and p.k.
-hipError_t launch_prefill_fp8(int D, bool causal, const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_fp8(int D, bool causal, const PrefillParams& p, hipStream_t stream,
+                              bool quantize_q = false);
 hipError_t launch_quantize_fp8(int D, const QuantParams& p, int cus, hipStream_t stream);
 // The prefill with a score modifier: mod 1 = ALiBi (p.alibi_slopes), 2 = soft-cap (p.softcap).
 hipError_t launch_prefill_mod(int D, bool causal, int mod, const PrefillParams& p, hipStream_t stream);

@@ -135,7 +135,8 @@ struct ScoreOperand<true> { typedef i32x8 type; };
 constexpr int kModNone = 0, kModAlibi = 1, kModSoftcap = 2;
 constexpr float kPosInf = __builtin_inff();
 
-template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false, int MOD = kModNone, bool VARLEN = false>
+template <int D, bool CAUSAL, bool WINDOW, bool FP8 = false, int MOD = kModNone, bool VARLEN = false,
+          bool QQ = false>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
     constexpr int NW = 8;                   // wavefronts: two groups of four
@@ -155,6 +156,8 @@ prefill_kernel(PrefillParams p) {
     static_assert(!FP8 || !WINDOW, "the FP8 scores are built without a window");
     static_assert(MOD == kModNone || (!FP8 && !WINDOW), "score modifiers are built for the bf16 kernel without a window");
     static_assert(!VARLEN || (!FP8 && !WINDOW && MOD == kModNone), "packed batches are built for the plain bf16 kernel");
+    static_assert(!QQ || FP8, "Q is quantized in the kernel only for FP8 scores");
+    constexpr bool QBF16 = !FP8 || QQ;      // Q arrives in bf16 (staged through LDS)
     // Split probabilities in the bf16 kernels at D = 128 without modifiers: the
     // modifier and FP8 instantiations keep bf16 probabilities throughout.
     constexpr bool CORR = D == 128 && !FP8 && MOD == kModNone;
@@ -173,7 +176,8 @@ prefill_kernel(PrefillParams p) {
     // a wavefront's vector phase and read in its next matrix phase.
     constexpr int NCH = KB * 2;                     // 16-key chunks per tile
     __shared__ __attribute__((aligned(16))) bf16x8 plo_lds[D == 128 ? NW * NCH * 64 : 1];
-    __shared__ __attribute__((aligned(16))) bf16 qst[(!FP8 && D == 64) ? 256 * 64 : 8];   // Q staging at D = 64
+    __shared__ __attribute__((aligned(16))) bf16 qst[(QBF16 && D == 64) ? 256 * 64 : 8];   // Q staging at D = 64
+    __shared__ float qmax_w[QQ ? NW : 1];   // QQ: each wavefront's largest |transformed Q|
     __shared__ int split_rows;              // rows of the workgroup found dominated by a few keys
 
     const int tid = threadIdx.x;
@@ -310,9 +314,13 @@ prefill_kernel(PrefillParams p) {
     constexpr bool REV = MOD == kModAlibi;
     auto tile_abs = [&](int t) { return (REV && t < ntiles) ? tb + ntiles - 1 - t : tb + t; };
 
+    // FP8: exponent scale of tile t = c s_q s_k(t); s_k is read one tile ahead
+    // (QQ: s_q is found in the prologue).
+    float cq = (FP8 && !QQ) ? p.c * p.q_scale[(size_t)(b * p.Hq + h) * p.n_qblocks + qblk] : p.c;
+
     // ---- Q tile: B operand of S^T, resident in registers -------------------
     SA qf[KSQ];
-    if constexpr (FP8) {
+    if constexpr (FP8 && !QQ) {
         const rsrc_t qbuf = make_rsrc(p.q8 + qoff, (uint32_t)Lq * D);   // rows >= Lq read as zero
 #pragma unroll
         for (int ks = 0; ks < KSQ; ++ks) {
@@ -339,7 +347,7 @@ prefill_kernel(PrefillParams p) {
     // The 16 rows of one 16-lane group of a fragment read then hit 16
     // distinct 16-byte bank groups.
     auto q_swz = [](int row) { return D == 128 ? row & 15 : (row >> 1) & 7; };
-    if constexpr (!FP8) {
+    if constexpr (QBF16) {
         const int vq = min(max(Lq - qw0, 0), 32);
         const i32x4 qd = make_desc(p.q + qoff + (size_t)min(qw0, Lq) * D, (uint32_t)vq * D * 2);
         const uint32_t qs_addr = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) bf16*)qs_w);
@@ -350,6 +358,132 @@ prefill_kernel(PrefillParams p) {
             copy16_to_lds_async(qd, (uint32_t)(row * D + ((P % CH) ^ q_swz(row)) * 8) * 2, qs_addr + i * 1024);
         }
     }
+    // QQ: the E4M3 codes of Q made here, exactly as the block quantizer makes
+    // them (one power-of-two scale per 256-row block, the workgroup's query
+    // block; the optional random-sign Hadamard transform, FlashAttention-3's
+    // incoherent processing).  A lane takes the D / 2 elements of its row that
+    // its E4M3 operand holds, 64 ks + 32 hi + e (e < 32), from the staged bf16
+    // rows; x' = H (sigma x) runs in fp64 as butterflies over the index bits,
+    // in the lane for bits 0-4 and 6 (positions 32 ks + e) and between lanes
+    // l and l ^ 32 for bit 5.  Every partial sum is exact in fp64 for inputs
+    // whose exponents span at most 38 binades, so the order of the
+    // butterflies does not change the result, rounded once to fp32.
+    constexpr int NE = QQ ? D / 2 : 1;
+    float qx[NE];
+    auto quantize_q_local = [&]() __attribute__((always_inline)) {
+        if constexpr (QQ) {
+            const int row = l & 31;
+            double x[NE];
+#pragma unroll
+            for (int ks = 0; ks < KSQ; ++ks)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int e0 = 64 * ks + 32 * hi + 8 * cc;   // first element of the chunk
+                    u32x4 raw = *reinterpret_cast<const u32x4*>(
+                        qs_w + row * D + (((8 * ks + 4 * hi + cc) ^ q_swz(row)) * 8));
+                    if (p.q_signs) {
+                        // sigma: a sign flip of the bf16 bits where the sign's
+                        // own sign bit is set (word k holds elements 2k, 2k+1).
+                        const u32x4 s0 = *reinterpret_cast<const u32x4*>(p.q_signs + e0);
+                        const u32x4 s1 = *reinterpret_cast<const u32x4*>(p.q_signs + e0 + 4);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const unsigned a = k < 2 ? s0[2 * k] : s1[2 * k - 4];
+                            const unsigned c = k < 2 ? s0[2 * k + 1] : s1[2 * k - 3];
+                            raw[k] ^= ((a >> 16) & 0x8000u) | (c & 0x80000000u);
+                        }
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        x[32 * ks + 8 * cc + 2 * k] = (double)__builtin_bit_cast(float, raw[k] << 16);
+                        x[32 * ks + 8 * cc + 2 * k + 1] = (double)__builtin_bit_cast(float, raw[k] & 0xFFFF0000u);
+                    }
+                }
+            if (p.q_signs) {
+#pragma unroll
+                for (int bit = 1; bit < NE; bit <<= 1)
+#pragma unroll
+                    for (int i = 0; i < NE; ++i)
+                        if ((i & bit) == 0) {
+                            const double a = x[i], c2 = x[i + bit];
+                            x[i] = a + c2;
+                            x[i + bit] = a - c2;
+                        }
+                // Index bit 5 lies between lanes l and l ^ 32.  One exchange
+                // of x[i] (upper lanes) with x[i + 4] (lower lanes), local
+                // bit 2 of i clear, gives each lane both partners of one
+                // index: the lower lanes of i, the upper lanes of i + 4.  The
+                // butterfly then leaves y(bit 5 clear) in slot i and y(bit 5
+                // set) in slot i + 4 on either half; the codes are exchanged
+                // back once encoded (four per word).
+#pragma unroll
+                for (int i = 0; i < NE; ++i)
+                    if ((i & 4) == 0) {
+                        const unsigned long long a = __builtin_bit_cast(unsigned long long, x[i]);
+                        const unsigned long long c2 = __builtin_bit_cast(unsigned long long, x[i + 4]);
+                        const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)a, (unsigned)c2, false, false);
+                        const auto up = __builtin_amdgcn_permlane32_swap((unsigned)(a >> 32), (unsigned)(c2 >> 32),
+                                                                         false, false);
+                        // [0]: x[i] with its upper lanes from x[i + 4] of the lower lanes;
+                        // [1]: x[i + 4] with its lower lanes from x[i] of the upper lanes.
+                        const double A = __builtin_bit_cast(double, ((unsigned long long)up[0] << 32) | lo[0]);
+                        const double C = __builtin_bit_cast(double, ((unsigned long long)up[1] << 32) | lo[1]);
+                        x[i] = A + C;
+                        x[i + 4] = A - C;
+                    }
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                qx[i] = (float)x[i];
+                amax = fmaxf(amax, fabsf(qx[i]));
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+            if (l == 0) qmax_w[w] = amax;       // read after the prologue's barrier
+        }
+    };
+    // After the barrier: the block maximum, its scale 2^k (the smallest power
+    // of two with max 2^-k <= 448, E4M3's largest finite value) and the codes
+    // of x' 2^-k (round to nearest even) as the B operand.
+    auto quantize_q_finish = [&]() __attribute__((always_inline)) {
+        if constexpr (QQ) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) amax = fmaxf(amax, qmax_w[i]);
+            int k = 0;
+            if (amax > 0.0f) {
+                int e;
+                (void)frexpf(amax, &e);     // amax in [2^(e-1), 2^e)
+                k = (amax <= ldexpf(0.875f, e)) ? e - 9 : e - 8;
+            }
+            cq = p.c * ldexpf(1.0f, k);
+            auto encode4 = [&](const float* v) __attribute__((always_inline)) {
+                const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -k), ldexpf(v[1], -k), 0, false);
+                return __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -k), ldexpf(v[3], -k), lo, true);
+            };
+#pragma unroll
+            for (int ks = 0; ks < KSQ; ++ks) {
+                SA f;
+#pragma unroll
+                for (int d = 0; d < 8; d += 2) {
+                    const int we = encode4(qx + 32 * ks + 4 * d);
+                    const int wo = encode4(qx + 32 * ks + 4 * d + 4);
+                    if (p.q_signs) {
+                        // Word d of the upper lanes is held by the lower lanes
+                        // (as their word d + 1) and the other way round.
+                        const auto r = __builtin_amdgcn_permlane32_swap((unsigned)we, (unsigned)wo, false, false);
+                        f[d] = (int)r[0];
+                        f[d + 1] = (int)r[1];
+                    } else {
+                        f[d] = we;
+                        f[d + 1] = wo;
+                    }
+                }
+                qf[ks] = f;
+            }
+        }
+    };
     auto read_q = [&]() __attribute__((always_inline)) {
         if constexpr (!FP8) {
             const int row = l & 31;
@@ -358,8 +492,6 @@ prefill_kernel(PrefillParams p) {
                 qf[ks] = *reinterpret_cast<const bf16x8*>(qs_w + row * D + (((2 * ks + hi) ^ q_swz(row)) * 8));
         }
     };
-    // FP8: exponent scale of tile t = c s_q s_k(t); s_k is read one tile ahead.
-    const float cq = FP8 ? p.c * p.q_scale[(size_t)(b * p.Hq + h) * p.n_qblocks + qblk] : p.c;
     const int nks = (p.Lk + kFp8KBlock - 1) / kFp8KBlock;
     const float* kscale = FP8 ? p.k_scale + (size_t)(b * p.Hkv + g) * nks : nullptr;
     auto k_scale_of = [&](int t) __attribute__((always_inline)) {   // tile index relative to tb
@@ -783,7 +915,7 @@ prefill_kernel(PrefillParams p) {
 
     // ---- prologue: K(0..2), V(0..1) resident; S(0) -> P(0) -------------------
     // V(1) waits for the prologue's barrier where its buffer stages Q.
-    constexpr bool LATE_V1 = !FP8 && D == 128;
+    constexpr bool LATE_V1 = QBF16 && D == 128;
     copy_k(0);
     copy_k(1);
     copy_v(0);
@@ -792,11 +924,13 @@ prefill_kernel(PrefillParams p) {
     // Q and K(0) only: the other tiles stream in while S(0) and P(0) are
     // computed (vmcnt counts in issue order, the Q copies first).
     wait_vector_loads_until<2 * NIK + (LATE_V1 ? 1 : 2) * NI>();
-    if constexpr (!FP8) {
+    if constexpr (QBF16) {
         asm volatile("" ::: "memory");      // the staged rows are read only after the wait
-        read_q();
+        if constexpr (QQ) quantize_q_local();
+        else read_q();
     }
     __syncthreads();                        // K(0) visible; every wavefront's Q read from its staging
+    if constexpr (QQ) quantize_q_finish();
     if (LATE_V1) copy_v(1);
     score_tile(0);
     softmax_tile(0, Const<3>{});
@@ -920,15 +1054,21 @@ void launch_prefill_d(bool causal, bool window, const PrefillParams& p, dim3 gri
     else             hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, block, 0, stream, p);
 }
 
-hipError_t launch_prefill_fp8(int D, bool causal, const PrefillParams& p, hipStream_t stream) {
+template <int D, bool QQ>
+void launch_prefill_fp8_d(bool causal, const PrefillParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+    if (causal) hipLaunchKernelGGL((prefill_kernel<D, true, false, true, kModNone, false, QQ>), grid, block, 0, stream, p);
+    else        hipLaunchKernelGGL((prefill_kernel<D, false, false, true, kModNone, false, QQ>), grid, block, 0, stream, p);
+}
+
+hipError_t launch_prefill_fp8(int D, bool causal, const PrefillParams& p, hipStream_t stream, bool quantize_q) {
     const long long total = (long long)p.B * p.Hq * p.n_qblocks;
     const dim3 grid((unsigned)total), block(512);
     if (D == 64) {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<64, true, false, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<64, false, false, true>), grid, block, 0, stream, p);
+        if (quantize_q) launch_prefill_fp8_d<64, true>(causal, p, grid, block, stream);
+        else            launch_prefill_fp8_d<64, false>(causal, p, grid, block, stream);
     } else {
-        if (causal) hipLaunchKernelGGL((prefill_kernel<128, true, false, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((prefill_kernel<128, false, false, true>), grid, block, 0, stream, p);
+        if (quantize_q) launch_prefill_fp8_d<128, true>(causal, p, grid, block, stream);
+        else            launch_prefill_fp8_d<128, false>(causal, p, grid, block, stream);
     }
     return hipGetLastError();
 }

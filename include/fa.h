@@ -24,6 +24,12 @@
  * (running max, running sum, rescaled accumulator; same page, section 4.1;
  * Cheat Sheet, section 5) so the Lq x Lk score matrix never reaches HBM.
  * Both matrix products run on bf16 MFMA with fp32 accumulation.
+ * Range: the results follow the definition while every score
+ * scale * q.k (after any modifier) has magnitude below 2^27.  Scores are
+ * held in fp32 in base-2 units, and the exponent of each term is formed as
+ * one fused multiply-add against a rounded per-row reference; far past that
+ * bound the reference's rounding error alone exceeds its headroom and a row
+ * may come out as NaN.
  *
  * Memory layout and ownership (all entry points):
  *   q   : bf16, device, contiguous [B, Hq,  Lq, D]
@@ -251,6 +257,29 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* ls
                const float* q_scales, const float* k_scales,
                int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal, float scale,
                const int* kv_lens, void* stream);
+
+/*
+ * fa_fwd_fp8 with Q quantized inside the attention kernel (FlashAttention
+ * 1-4, FlashAttention-3 point 3; FlashAttention from Scratch, section 10.3):
+ * the result is that of
+ *     fa_quantize_fp8(q, q8, q_scales, B * Hq, Lq, D, 256, signs, stream);
+ *     fa_fwd_fp8(q8, k8, v, o, lse, q_scales, k_scales, ...);
+ * bit for bit, without the Q codes or scales reaching memory: each
+ * workgroup's query block is exactly one 256-row scale block, so it
+ * transforms, scales and encodes its own rows.  K is quantized beforehand
+ * (its blocks are shared by many workgroups), with the same signs.  (Both
+ * transforms sum in fp64, exactly for rows whose nonzero entries span at
+ * most 2^38 in magnitude; the equality is stated for such rows.)
+ *   q      : bf16, device, contiguous [B, Hq, Lq, D], 16-byte aligned
+ *   signs  : fp32, device, D values +1 or -1 (the transform's sign flips, as
+ *            given to fa_quantize_fp8 for K), 16-byte aligned, or NULL for no
+ *            transform
+ *   k8, k_scales, v, o, lse, kv_lens, causal, scale, stream: as for fa_fwd_fp8
+ * D = 64 or 128 (FA_ERR_UNSUPPORTED otherwise); other errors as for fa_fwd_fp8.
+ */
+int fa_fwd_fp8_q(const void* q, const float* signs, const void* k8, const void* v, void* o, float* lse,
+                 const float* k_scales, int B, int Hq, int Hkv, int Lq, int Lk, int D, int causal,
+                 float scale, const int* kv_lens, void* stream);
 
 /*
  * Attention over a batch of variable-length sequences packed end to end

@@ -246,6 +246,32 @@ def test_fwd_fp8_validation(lib, kw, status):
     assert lib.fa_last_error().decode() != ""
 
 
+def call_fp8_q(lib, q=P, signs=None, k8=P, v=P, o=P, lse=P, ks=P, B=1, Hq=2, Hkv=1, Lq=4, Lk=8, D=128,
+               causal=0, scale=0.125, kv_lens=None):
+    return lib.fa_fwd_fp8_q(q, signs, k8, v, o, lse, ks, B, Hq, Hkv, Lq, Lk, D, causal,
+                            ctypes.c_float(scale), kv_lens, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=32), binding.FA_ERR_UNSUPPORTED),
+    (dict(D=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(ks=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ks=ctypes.c_void_p((1 << 20) + 2)), binding.FA_ERR_INVALID_ARG),
+    (dict(signs=ctypes.c_void_p((1 << 20) + 4)), binding.FA_ERR_INVALID_ARG),   # 16-byte alignment
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(q=MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(k8=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+])
+def test_fwd_fp8_q_validation(lib, kw, status):
+    got = call_fp8_q(lib, **kw)
+    assert got == status, (kw, got, lib.fa_last_error())
+    assert lib.fa_last_error().decode() != ""
+
+
 def test_fp8_binding_requires_gpu_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
@@ -254,6 +280,8 @@ def test_fp8_binding_requires_gpu_tensors():
     with pytest.raises(ValueError):
         binding._prepare_fp8(x.to(torch.uint8), x.to(torch.uint8), x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1),
                              None, None, None, True)
+    with pytest.raises(ValueError):
+        binding._prepare_fp8_q(x, x.to(torch.uint8), x, torch.zeros(1, 1, 1), None, None, None, None, True)
 
 
 def call_mod(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Lq=4, Lk=8, D=64, causal=0,

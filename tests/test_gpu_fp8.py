@@ -221,3 +221,68 @@ def test_fp8_d64_long_causal_sampled_rows(dev):
         ro, rl = oracle.attention_rows(qv, kv, c.v[b:b + 1, h:h + 1], eff, True, None, 0, 0, rows=rr)
         m = compare(o[b, h][rr], lse[b, h][rr], ro, rl)
         print(f"[parity] fp8 D=64 long causal (b={b}, h={h}): {m}", flush=True)
+
+
+FUSED_CASES = [
+    # B, Hq, Hkv, Lq, Lk, causal, kv_lens, transform
+    (1, 2, 2, 64, 64, False, None, False),
+    (2, 4, 2, 300, 333, True, None, True),
+    (2, 4, 2, 257, 300, True, "ragged", False),
+    (3, 8, 2, 129, 190, False, "ragged", True),
+    (2, 4, 4, 1, 500, False, "ragged", True),       # one query per head
+    (1, 2, 2, 100, 60, True, None, True),           # more queries than keys: empty rows
+    (1, 4, 1, 700, 650, True, None, True),          # three query blocks, the last partial
+]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"_{c[6] is not None}_{c[7]}")
+def test_fused_q_equals_quantize_then_forward(dev, case, D):
+    # fa_fwd_fp8_q quantizes Q inside the forward with the block quantizer's
+    # recipe (256-row blocks, the same transform and scale rule): outputs and
+    # LSE equal bit for bit those of fa_quantize_fp8 on Q followed by
+    # fa_fwd_fp8.  Q blocks of every scale regime: outlier channels, an
+    # all-zero block (scale 1), a block of tiny values and one of large ones.
+    B, Hq, Hkv, Lq, Lk, causal, lens, tr = case
+    c = W.random_case(1500 + Lq + Lk + (D == 64), B, Hq, Hkv, Lq, Lk, D, causal, lens)
+    q = rows(1600 + Lq + D, (B, Hq, Lq, D), 2)
+    if Lq > 512:
+        q[0, 0, :256] = 0
+        q[0, 1, 256:512] = q[0, 1, 256:512] * 2.0 ** -40
+        q[0, 2, 512:] = q[0, 2, 512:] * 2.0 ** 12      # scores within the documented range
+    sg = signs_of(17 + D, D).to(dev) if tr else None
+    q, k, v = q.to(dev), c.k.to(dev), c.v.to(dev)
+    kl = None if c.kv_lens is None else c.kv_lens.to(dev)
+    eff = c.scale / D if tr else c.scale
+    q8, qs = binding.quantize_fp8(q, binding.FP8_Q_BLOCK, sg)
+    k8, ks = binding.quantize_fp8(k, binding.FP8_K_BLOCK, sg)
+    o1, l1 = binding.fa_fwd_fp8(q8, k8, v, qs, ks, causal=causal, scale=eff, kv_lens=kl)
+    o2 = torch.full_like(q, float("nan"))
+    l2 = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=dev)
+    binding.fa_fwd_fp8_q(q, k8, v, ks, sg, o2, l2, causal=causal, scale=eff, kv_lens=kl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), (o1 - o2).abs().max().item()
+    assert torch.equal(l1.isnan(), l2.isnan()) and torch.equal(l1.nan_to_num(), l2.nan_to_num())
+    if case == FUSED_CASES[1]:
+        ro, rl, *_ = oracle.fp8.fp8_attention_forward(q.cpu(), c.k, c.v, c.scale, causal, c.kv_lens,
+                                                      None if sg is None else sg.cpu().numpy())
+        m = compare(o2.cpu(), l2.cpu(), ro, rl)
+        print(f"[parity] fused-Q fp8 D={D} {case}: {m}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["fp8_causal_b2_h16_l4096_d128", "fp8_gqa_causal_b1_hq32_hkv8_l16384_d128"])
+def test_fused_q_full_size_equals_quantize_then_forward(dev, name):
+    # The FP8 workloads at full size: the fused-Q forward equals the two-step
+    # path bit for bit (the two-step path is checked against the oracle above).
+    w = W.BY_NAME[name]
+    inp = W.make_inputs(w)
+    sg = inp.meta["signs"].to(dev)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    eff = w.scale / w.D
+    q8, qs = binding.quantize_fp8(q, binding.FP8_Q_BLOCK, sg)
+    k8, ks = binding.quantize_fp8(k, binding.FP8_K_BLOCK, sg)
+    o1, l1 = binding.fa_fwd_fp8(q8, k8, v, qs, ks, causal=True, scale=eff)
+    o2, l2 = binding.fa_fwd_fp8_q(q, k8, v, ks, sg, causal=True, scale=eff)
+    torch.cuda.synchronize()
+    print(f"[fp8] fused-Q {name}: max |dO| {(o1.float() - o2.float()).abs().max().item()}", flush=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
