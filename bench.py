@@ -279,6 +279,9 @@ def time_workload(w, steps, warmup, dev, trials=True, warm_ms=0.0):
             del unsorted
         rec["sequence_lengths"] = inp.meta["lens_q"]
         rec["total_tokens"] = int(q.shape[1])
+    if w.name in FIVE:
+        torch.cuda.synchronize()
+        inp.meta["gpu_out"] = (o.cpu(), lse.cpu())   # compared with the oracle's sample in cpu_baseline
     del call, q, k, v, o, lse, kl
     torch.cuda.empty_cache()
     return rec, inp
@@ -314,11 +317,23 @@ def cpu_baseline(w, inp, seconds, chunk=512):
     units = [(b, h, r0, min(r0 + chunk, w.Lq)) for b in range(w.B) for h in range(w.Hq)
              for r0 in range(0, w.Lq, chunk)]
 
+    got = inp.meta.get("gpu_out")
+
     def unit_work(u):
         b, h, r0, r1 = u
         rows = np.arange(r0, r1)
-        oracle.attention_rows(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens, b, h, rows,
-                              window=w.window)
+        ro, rl = oracle.attention_rows(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens, b, h, rows,
+                                       window=w.window)
+        if got is not None:
+            # The same rows of the timed kernel's output against the oracle's.
+            go = got[0][b, h, r0:r1].double().numpy()
+            gl = got[1][b, h, r0:r1].double().numpy()
+            ro, rl = np.asarray(ro, np.float64), np.asarray(rl, np.float64)
+            d = np.abs(go - ro)
+            both_inf = np.isneginf(gl) & np.isneginf(rl)
+            dl = np.where(both_inf, 0.0, np.abs(gl - rl))
+            err.append((float(d.max(initial=0.0)), float((d * d).sum()), float((ro * ro).sum()),
+                        float(dl.max(initial=0.0)), u))
         n = ns[b]
         off = n - w.Lq
         pairs = 0
@@ -331,6 +346,7 @@ def cpu_baseline(w, inp, seconds, chunk=512):
         return 4 * w.D * pairs, (r1 - r0) * (2 * w.D * 2 + 4) + kv_bytes
 
     done_flops = done_bytes = done = 0
+    err = []
     ctx = threadpool_limits(limits=1, user_api="blas") if threadpool_limits else None
     t0 = time.perf_counter()
     try:
@@ -356,10 +372,29 @@ def cpu_baseline(w, inp, seconds, chunk=512):
     sample = (f"{done} (batch, query head, {chunk}-row) units of {len(units)} in the workload "
               f"({done / len(units):.3f} passes) on {cores} threads, fp64 dense S, P, O, {dt:.1f} s")
     if w.Lq == 1:
-        return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-                "sample": sample}
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": sample}
+        res = {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": sample}
+    else:
+        res = {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": sample}
+    if err:
+        # Parity of the timed output on the oracle's sample, against the
+        # forward's bar: max |dO| <= 1e-2, relative L2 of O <= 4e-3, max |dLSE| <= 1e-3.
+        max_abs = max(e[0] for e in err)
+        rel_l2 = math.sqrt(sum(e[1] for e in err) / max(sum(e[2] for e in err), 1e-300))
+        dlse = max(e[3] for e in err)
+        res["parity"] = {"rows": sum(u[3] - u[2] for u in {e[4] for e in err}), "max_abs": max_abs, "rel_l2": rel_l2,
+                         "max_abs_dlse": dlse, "bar": {"max_abs": 1e-2, "rel_l2": 4e-3, "max_abs_dlse": 1e-3},
+                         "within_bar": bool(max_abs <= 1e-2 and rel_l2 <= 4e-3 and dlse <= 1e-3)}
+    return res
+
+
+def print_parity(name, cpu):
+    par = cpu.get("parity")
+    if par:
+        print(f"[bench] parity of {name} on the oracle's {par['rows']} sampled rows: max |dO| {par['max_abs']:.3e}, "
+              f"rel L2 {par['rel_l2']:.3e}, max |dLSE| {par['max_abs_dlse']:.3e}, "
+              f"{'within' if par['within_bar'] else 'OUTSIDE'} the forward's bar", flush=True)
 
 
 def copy_calibration(mib, dev):
@@ -432,6 +467,7 @@ def main():
             if w.name in FIVE and not args.no_cpu:
                 print(f"[bench] CPU oracle baseline on {w.name} (~{args.cpu_seconds_each:.0f} s)", flush=True)
                 r["cpu_baseline"] = cpu_baseline(w, winp, args.cpu_seconds_each)
+                print_parity(w.name, r["cpu_baseline"])
             del winp
             r["traffic"] = stored_traffic(w.name)
             extra[w.name] = rounded(r)
@@ -457,6 +493,7 @@ def main():
     if not args.no_cpu and head.varlen is None:   # the oracle baseline is for the batched layout
         print(f"[bench] CPU oracle baseline on {head.name} (~{args.cpu_seconds:.0f} s)", flush=True)
         cpu = cpu_baseline(head, inp, args.cpu_seconds)
+        print_parity(head.name, cpu)
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(rec["ms_per_step"], 6),
