@@ -306,6 +306,7 @@ def cpu_baseline(w, inp, seconds, chunk=512):
     from concurrent.futures import ThreadPoolExecutor, FIRST_COMPLETED, wait
 
     import numpy as np
+    import torch
     import oracle
     from exact_attention_07_amd import workloads as W
     try:
@@ -332,8 +333,16 @@ def cpu_baseline(w, inp, seconds, chunk=512):
             d = np.abs(go - ro)
             both_inf = np.isneginf(gl) & np.isneginf(rl)
             dl = np.where(both_inf, 0.0, np.abs(gl - rl))
-            err.append((float(d.max(initial=0.0)), float((d * d).sum()), float((ro * ro).sum()),
-                        float(dl.max(initial=0.0)), u))
+            # Elements that no bf16 value can bring within 1e-2 (|O| >= 4, O
+            # more than 1e-2 from both bf16 neighbours) must be one of those
+            # neighbours: an error below one bf16 spacing of O.
+            floor = np.abs(torch.from_numpy(ro).to(torch.bfloat16).double().numpy() - ro)
+            unrep = floor > 1e-2
+            spacing = np.ldexp(1.0, np.frexp(np.abs(ro))[1] - 8)
+            bad_unrep = int(np.count_nonzero(unrep & (d >= spacing)))
+            err.append((float(np.where(unrep, 0.0, d).max(initial=0.0)), float((d * d).sum()), float((ro * ro).sum()),
+                        float(dl.max(initial=0.0)), u, float(d.max(initial=0.0)), int(np.count_nonzero(unrep)),
+                        bad_unrep))
         n = ns[b]
         off = n - w.Lq
         pairs = 0
@@ -379,20 +388,31 @@ def cpu_baseline(w, inp, seconds, chunk=512):
                "sample": sample}
     if err:
         # Parity of the timed output on the oracle's sample, against the
-        # forward's bar: max |dO| <= 1e-2, relative L2 of O <= 4e-3, max |dLSE| <= 1e-3.
-        max_abs = max(e[0] for e in err)
+        # forward's bar: max |dO| <= 1e-2 wherever a bf16 value can meet it
+        # (elsewhere one of O's two bf16 neighbours), relative L2 of O <= 4e-3,
+        # max |dLSE| <= 1e-3.
+        seen = {}
+        for e in err:
+            seen[e[4]] = e                  # units timed more than once: count each once
+        err = list(seen.values())
+        max_rep = max(e[0] for e in err)
         rel_l2 = math.sqrt(sum(e[1] for e in err) / max(sum(e[2] for e in err), 1e-300))
         dlse = max(e[3] for e in err)
-        res["parity"] = {"rows": sum(u[3] - u[2] for u in {e[4] for e in err}), "max_abs": max_abs, "rel_l2": rel_l2,
-                         "max_abs_dlse": dlse, "bar": {"max_abs": 1e-2, "rel_l2": 4e-3, "max_abs_dlse": 1e-3},
-                         "within_bar": bool(max_abs <= 1e-2 and rel_l2 <= 4e-3 and dlse <= 1e-3)}
+        bad = sum(e[7] for e in err)
+        res["parity"] = {"rows": sum(e[4][3] - e[4][2] for e in err), "max_abs": max(e[5] for e in err),
+                         "max_abs_representable": max_rep, "unrepresentable": sum(e[6] for e in err),
+                         "unrepresentable_off_neighbours": bad, "rel_l2": rel_l2, "max_abs_dlse": dlse,
+                         "bar": {"max_abs": 1e-2, "rel_l2": 4e-3, "max_abs_dlse": 1e-3},
+                         "within_bar": bool(max_rep <= 1e-2 and bad == 0 and rel_l2 <= 4e-3 and dlse <= 1e-3)}
     return res
 
 
 def print_parity(name, cpu):
     par = cpu.get("parity")
     if par:
-        print(f"[bench] parity of {name} on the oracle's {par['rows']} sampled rows: max |dO| {par['max_abs']:.3e}, "
+        print(f"[bench] parity of {name} on the oracle's {par['rows']} sampled rows: max |dO| {par['max_abs']:.3e} "
+              f"({par['max_abs_representable']:.3e} where bf16 can meet 1e-2; {par['unrepresentable']} elements "
+              f"where it cannot, {par['unrepresentable_off_neighbours']} of them off O's bf16 neighbours), "
               f"rel L2 {par['rel_l2']:.3e}, max |dLSE| {par['max_abs_dlse']:.3e}, "
               f"{'within' if par['within_bar'] else 'OUTSIDE'} the forward's bar", flush=True)
 
