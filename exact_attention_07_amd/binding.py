@@ -404,16 +404,21 @@ def fa_fwd_fp8(q8, k8, v, q_scales, k_scales, o=None, lse=None, *, causal=False,
     return o, lse
 
 
-def attention_fp8(q, k, v, *, causal=False, scale=None, kv_lens=None, signs=None, stream=None):
+def attention_fp8(q, k, v, *, causal=False, scale=None, kv_lens=None, signs=None, stream=None,
+                  quantize_q_in_kernel=False):
     """bf16 Q, K, V -> FP8 attention: Q and K block-quantized (after the
     Hadamard transform with ``signs`` when given, whose factor D in the
-    scores is divided out of the scale), then ``fa_fwd_fp8``.  Returns
-    (o, lse)."""
+    scores is divided out of the scale), then ``fa_fwd_fp8``; with
+    ``quantize_q_in_kernel`` K alone is quantized first and
+    ``fa_fwd_fp8_q`` quantizes Q inside the forward (the same result, bit
+    for bit).  Returns (o, lse)."""
     D = q.shape[3]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    q8, qs = quantize_fp8(q, FP8_Q_BLOCK, signs, stream)
     k8, ks = quantize_fp8(k, FP8_K_BLOCK, signs, stream)
     eff = scale / D if signs is not None else scale
+    if quantize_q_in_kernel:
+        return fa_fwd_fp8_q(q, k8, v, ks, signs, causal=causal, scale=eff, kv_lens=kv_lens, stream=stream)
+    q8, qs = quantize_fp8(q, FP8_Q_BLOCK, signs, stream)
     return fa_fwd_fp8(q8, k8, v, qs, ks, causal=causal, scale=eff, kv_lens=kv_lens, stream=stream)
 
 

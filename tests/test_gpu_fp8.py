@@ -270,6 +270,28 @@ def test_fused_q_equals_quantize_then_forward(dev, case, D):
         print(f"[parity] fused-Q fp8 D={D} {case}: {m}", flush=True)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_fused_q_edge_cases(dev, D):
+    # No keys at all (Lk = 0), and sequences of zero length beside full ones:
+    # O = 0 and LSE = -inf on rows with no allowed key, from both paths alike;
+    # attention_fp8's two forms agree bit for bit.
+    sg = signs_of(19 + D, D).to(dev)
+    q = rows(1700 + D, (2, 4, 40, D)).to(dev)
+    k = torch.zeros(2, 2, 0, D, dtype=torch.bfloat16, device=dev)
+    k8 = torch.zeros(2, 2, 0, D, dtype=torch.uint8, device=dev)
+    ks = torch.zeros(2, 2, 0, dtype=torch.float32, device=dev)
+    o, lse = binding.fa_fwd_fp8_q(q, k8, k.clone(), ks, sg, causal=False, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    c = W.random_case(1710 + D, 3, 4, 2, 70, 90, D, True, [90, 0, 33])
+    kl = c.kv_lens.to(dev)
+    outs = [binding.attention_fp8(c.q.to(dev), c.k.to(dev), c.v.to(dev), causal=True, scale=c.scale, kv_lens=kl,
+                                  signs=sg, quantize_q_in_kernel=f) for f in (False, True)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.all(outs[1][0][1] == 0) and torch.all(torch.isneginf(outs[1][1][1]))
+
+
 @pytest.mark.parametrize("name", ["fp8_causal_b2_h16_l4096_d128", "fp8_gqa_causal_b1_hq32_hkv8_l16384_d128"])
 def test_fused_q_full_size_equals_quantize_then_forward(dev, name):
     # The FP8 workloads at full size: the fused-Q forward equals the two-step
