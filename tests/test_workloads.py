@@ -102,3 +102,39 @@ def test_varlen_case_offsets():
     assert c.meta["cu_seqlens_q"].tolist() == [0, 3, 3, 10]
     assert c.meta["cu_seqlens_k"].tolist() == [0, 4, 6, 13]
     assert tuple(c.q.shape) == (4, 10, 64) and tuple(c.k.shape) == (2, 13, 64)
+
+
+def test_bench_parity_report_flags_planted_errors():
+    # bench.py's cpu_baseline leg compares the timed output with the oracle's
+    # rows.  Fed the oracle's own output rounded to bf16 it must report the
+    # forward's bar met; an element 0.02 off, or an element no bf16 value can
+    # bring within 1e-2 placed off both of its bf16 neighbours, must fail it.
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    import oracle
+
+    w = W.BY_NAME["tiny_b1_h2_l256_d64"]
+    inp = W.make_inputs(w)
+    inp.v = (inp.v.float() * 16).to(torch.bfloat16)       # |O| up to ~8: unrepresentable elements exist
+    ro, rl = oracle.attention_forward(inp.q, inp.k, inp.v, w.scale, w.causal, inp.kv_lens)
+    ro, rl = np.asarray(ro), np.asarray(rl)
+    good = torch.from_numpy(ro).to(torch.bfloat16)
+
+    def report(o):
+        inp.meta["gpu_out"] = (o, torch.from_numpy(rl).float())
+        return bench.cpu_baseline(w, inp, 0.5)["parity"]
+
+    par = report(good)
+    assert par["within_bar"] and par["unrepresentable"] > 0 and par["rows"] == w.B * w.Hq * w.Lq
+    off = good.clone()
+    off[0, 1, 100, 7] += 0.02 if abs(float(off[0, 1, 100, 7])) < 2 else 0.1
+    assert not report(off)["within_bar"]
+    g = good.double().numpy()
+    unrep = np.argwhere(np.abs(g - ro) > 1e-2)[0]
+    t = tuple(unrep)
+    spacing = 2.0 ** (np.frexp(abs(ro[t]))[1] - 8)
+    bad = good.clone()
+    bad[t] = float(g[t] + 2 * spacing * np.sign(g[t] - ro[t]))   # two spacings out: off both neighbours
+    par = report(bad)
+    assert not par["within_bar"] and par["unrepresentable_off_neighbours"] == 1
